@@ -1,0 +1,1 @@
+"""CPU oracle package (test infrastructure only; never used by the product path)."""

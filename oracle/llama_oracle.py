@@ -1,0 +1,251 @@
+"""Plain CPU oracle for one pre-norm LLaMA decoder layer forward.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's CPU
+baseline leg use it.  It shares no code with the HIP library.
+
+Everything is computed in fp64 with numpy, materialising every intermediate
+(full score matrices, an explicitly repeated K/V for grouped-query attention).
+Sources, cited by page title and section:
+
+  [LMDrive]   "LMDrive 大语言模型（LLM）核心推理单元" (LMDrive LLM core
+              inference unit): §2.1 LlamaRMSNorm, §2.2 LlamaRotaryEmbedding,
+              §2.3 LlamaAttention, §2.4 LlamaMLP, §2.5 LlamaDecoderLayer.
+  [Notes]     "LLM 核心机制交互讲义" (LLM mechanics lecture notes):
+              Ch.02 §02.1 causal mask, §02.2 RoPE, §02.3 RMSNorm, §02.4 SwiGLU,
+              the pre-norm block equation; Ch.04 prefill/decode, KV cache and
+              its memory accounting.
+  [MLP]       "深入解析Llama MLP模块：SwiGLU激活函数与参数配置详解" (Llama MLP
+              deep dive): §2.2 the gate/up/down computation, §3 parameter counts.
+
+Two modes:
+  plain       no intermediate rounding (the gate for fp32 layers);
+  bf16 points round-to-nearest-even to bf16 (this module's own rounding) of
+              exactly the tensors a bf16 layer stores or feeds to bf16 matrix
+              products: the normalised activations, q, k, v (the cache dtype),
+              the attention output, and the SwiGLU product.  Scores, softmax
+              weights, the residual stream X' and the returned y are never
+              rounded.
+
+Parity status: every function below is pinned by a CPU test against what the
+pages or the mathematics fix (worked examples, invariants, library routines
+on tiny inputs); see tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding (used only in the "bf16 points" mode)
+# --------------------------------------------------------------------------
+
+def bf16_round(a):
+    """Round fp64 values to the nearest bf16 value, ties to even.
+
+    bf16 keeps 8 significant bits (1 implicit + 7 stored) and fp32's exponent
+    range.  frexp gives a = m * 2^e with 0.5 <= |m| < 1, so m * 2^8 carries
+    exactly the 8 bits to keep; np.rint rounds half to even.  Values this
+    layer produces never reach bf16's overflow or subnormal range.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    return np.ldexp(np.rint(m * 256.0), e - 8)
+
+
+def _maybe_round(a, bf16_points: bool):
+    return bf16_round(a) if bf16_points else a
+
+
+# --------------------------------------------------------------------------
+# RMSNorm  [LMDrive §2.1; Notes §02.3]
+# --------------------------------------------------------------------------
+
+def rms_norm(x, g, eps):
+    """g * x / sqrt(mean(x^2) + eps) over the last axis.
+
+    eps sits inside the square root, next to the mean square.  The gain is
+    applied after normalising, in the same precision (the order in the notes'
+    runnable example 05, one rounding at the end)."""
+    x = np.asarray(x, dtype=np.float64)
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return np.asarray(g, dtype=np.float64) * (x / np.sqrt(ms + eps))
+
+
+# --------------------------------------------------------------------------
+# RoPE, rotate-half convention  [LMDrive §2.2; Notes §02.2]
+# --------------------------------------------------------------------------
+
+def rope_inv_freq(head_dim, base):
+    """theta_i = base^(-2i/head_dim), i = 0 .. head_dim/2 - 1."""
+    i = np.arange(0, head_dim // 2, dtype=np.float64)
+    return 1.0 / (float(base) ** (2.0 * i / head_dim))
+
+
+def rope_cos_sin(positions, head_dim, base):
+    """cos and sin of angle p * theta_i, shape positions.shape + (head_dim/2,)."""
+    ang = np.asarray(positions, dtype=np.float64)[..., None] * rope_inv_freq(head_dim, base)
+    return np.cos(ang), np.sin(ang)
+
+
+def rope(x, positions, base):
+    """Rotate-half RoPE of x[..., head_dim] at the given positions.
+
+    Dimension i (i < head_dim/2) is paired with i + head_dim/2 and the pair is
+    turned by the angle p * theta_i:
+        x'_i          = x_i cos - x_{i+half} sin
+        x'_{i+half}   = x_{i+half} cos + x_i sin
+    `positions` broadcasts against x's leading axes (no head axis)."""
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
+    cos, sin = rope_cos_sin(positions, x.shape[-1], base)
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+# --------------------------------------------------------------------------
+# Attention  [LMDrive §2.3; Notes §02.1, Ch.04]
+# --------------------------------------------------------------------------
+
+def repeat_kv(kv, n_rep):
+    """[..., Hkv, S, dh] -> [..., Hkv*n_rep, S, dh]; kv head g serves query
+    heads g*n_rep .. g*n_rep + n_rep - 1 (each kv head repeated in place)."""
+    return np.repeat(kv, n_rep, axis=-3)
+
+
+def masked_softmax_attention(q, k, v, q_pos, k_pos):
+    """softmax(q k^T / sqrt(dh) + M) v for one head.
+
+    q [Tq, dh], k/v [S, dh]; M_ij = 0 if k_pos[j] <= q_pos[i] else -inf,
+    added before the softmax.  Returns (output [Tq, dh], weights [Tq, S])."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    dh = q.shape[-1]
+    scores = (q @ k.T) / np.sqrt(dh)
+    mask = np.where(np.asarray(k_pos)[None, :] <= np.asarray(q_pos)[:, None], 0.0, -np.inf)
+    s = scores + mask
+    s = s - np.max(s, axis=-1, keepdims=True)
+    e = np.exp(s)
+    a = e / np.sum(e, axis=-1, keepdims=True)
+    return a @ v, a
+
+
+# --------------------------------------------------------------------------
+# SwiGLU MLP  [LMDrive §2.4; MLP §2.2; Notes §02.4]
+# --------------------------------------------------------------------------
+
+def silu(z):
+    """z * sigmoid(z)."""
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_hidden(xn, w_gate, w_up):
+    """SiLU(xn W_gate^T) * (xn W_up^T); the activation acts on the gate branch only."""
+    return silu(xn @ np.asarray(w_gate, np.float64).T) * (xn @ np.asarray(w_up, np.float64).T)
+
+
+def mlp_param_count(d_model, d_ff):
+    """Parameters of the bias-free gate/up/down MLP: three d x f matrices."""
+    return 3 * d_model * d_ff
+
+
+def kv_cache_bytes(layers, batch, tokens, n_kv_heads, head_dim, elem_bytes):
+    """L x 2 (K and V) x B x T x H_kv x d_h x bytes per element [Notes Ch.04]."""
+    return layers * 2 * batch * tokens * n_kv_heads * head_dim * elem_bytes
+
+
+# --------------------------------------------------------------------------
+# The decoder layer  [LMDrive §2.5; Notes Ch.02 block equation, Ch.04]
+# --------------------------------------------------------------------------
+
+def _f64(a):
+    if hasattr(a, "detach"):  # torch tensor
+        a = a.detach().to("cpu")
+        import torch
+        a = a.to(torch.float64).numpy()
+    return np.asarray(a, dtype=np.float64)
+
+
+def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_heads,
+                  eps=1e-6, rope_base=10000.0, bf16_points=False, rows=None):
+    """One pre-norm decoder layer forward over B sequences with a KV cache.
+
+        X'  = x  + o_proj(CausalAttn(RoPE(q, k), v))      q,k,v = proj(RMSNorm1(x))
+        y   = X' + down(SiLU(gate(RMSNorm2(X'))) * up(RMSNorm2(X')))
+
+    x          [B, T, d]       token (b, t) sits at position positions[b, t]
+    positions  [B, T] ints     its post-RoPE key and raw value are written to
+                               cache slot positions[b, t]; its query sees every
+                               slot j <= positions[b, t] of sequence b.
+    weights    dict of nn.Linear-layout [out, in] matrices wq, wk, wv, wo,
+               w_gate, w_up, w_down and gains attn_norm, ffn_norm.
+    k_cache, v_cache [B, Hkv, S, dh]: slots below a sequence's first position
+               hold its prior (already rotated) keys and values.
+    rows       optional list of flat token indices b*T + t; when given, the
+               output is computed for those tokens only (keys and values are
+               still computed for every token, as the cache needs them).
+
+    Returns (y [B, T, d] (rows not asked for are NaN), k_cache', v_cache').
+    """
+    x = _f64(x)
+    B, T, d = x.shape
+    pos = np.asarray(_f64(positions), dtype=np.int64).reshape(B, T)
+    W = {k_: _f64(v_) for k_, v_ in weights.items()}
+    kc = _f64(k_cache).copy()
+    vc = _f64(v_cache).copy()
+    H, Hkv = n_heads, n_kv_heads
+    dh = W["wq"].shape[0] // H
+    n_rep = H // Hkv
+    r = lambda a: _maybe_round(a, bf16_points)  # noqa: E731
+
+    xn = r(rms_norm(x, W["attn_norm"], eps))                         # [B,T,d]
+
+    # keys and values for every token: cache write at slot = position
+    k = xn @ W["wk"].T                                               # [B,T,Hkv*dh]
+    v = xn @ W["wv"].T
+    k = k.reshape(B, T, Hkv, dh).transpose(0, 2, 1, 3)               # [B,Hkv,T,dh]
+    v = v.reshape(B, T, Hkv, dh).transpose(0, 2, 1, 3)
+    k = r(rope(k, pos[:, None, :], rope_base))
+    v = r(v)
+    for b in range(B):
+        kc[b][:, pos[b], :] = k[b]
+        vc[b][:, pos[b], :] = v[b]
+
+    want = np.zeros(B * T, dtype=bool)
+    if rows is None:
+        want[:] = True
+    else:
+        want[np.asarray(rows, dtype=np.int64)] = True
+    want = want.reshape(B, T)
+
+    y = np.full((B, T, d), np.nan)
+    for b in range(B):
+        ts = np.nonzero(want[b])[0]
+        if ts.size == 0:
+            continue
+        xb, xnb, pb = x[b, ts], xn[b, ts], pos[b, ts]               # [n,d]
+        q = (xnb @ W["wq"].T).reshape(ts.size, H, dh).transpose(1, 0, 2)   # [H,n,dh]
+        q = r(rope(q, pb[None, :], rope_base))
+        S = int(pb.max()) + 1                                        # slots 0 .. max position
+        kk = repeat_kv(kc[b][:, :S], n_rep)                          # [H,S,dh]
+        vv = repeat_kv(vc[b][:, :S], n_rep)
+        heads = [masked_softmax_attention(q[h], kk[h], vv[h], pb, np.arange(S))[0]
+                 for h in range(H)]
+        o = r(np.stack(heads, axis=1).reshape(ts.size, H * dh))      # heads concatenated
+        x1 = xb + o @ W["wo"].T                                      # X', never rounded
+        xn2 = r(rms_norm(x1, W["ffn_norm"], eps))
+        h_ = r(swiglu_hidden(xn2, W["w_gate"], W["w_up"]))
+        y[b, ts] = x1 + h_ @ W["w_down"].T
+    return y, kc, vc
+
+
+def decoder_layer_decode(x, positions, weights, k_cache, v_cache, **kw):
+    """One decode step: x [B, d], positions [B] (= each sequence's cache length).
+    The same layer with T = 1; returns (y [B, d], k_cache', v_cache')."""
+    x = _f64(x)
+    B, d = x.shape
+    pos = np.asarray(_f64(positions), dtype=np.int64).reshape(B, 1)
+    y, kc, vc = decoder_layer(x.reshape(B, 1, d), pos, weights, k_cache, v_cache, **kw)
+    return y.reshape(B, d), kc, vc
