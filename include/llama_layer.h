@@ -1,0 +1,145 @@
+/*
+ * llama_layer.h — C ABI of an MI355X (gfx950) library for one pre-norm LLaMA
+ * decoder layer forward, with grouped-query attention and a KV cache.
+ *
+ * What one call computes (sources cited by page title and section):
+ *   "LMDrive LLM core inference unit" page (LMDrive 大语言模型（LLM）核心推理单元),
+ *     §2.5 LlamaDecoderLayer: pre-norm, residual + attention, residual + MLP;
+ *     §2.1 LlamaRMSNorm; §2.2 LlamaRotaryEmbedding (rotate-half RoPE);
+ *     §2.3 LlamaAttention (q/k/v/o projections, KV-cache append, repeat_kv GQA,
+ *          softmax(q k^T / sqrt(dh) + mask) v); §2.4 LlamaMLP (SwiGLU).
+ *   "LLM mechanics lecture notes" (LLM 核心机制交互讲义), Ch.02: the block
+ *     equation X' = X + Attn(RMSNorm(X)), X'' = X' + SwiGLU(RMSNorm(X')),
+ *     §02.1 causal mask added before the softmax; Ch.04: prefill vs decode,
+ *     K/V appended to the cache, decode RoPE position = cache length.
+ *
+ *   xn  = RMSNorm(x; attn_norm, eps)
+ *   q,k,v = xn Wq^T, xn Wk^T, xn Wv^T             (no bias)
+ *   q,k  <- rotate-half RoPE at each token's position (base rope_base)
+ *   K/V cache slot `pos` of the token's sequence <- k (rotated), v
+ *   o   = softmax(q K^T / sqrt(dh), slots j <= pos only) V   per query head;
+ *         query head h reads kv head h / (n_heads / n_kv_heads)
+ *   X'  = x + o Wo^T
+ *   xn2 = RMSNorm(X'; ffn_norm, eps)
+ *   y   = X' + (SiLU(xn2 Wgate^T) * (xn2 Wup^T)) Wdown^T
+ *
+ * Layout.  Row-major everywhere.  Weights use nn.Linear's [out, in] layout.
+ * Hidden states are [tokens, d_model]; token (b, t) of a prefill call is row
+ * b*T + t.  Each KV cache (K and V separately) is [B, n_kv_heads, max_pos,
+ * head_dim]: slot p of sequence b, kv head g starts at element
+ * ((b*n_kv_heads + g)*max_pos + p)*head_dim.  Keys are stored after RoPE.
+ * Positions are int32 on the device.
+ *
+ * Precision.  LLAMA_BF16: weights, activations, gains and caches are bf16;
+ * products accumulate in fp32; RMSNorm, RoPE, softmax and the SwiGLU
+ * epilogue run in fp32; the residual stream X' stays fp32 between the two
+ * halves.  LLAMA_F32: everything fp32 (any shape; meant for small layers).
+ *
+ * Streams and ownership.  All pointers except the config/weights structs are
+ * device pointers.  Calls enqueue work on `stream` (a hipStream_t; NULL is
+ * the default stream) and return without waiting; a return of LLAMA_OK means
+ * "enqueued".  x, y, positions and the caches stay owned by the caller;
+ * y may be the same buffer as x, but must not partially overlap it.  One
+ * handle owns scratch memory, so calls on the same handle must not overlap
+ * (serialise them on one stream).  No call allocates device memory except
+ * llama_layer_create.
+ *
+ * Errors.  Functions return 0 (LLAMA_OK) or a negative status; nothing is
+ * launched when a call fails its argument checks.  llama_layer_last_error()
+ * returns a thread-local message for the last failure on the calling thread.
+ */
+#ifndef LLAMA_LAYER_H
+#define LLAMA_LAYER_H
+
+#include <stdint.h>
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  LLAMA_OK = 0,
+  LLAMA_ERR_NULL = -1,         /* a required pointer is NULL */
+  LLAMA_ERR_INVALID = -2,      /* inconsistent sizes (see llama_layer_create) */
+  LLAMA_ERR_UNSUPPORTED = -3,  /* valid, but a shape this build has no kernel for */
+  LLAMA_ERR_CAPACITY = -4,     /* B*T above max_tokens, or T above max_pos */
+  LLAMA_ERR_HIP = -5,          /* a HIP runtime call failed */
+  LLAMA_ERR_ALLOC = -6         /* device or host allocation failed */
+};
+
+typedef enum { LLAMA_F32 = 0, LLAMA_BF16 = 1 } llama_dtype;
+
+typedef struct {
+  int32_t d_model;     /* hidden size d */
+  int32_t n_heads;     /* query heads H */
+  int32_t n_kv_heads;  /* key/value heads Hkv; H % Hkv == 0 (Hkv == H: MHA) */
+  int32_t head_dim;    /* dh (even); bf16 needs 128 */
+  int32_t d_ff;        /* intermediate size f */
+  float rms_eps;       /* RMSNorm epsilon, inside the square root (1e-6) */
+  float rope_base;     /* RoPE base (10000) */
+  int32_t max_pos;     /* cache capacity per sequence; every position < max_pos */
+  int32_t max_tokens;  /* largest B*T a call may pass; sizes the scratch */
+  int32_t dtype;       /* llama_dtype */
+} llama_layer_config;
+
+/* Device pointers to the caller's weights, each [out, in] row-major in the
+ * layer dtype.  llama_layer_create copies them into buffers the handle owns,
+ * so the caller may free them once create has returned. */
+typedef struct {
+  const void *attn_norm; /* [d] */
+  const void *wq;        /* [H*dh, d] */
+  const void *wk;        /* [Hkv*dh, d] */
+  const void *wv;        /* [Hkv*dh, d] */
+  const void *wo;        /* [d, H*dh] */
+  const void *ffn_norm;  /* [d] */
+  const void *w_gate;    /* [f, d] */
+  const void *w_up;      /* [f, d] */
+  const void *w_down;    /* [d, f] */
+} llama_layer_weights;
+
+typedef struct llama_layer llama_layer;
+
+/* Validate the config, allocate the handle's weights, RoPE table (cos and sin
+ * of p * base^(-2i/dh), built in fp64 on the host) and scratch, and copy the
+ * weights.  Blocks until the copies on `stream` are done.
+ * Errors: NULL (any pointer), INVALID (non-positive sizes, H % Hkv != 0, odd
+ * dh, non-finite eps/base), UNSUPPORTED (bf16 with dh != 128 or d, f not
+ * multiples of 128), HIP, ALLOC. */
+int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights* w,
+                       void* stream, llama_layer** out);
+
+/* Prefill: B sequences of T new tokens each.
+ * x, y       [B*T, d] (layer dtype)
+ * positions  [B*T] int32: token (b, t) sits at positions[b*T + t]; within a
+ *            sequence the positions are distinct and each is < max_pos.  Its
+ *            rotated key and its value are written to cache slot positions[.];
+ *            its query attends to slots 0 .. positions[.] of sequence b, so
+ *            slots below the sequence's new positions must already hold that
+ *            sequence's earlier keys and values (a chunked prefill continues a
+ *            cache; positions 0..T-1 start one).
+ * k_cache, v_cache  [B, Hkv, max_pos, dh] (layer dtype), updated in place.
+ * Errors: NULL, INVALID (B or T < 1), CAPACITY (B*T > max_tokens or
+ * T > max_pos), HIP (launch failure). */
+int llama_layer_prefill(llama_layer* layer, const void* x, void* y, const int32_t* positions,
+                        int32_t B, int32_t T, void* k_cache, void* v_cache, void* stream);
+
+/* Decode: one new token for each of B sequences — the same layer with T = 1.
+ * x, y [B, d]; positions [B] (normally each sequence's current cache length);
+ * caches as for prefill.  Same errors as prefill with T = 1. */
+int llama_layer_decode(llama_layer* layer, const void* x, void* y, const int32_t* positions,
+                       int32_t B, void* k_cache, void* v_cache, void* stream);
+
+/* Free everything the handle owns (waits for the device first).  NULL is a no-op. */
+void llama_layer_destroy(llama_layer* layer);
+
+/* Static description of a status code. */
+const char* llama_layer_strerror(int status);
+
+/* Thread-local detail of the last failure on this thread ("" if none). */
+const char* llama_layer_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* LLAMA_LAYER_H */

@@ -1,0 +1,180 @@
+"""Python binding of libllama_layer.so, the gfx950 decoder-layer library.
+
+Argument marshalling only: torch tensors are turned into device pointers,
+the current HIP stream is passed through, and status codes become
+exceptions.  Every step of the layer runs in the library's HIP kernels; there
+is no fallback of any kind — importing this package fails if the library has
+not been built (``python -m llama_decoder_block_amd.build``).
+
+The functions mirror the C ABI in include/llama_layer.h:
+
+    handle = llama_layer_create(config, weights)
+    llama_layer_prefill(handle, x, y, positions, B, T, k_cache, v_cache)
+    llama_layer_decode(handle, x, y, positions, B, k_cache, v_cache)
+    llama_layer_destroy(handle)
+
+``LlamaLayer`` wraps a handle with the same calls.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libllama_layer.so")
+
+LLAMA_OK = 0
+LLAMA_ERR_NULL = -1
+LLAMA_ERR_INVALID = -2
+LLAMA_ERR_UNSUPPORTED = -3
+LLAMA_ERR_CAPACITY = -4
+LLAMA_ERR_HIP = -5
+LLAMA_ERR_ALLOC = -6
+LLAMA_F32 = 0
+LLAMA_BF16 = 1
+
+EXPORTED = ("llama_layer_create", "llama_layer_prefill", "llama_layer_decode",
+            "llama_layer_destroy", "llama_layer_strerror", "llama_layer_last_error")
+
+
+class LlamaLayerConfig(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("d_ff", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+                ("rope_base", ctypes.c_float), ("max_pos", ctypes.c_int32),
+                ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+WEIGHT_NAMES = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
+
+
+class LlamaLayerWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
+
+
+class LlamaLayerError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m llama_decoder_block_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.llama_layer_create.argtypes = [ctypes.POINTER(LlamaLayerConfig),
+                                       ctypes.POINTER(LlamaLayerWeights), vp, ctypes.POINTER(vp)]
+    lib.llama_layer_create.restype = ctypes.c_int
+    lib.llama_layer_prefill.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp]
+    lib.llama_layer_prefill.restype = ctypes.c_int
+    lib.llama_layer_decode.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.llama_layer_decode.restype = ctypes.c_int
+    lib.llama_layer_destroy.argtypes = [vp]
+    lib.llama_layer_destroy.restype = None
+    lib.llama_layer_strerror.argtypes = [ctypes.c_int]
+    lib.llama_layer_strerror.restype = ctypes.c_char_p
+    lib.llama_layer_last_error.argtypes = []
+    lib.llama_layer_last_error.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def _check(status: int):
+    if status != LLAMA_OK:
+        detail = LIB.llama_layer_last_error().decode(errors="replace")
+        raise LlamaLayerError(status, f"{LIB.llama_layer_strerror(status).decode()}: {detail}")
+
+
+def _stream_ptr(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _ptr(t, name, dtype=None):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def make_config(d_model, n_heads, n_kv_heads, head_dim, d_ff, max_pos, max_tokens, dtype,
+                rms_eps=1e-6, rope_base=10000.0) -> LlamaLayerConfig:
+    return LlamaLayerConfig(int(d_model), int(n_heads), int(n_kv_heads), int(head_dim), int(d_ff),
+                            float(rms_eps), float(rope_base), int(max_pos), int(max_tokens),
+                            LLAMA_BF16 if dtype in ("bf16", LLAMA_BF16) else LLAMA_F32)
+
+
+def llama_layer_create(config: LlamaLayerConfig, weights: dict, stream=None) -> ctypes.c_void_p:
+    import torch
+    dt = torch.bfloat16 if config.dtype == LLAMA_BF16 else torch.float32
+    w = LlamaLayerWeights(*[_ptr(weights[n], n, dt) for n in WEIGHT_NAMES])
+    handle = ctypes.c_void_p()
+    _check(LIB.llama_layer_create(ctypes.byref(config), ctypes.byref(w), _stream_ptr(stream),
+                                  ctypes.byref(handle)))
+    return handle
+
+
+def llama_layer_prefill(handle, x, y, positions, B, T, k_cache, v_cache, stream=None):
+    import torch
+    _check(LIB.llama_layer_prefill(handle, _ptr(x, "x"), _ptr(y, "y"),
+                                   _ptr(positions, "positions", torch.int32), int(B), int(T),
+                                   _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+                                   _stream_ptr(stream)))
+
+
+def llama_layer_decode(handle, x, y, positions, B, k_cache, v_cache, stream=None):
+    import torch
+    _check(LIB.llama_layer_decode(handle, _ptr(x, "x"), _ptr(y, "y"),
+                                  _ptr(positions, "positions", torch.int32), int(B),
+                                  _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+                                  _stream_ptr(stream)))
+
+
+def llama_layer_destroy(handle):
+    LIB.llama_layer_destroy(handle)
+
+
+class LlamaLayer:
+    """One decoder layer bound to its weights (copied at construction)."""
+
+    def __init__(self, config: LlamaLayerConfig, weights: dict, stream=None):
+        self.config = config
+        self.handle = llama_layer_create(config, weights, stream)
+
+    def prefill(self, x, positions, k_cache, v_cache, y=None, stream=None):
+        """x [B, T, d] -> y [B, T, d]; positions [B, T] int32; caches updated in place."""
+        import torch
+        B, T = int(x.shape[0]), int(x.shape[1])
+        y = torch.empty_like(x) if y is None else y
+        llama_layer_prefill(self.handle, x, y, positions, B, T, k_cache, v_cache, stream)
+        return y
+
+    def decode(self, x, positions, k_cache, v_cache, y=None, stream=None):
+        """x [B, d] -> y [B, d]; positions [B] int32 (each sequence's cache length)."""
+        import torch
+        y = torch.empty_like(x) if y is None else y
+        llama_layer_decode(self.handle, x, y, positions, int(x.shape[0]), k_cache, v_cache, stream)
+        return y
+
+    def close(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            llama_layer_destroy(h)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

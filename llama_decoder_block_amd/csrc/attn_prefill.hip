@@ -1,0 +1,252 @@
+// Causal flash attention for prefill, bf16 in and out, head_dim 128.
+//
+// Computes, for every query token m (sequence b, position p_m) and query head
+// h, o = sum_j softmax_j(q.k_j / sqrt(128)) v_j over the cache slots
+// j = 0 .. p_m of sequence b and kv head g = h / (H / Hkv).
+//
+// Sources: "LMDrive LLM core inference unit" page, §2.3 LlamaAttention
+// (scores q k^T / sqrt(head_dim), additive mask, softmax, weights times v;
+// repeat_kv for grouped-query attention, which here is plain kv-head
+// indexing); "LLM mechanics lecture notes" §02.1 (M_ij = -inf for j > i,
+// added before the softmax, so future weights are exactly zero) and Ch.04
+// (a query reads every visible cached K/V).  The mask compares cache slot
+// (= position) with the query's position, which equals the notes' index mask
+// when positions are 0..T-1 and extends it to a prefill that continues a cache.
+//
+// gfx950 design.  One workgroup = 4 wavefronts = 128 queries of one head;
+// each wave owns 32 queries.  K/V tiles of 64 slots are staged in LDS (two
+// stages, register prefetch of the next tile).  Scores are computed
+// transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so each lane owns
+// one query: its row max / row sum need only a lane-pair exchange.  The K rows
+// fed to the MFMA are permuted (bits 2 and 3 of the row index swapped) so that
+// a lane's 16 score registers are two runs of 8 consecutive keys — exactly the
+// B operand of the next MFMA, O^T += V^T P^T, with no register shuffling.  V
+// is transposed to [dd][slot] while it is written to LDS.  P stays in fp32 in
+// the online softmax and is fed to the PV product as bf16 hi + bf16 lo (two
+// MFMAs), so the product sees P to about 16 bits instead of bf16's 8.
+// Query tiles are launched heaviest first (the causal workload grows with the
+// tile index).  Tiles that lie wholly above a wave's diagonal are skipped, and
+// the -inf mask is applied only on tiles that cross it.
+#include "common.h"
+
+#include <math.h>
+
+namespace llama {
+namespace {
+
+constexpr int DH = 128;
+constexpr int BQ = 128;          // queries per workgroup
+constexpr int BKV = 64;          // cache slots per tile
+constexpr int KSTR = DH + 8;     // LDS row of K, bf16 elements (272 B)
+constexpr int VSTR = BKV + 8;    // LDS row of V^T, bf16 elements (144 B)
+
+__device__ __forceinline__ int kappa(int m) {  // swap bits 2 and 3
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
+    const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ pos, bf16_t* __restrict__ o,
+    int T, int H, int Hkv, int max_pos, float scale_log2) {
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BKV * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DH * VSTR];
+
+  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest tiles first
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int g = h / (H / Hkv);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int hl = lane >> 5, lq = lane & 31;
+
+  // ---- this lane's query
+  const int t = qt * BQ + wave * 32 + lq;
+  const bool valid = t < T;
+  const size_t row = static_cast<size_t>(b) * T + (valid ? t : 0);
+  int pq = valid ? pos[row] : -1;
+  pq = min(pq, max_pos - 1);
+
+  // wave / workgroup position range
+  int wmax = pq, wmin = valid ? pq : 0x7fffffff;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    wmax = max(wmax, __shfl_xor(wmax, s, 64));
+    wmin = min(wmin, __shfl_xor(wmin, s, 64));
+  }
+  __shared__ int s_max[4];
+  if (lane == 0) s_max[wave] = wmax;
+  __syncthreads();
+  const int gmax = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  if (gmax < 0) return;  // no valid query in the whole tile (uniform)
+  const int ntiles = gmax / BKV + 1;
+
+  // ---- Q fragments (B operand of S^T = K Q^T): lane holds query lq, dims s*16 + hl*8 .. +8
+  const size_t qstride = static_cast<size_t>(H) * DH;
+  bf16x8 qf[8];
+  {
+    const bf16_t* qrow = q + row * qstride + static_cast<size_t>(h) * DH + hl * 8;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      uint4 u = valid ? *reinterpret_cast<const uint4*>(qrow + s * 16) : make_uint4(0, 0, 0, 0);
+      qf[s] = as_bf16x8(u);
+    }
+  }
+
+  // ---- K / V tile staging (buffer loads over this (b, g) cache slice)
+  const size_t slice = (static_cast<size_t>(b) * Hkv + g) * max_pos * DH;
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k_cache + slice, static_cast<uint32_t>(max_pos) * DH * 2u);
+  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v_cache + slice, static_cast<uint32_t>(max_pos) * DH * 2u);
+  // K: 64 rows x 16 chunks; thread handles chunks tid + 256 i
+  const int kr = tid >> 4, kc = tid & 15;
+  // V: thread handles slots 4*vg .. +3 at dims 8*vd .. +7
+  const int vg = tid >> 4, vd = tid & 15;
+  uint4 kreg[4], vreg[4];
+  auto gload = [&](int j0) {
+    const uint32_t so = static_cast<uint32_t>(j0) * DH * 2u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(k_rs, ((kr + 16 * i) * DH + kc * 8) * 2u, so);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(v_rs, ((4 * vg + i) * DH + vd * 8) * 2u, so);
+  };
+  auto lstore = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(&Ks[st][(kr + 16 * i) * KSTR + kc * 8]) = kreg[i];
+    // transpose 4 slots x 8 dims -> 8 rows (dims) of 4 slots
+    const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
+    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
+    const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
+    const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      // dims 2e (low halves) and 2e+1 (high halves)
+      uint2 lo, hi;
+      lo.x = __builtin_amdgcn_perm(v1[e], v0[e], 0x05040100);  // slot0.lo | slot1.lo << 16
+      lo.y = __builtin_amdgcn_perm(v3[e], v2[e], 0x05040100);
+      hi.x = __builtin_amdgcn_perm(v1[e], v0[e], 0x07060302);
+      hi.y = __builtin_amdgcn_perm(v3[e], v2[e], 0x07060302);
+      *reinterpret_cast<uint2*>(&Vt[st][(vd * 8 + 2 * e) * VSTR + 4 * vg]) = lo;
+      *reinterpret_cast<uint2*>(&Vt[st][(vd * 8 + 2 * e + 1) * VSTR + 4 * vg]) = hi;
+    }
+  };
+
+  f32x16 oacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+
+  const int k_row0 = kappa(lq) * KSTR + hl * 8;
+  const int v_row0 = lq * VSTR + hl * 8;
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int st = it & 1;
+    const int j0 = it * BKV;
+    if (it + 1 < ntiles) gload(j0 + BKV);
+
+    if (j0 <= wmax) {  // wave-uniform: skip tiles wholly above this wave's diagonal
+      // S^T for 2 blocks of 32 slots
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[st][k_row0 + kb * 32 * KSTR + s * 16]);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
+        }
+      }
+      // scale, mask, tile max. Register r of block kb is slot
+      // j0 + 32 kb + 16 (r/8) + 8 hl + r%8.
+      const bool need_mask = j0 + BKV - 1 > wmin;
+      float mt = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = sacc[kb][r] * scale_log2;
+          if (need_mask) {
+            const int j = j0 + 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
+            if (j > pq) v = -INFINITY;
+          }
+          sacc[kb][r] = v;
+          mt = fmaxf(mt, v);
+        }
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      const float m_new = fmaxf(m_run, mt);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2f(m_run - m_use);
+      m_run = m_new;
+      float lsum = 0.f;
+      uint32_t phi[2][2][4], plo[2][2][4];  // [kb][half][packed pair]
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = exp2f(sacc[kb][r] - m_use);
+          const float p1 = exp2f(sacc[kb][r + 1] - m_use);
+          lsum += p0 + p1;
+          const uint32_t hp = pack_bf16x2(p0, p1);
+          phi[kb][r >> 3][(r & 7) >> 1] = hp;
+          plo[kb][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0 - lo_bf16(hp), p1 - hi_bf16(hp));
+        }
+      l_run = l_run * alpha + lsum;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      // O^T += V^T P^T over 4 blocks of 16 slots
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const bf16x8 bh = as_bf16x8(make_uint4(phi[kb][half][0], phi[kb][half][1], phi[kb][half][2], phi[kb][half][3]));
+          const bf16x8 bl = as_bf16x8(make_uint4(plo[kb][half][0], plo[kb][half][1], plo[kb][half][2], plo[kb][half][3]));
+          const int kcol = (kb * 2 + half) * 16;
+#pragma unroll
+          for (int fd = 0; fd < 4; ++fd) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[st][v_row0 + fd * 32 * VSTR + kcol]);
+            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, oacc[fd], 0, 0, 0);
+            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, oacc[fd], 0, 0, 0);
+          }
+        }
+    }
+    if (it + 1 < ntiles) lstore(st ^ 1);
+    __syncthreads();
+  }
+
+  // ---- normalise and store: oacc[fd] register r is dim fd*32 + 8(r/4) + 4 hl + r%4
+  if (!valid) return;
+  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  bf16_t* orow = o + row * qstride + static_cast<size_t>(h) * DH;
+#pragma unroll
+  for (int fd = 0; fd < 4; ++fd)
+#pragma unroll
+    for (int rq = 0; rq < 4; ++rq) {
+      uint2 w;
+      w.x = pack_bf16x2(oacc[fd][4 * rq] * inv, oacc[fd][4 * rq + 1] * inv);
+      w.y = pack_bf16x2(oacc[fd][4 * rq + 2] * inv, oacc[fd][4 * rq + 3] * inv);
+      *reinterpret_cast<uint2*>(orow + fd * 32 + 8 * rq + 4 * hl) = w;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
+                               const int32_t* pos, bf16_t* o, int B, int T, int n_heads,
+                               int n_kv_heads, int max_pos, hipStream_t s) {
+  const dim3 grid((T + BQ - 1) / BQ, n_heads, B);
+  const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
+  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, o, T,
+                     n_heads, n_kv_heads, max_pos, scale_log2);
+  return hipGetLastError();
+}
+
+}  // namespace llama

@@ -1,0 +1,131 @@
+// Shared device helpers and internal launch entry points of the gfx950
+// decoder-layer kernels.  Everything here is internal to libllama_layer.so;
+// the public surface is include/llama_layer.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace llama {
+
+typedef uint16_t bf16_t;  // bf16 bit pattern as stored in memory
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Two fp32 -> packed pair of bf16 (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Raw buffer resource over [base, base + bytes): loads at or past the end
+// return zeros (hardware range check), which is how tiles handle ragged edges.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), 0x00020000);
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+
+// -------------------------------------------------------------------------
+// Internal launchers (each returns hipGetLastError() of its launch).
+// -------------------------------------------------------------------------
+
+// RMSNorm rows: out[r, :] = g * in[r, :] / sqrt(mean(in[r,:]^2) + eps).
+// in is bf16 (in_f32 = 0) or fp32 (in_f32 = 1); out is bf16 or fp32.
+hipError_t launch_rmsnorm(const void* in, int in_f32, const void* gain, int gain_f32, void* out,
+                          int out_f32, int rows, int d, float eps, hipStream_t s);
+
+// Tiled bf16 MFMA GEMM, C = A[M,K] . B[N,K]^T with a fused epilogue.
+struct QkvEpilogue {
+  bf16_t* q;               // [M, H*dh]
+  bf16_t* k_cache;         // [B, Hkv, max_pos, dh]
+  bf16_t* v_cache;
+  const int32_t* pos;      // [M]
+  const float* rope_cos;   // [max_pos, dh/2]
+  const float* rope_sin;
+  int T, n_heads, n_kv_heads, max_pos;
+};
+
+hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,
+                           const QkvEpilogue& ep, hipStream_t s);
+// out_f32[M,N] = A.W^T + resid_bf16[M,N]
+hipError_t launch_gemm_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
+                                    const bf16_t* resid, float* out, hipStream_t s);
+// out_bf16[M,N] = bf16(A.W^T + resid_f32[M,N])
+hipError_t launch_gemm_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
+                                     const float* resid, bf16_t* out, hipStream_t s);
+// W is the gate/up matrix packed in blocks of 64 rows [gate 64 | up 64]
+// (N = 2f); out[M, f] = bf16(SiLU(gate) * up)
+hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, int K,
+                              bf16_t* out, hipStream_t s);
+
+// Skinny (M <= 64 tokens) weight-streaming versions of the same four GEMMs.
+hipError_t launch_skinny_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,
+                             const QkvEpilogue& ep, hipStream_t s);
+hipError_t launch_skinny_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
+                                      const bf16_t* resid, float* out, hipStream_t s);
+hipError_t launch_skinny_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
+                                       const float* resid, bf16_t* out, hipStream_t s);
+hipError_t launch_skinny_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int f, int K,
+                                bf16_t* out, hipStream_t s);
+
+// Causal flash attention over the cache for prefill (bf16, dh = 128).
+// q/o [B*T, H*128]; the query of token m sees cache slots 0..pos[m].
+hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
+                               const int32_t* pos, bf16_t* o, int B, int T, int n_heads,
+                               int n_kv_heads, int max_pos, hipStream_t s);
+
+// Split-K decode attention (bf16, dh = 128) for one query per sequence,
+// followed by the combine of the splits.  part holds
+// B*H*n_split*(128+2) floats.
+int decode_attn_splits(int max_pos, int B, int n_kv_heads);
+hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
+                              const int32_t* pos, bf16_t* o, float* part, int n_split, int B,
+                              int n_heads, int n_kv_heads, int max_pos, hipStream_t s);
+
+// fp32 path (any shape).
+struct F32Layer {
+  int d, H, Hkv, dh, f, max_pos;
+  float eps;
+  const float* g1; const float* g2;
+  const float* wqkv; const float* wo; const float* wgu; const float* wd;  // wgu: [gate; up]
+  const float* rope_cos; const float* rope_sin;  // [max_pos, dh/2]
+  // scratch: xn [M,d], qkv [M,(H+2Hkv)dh], attn [M,H dh], x1 [M,d], gu [M,2f], h [M,f]
+  float* xn; float* qkv; float* attn; float* x1; float* gu; float* h;
+};
+hipError_t run_f32_layer(const F32Layer& L, const float* x, float* y, const int32_t* pos, int B,
+                         int T, float* k_cache, float* v_cache, hipStream_t s);
+
+}  // namespace llama

@@ -1,0 +1,381 @@
+// C ABI of the decoder-layer library: argument checks, weight packing, the
+// RoPE table, scratch memory, and the launch sequence of one layer call.
+//
+// Launch sequence (bf16), one pre-norm layer as on the "LMDrive LLM core
+// inference unit" page §2.5 and the "LLM mechanics lecture notes" Ch.02 block
+// equation:
+//   1  RMSNorm(x)                        -> xn          (bf16)
+//   2  xn Wqkv^T, RoPE, cache append     -> q scratch, K/V cache slots
+//   3  causal attention over the cache   -> o           (flash kernel for T > 1,
+//                                                        split-K kernel for T = 1)
+//   4  o Wo^T + x                        -> X'          (fp32 residual stream)
+//   5  RMSNorm(X')                       -> xn          (bf16)
+//   6  SiLU(xn Wg^T) * (xn Wu^T)         -> h           (bf16)
+//   7  h Wd^T + X'                       -> y           (bf16)
+// Steps 2, 4, 6, 7 use the tiled MFMA GEMMs when the call has more than 64
+// tokens and the weight-streaming GEMMs otherwise.
+#include "common.h"
+#include "../../include/llama_layer.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+#include <vector>
+
+using namespace llama;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(LLAMA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_OR_RETURN(expr, what)              \
+  do {                                         \
+    hipError_t e_ = (expr);                    \
+    if (e_ != hipSuccess) return hip_fail(e_, what); \
+  } while (0)
+
+constexpr int kSkinnyMaxTokens = 64;
+constexpr int kDecodeChunk = 64;  // sequences per split-K attention launch
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+}  // namespace
+
+struct llama_layer {
+  llama_layer_config cfg;
+  int device = 0;
+  size_t es = 2;  // element size of the layer dtype
+  // weights (owned)
+  void* wqkv = nullptr;  // [(H + 2 Hkv) dh, d]
+  void* wo = nullptr;    // [d, H dh]
+  void* wgu = nullptr;   // bf16: [2f, d] in 64-row blocks [gate | up]; fp32: [gate; up]
+  void* wd = nullptr;    // [d, f]
+  void* g1 = nullptr;
+  void* g2 = nullptr;
+  float* rope_cos = nullptr;  // [max_pos, dh/2]
+  float* rope_sin = nullptr;
+  // scratch (owned)
+  void* xn = nullptr;     // [max_tokens, d]
+  void* q = nullptr;      // bf16: [max_tokens, H dh]; fp32: qkv [max_tokens, (H+2Hkv) dh]
+  void* o = nullptr;      // [max_tokens, H dh]
+  float* x1 = nullptr;    // [max_tokens, d] fp32
+  void* h = nullptr;      // [max_tokens, f]
+  float* gu = nullptr;    // fp32 path: [max_tokens, 2f]
+  float* part = nullptr;  // split-K partials
+  int part_seqs = 0;      // sequences the partial buffer holds at once
+};
+
+namespace {
+
+void release(llama_layer* L) {
+  void* bufs[] = {L->wqkv, L->wo, L->wgu, L->wd, L->g1, L->g2, L->rope_cos, L->rope_sin,
+                  L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part};
+  for (void* p : bufs)
+    if (p) (void)hipFree(p);
+}
+
+int alloc(void** p, size_t bytes) {
+  if (bytes == 0) bytes = 16;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) {
+    *p = nullptr;
+    return fail(LLAMA_ERR_ALLOC, "hipMalloc(%zu bytes): %s", bytes, hipGetErrorString(e));
+  }
+  return LLAMA_OK;
+}
+
+int check_config(const llama_layer_config* c) {
+  if (c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->d_ff <= 0 ||
+      c->max_pos <= 0 || c->max_tokens <= 0)
+    return fail(LLAMA_ERR_INVALID, "sizes must be positive");
+  if (c->n_heads % c->n_kv_heads != 0)
+    return fail(LLAMA_ERR_INVALID, "n_heads (%d) must be a multiple of n_kv_heads (%d)", c->n_heads,
+                c->n_kv_heads);
+  if (c->head_dim % 2 != 0) return fail(LLAMA_ERR_INVALID, "head_dim must be even");
+  if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps) || !(c->rope_base > 0.f) || !isfinite(c->rope_base))
+    return fail(LLAMA_ERR_INVALID, "rms_eps must be finite and >= 0, rope_base finite and > 0");
+  if (c->dtype != LLAMA_F32 && c->dtype != LLAMA_BF16) return fail(LLAMA_ERR_INVALID, "unknown dtype");
+  if (c->dtype == LLAMA_BF16) {
+    if (c->head_dim != 128) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 kernels need head_dim 128");
+    if (c->d_model % 128 || c->d_ff % 128)
+      return fail(LLAMA_ERR_UNSUPPORTED, "bf16 kernels need d_model and d_ff multiples of 128");
+    // kernels address every operand with 32-bit byte offsets
+    const double lim = 4294967295.0;
+    const double d = c->d_model, f = c->d_ff, qd = 128.0 * c->n_heads,
+                 nqkv = 128.0 * (c->n_heads + 2 * c->n_kv_heads), mt = c->max_tokens + 256.0;
+    if (nqkv * d * 2 > lim || 2 * f * d * 2 > lim || d * qd * 2 > lim || d * f * 2 > lim ||
+        mt * f * 2 > lim || mt * d * 4 > lim || mt * qd * 2 > lim || 256.0 * c->max_pos > lim)
+      return fail(LLAMA_ERR_UNSUPPORTED, "an operand exceeds 4 GiB (32-bit buffer offsets)");
+  }
+  return LLAMA_OK;
+}
+
+int part_floats(const llama_layer_config& c, int* seqs) {
+  const int s = c.max_tokens < kDecodeChunk ? c.max_tokens : kDecodeChunk;
+  long long best = 0;
+  for (int b = 1; b <= s; ++b) {
+    const long long n = static_cast<long long>(b) * c.n_heads * decode_attn_splits(c.max_pos, b, c.n_kv_heads) * 130;
+    if (n > best) best = n;
+  }
+  *seqs = s;
+  return static_cast<int>(best);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* llama_layer_strerror(int status) {
+  switch (status) {
+    case LLAMA_OK: return "ok";
+    case LLAMA_ERR_NULL: return "null pointer argument";
+    case LLAMA_ERR_INVALID: return "invalid argument";
+    case LLAMA_ERR_UNSUPPORTED: return "unsupported shape";
+    case LLAMA_ERR_CAPACITY: return "call exceeds the handle's capacity";
+    case LLAMA_ERR_HIP: return "HIP runtime error";
+    case LLAMA_ERR_ALLOC: return "allocation failed";
+    default: return "unknown status";
+  }
+}
+
+const char* llama_layer_last_error(void) { return g_last_error.c_str(); }
+
+int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights* w, void* stream,
+                       llama_layer** out) {
+  g_last_error.clear();
+  if (!cfg || !w || !out) return fail(LLAMA_ERR_NULL, "cfg, weights and out must be non-null");
+  *out = nullptr;
+  const void* wp[] = {w->attn_norm, w->wq, w->wk, w->wv, w->wo, w->ffn_norm, w->w_gate, w->w_up, w->w_down};
+  for (const void* p : wp)
+    if (!p) return fail(LLAMA_ERR_NULL, "every weight pointer must be non-null");
+  int st = check_config(cfg);
+  if (st != LLAMA_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  llama_layer* L = new (std::nothrow) llama_layer();
+  if (!L) return fail(LLAMA_ERR_ALLOC, "host allocation failed");
+  L->cfg = *cfg;
+  L->es = cfg->dtype == LLAMA_BF16 ? 2 : 4;
+  hipError_t e = hipGetDevice(&L->device);
+  if (e != hipSuccess) { delete L; return hip_fail(e, "hipGetDevice"); }
+
+  const size_t es = L->es;
+  const size_t d = cfg->d_model, H = cfg->n_heads, Hkv = cfg->n_kv_heads, dh = cfg->head_dim,
+               f = cfg->d_ff, mt = cfg->max_tokens, mp = cfg->max_pos;
+  const size_t nq = H * dh, nkv = Hkv * dh;
+#define ALLOC_OR_FAIL(ptr, bytes)                               \
+  do {                                                          \
+    int a_ = alloc(reinterpret_cast<void**>(&(ptr)), (bytes));  \
+    if (a_ != LLAMA_OK) { release(L); delete L; return a_; }    \
+  } while (0)
+#define HIP_OR_FAIL(expr, what)                                      \
+  do {                                                               \
+    hipError_t e_ = (expr);                                          \
+    if (e_ != hipSuccess) { release(L); delete L; return hip_fail(e_, what); } \
+  } while (0)
+
+  ALLOC_OR_FAIL(L->wqkv, (nq + 2 * nkv) * d * es);
+  ALLOC_OR_FAIL(L->wo, d * nq * es);
+  ALLOC_OR_FAIL(L->wgu, 2 * f * d * es);
+  ALLOC_OR_FAIL(L->wd, d * f * es);
+  ALLOC_OR_FAIL(L->g1, d * es);
+  ALLOC_OR_FAIL(L->g2, d * es);
+  ALLOC_OR_FAIL(L->rope_cos, mp * (dh / 2) * sizeof(float));
+  ALLOC_OR_FAIL(L->rope_sin, mp * (dh / 2) * sizeof(float));
+  ALLOC_OR_FAIL(L->xn, mt * d * es);
+  ALLOC_OR_FAIL(L->o, mt * nq * es);
+  ALLOC_OR_FAIL(L->x1, mt * d * sizeof(float));
+  ALLOC_OR_FAIL(L->h, mt * f * es);
+  if (cfg->dtype == LLAMA_BF16) {
+    ALLOC_OR_FAIL(L->q, mt * nq * es);
+    const int pf = part_floats(*cfg, &L->part_seqs);
+    ALLOC_OR_FAIL(L->part, static_cast<size_t>(pf) * sizeof(float));
+  } else {
+    ALLOC_OR_FAIL(L->q, mt * (nq + 2 * nkv) * es);
+    ALLOC_OR_FAIL(L->gu, mt * 2 * f * sizeof(float));
+  }
+
+  const hipMemcpyKind dd = hipMemcpyDeviceToDevice;
+  char* qkv = static_cast<char*>(L->wqkv);
+  HIP_OR_FAIL(hipMemcpyAsync(qkv, w->wq, nq * d * es, dd, s), "copy wq");
+  HIP_OR_FAIL(hipMemcpyAsync(qkv + nq * d * es, w->wk, nkv * d * es, dd, s), "copy wk");
+  HIP_OR_FAIL(hipMemcpyAsync(qkv + (nq + nkv) * d * es, w->wv, nkv * d * es, dd, s), "copy wv");
+  HIP_OR_FAIL(hipMemcpyAsync(L->wo, w->wo, d * nq * es, dd, s), "copy wo");
+  HIP_OR_FAIL(hipMemcpyAsync(L->wd, w->w_down, d * f * es, dd, s), "copy w_down");
+  HIP_OR_FAIL(hipMemcpyAsync(L->g1, w->attn_norm, d * es, dd, s), "copy attn_norm");
+  HIP_OR_FAIL(hipMemcpyAsync(L->g2, w->ffn_norm, d * es, dd, s), "copy ffn_norm");
+  if (cfg->dtype == LLAMA_BF16) {
+    // 64-row blocks: packed rows [128 j, 128 j + 64) = gate rows [64 j, 64 j + 64),
+    // packed rows [128 j + 64, 128 j + 128) = up rows [64 j, 64 j + 64)
+    const size_t blk = 64 * d * es;
+    char* gu = static_cast<char*>(L->wgu);
+    HIP_OR_FAIL(hipMemcpy2DAsync(gu, 2 * blk, w->w_gate, blk, blk, f / 64, dd, s), "pack w_gate");
+    HIP_OR_FAIL(hipMemcpy2DAsync(gu + blk, 2 * blk, w->w_up, blk, blk, f / 64, dd, s), "pack w_up");
+  } else {
+    HIP_OR_FAIL(hipMemcpyAsync(L->wgu, w->w_gate, f * d * es, dd, s), "copy w_gate");
+    HIP_OR_FAIL(hipMemcpyAsync(static_cast<char*>(L->wgu) + f * d * es, w->w_up, f * d * es, dd, s),
+                "copy w_up");
+  }
+
+  // RoPE table: angle p * base^(-2i/dh), evaluated in fp64, stored fp32
+  {
+    const size_t half = dh / 2;
+    std::vector<float> cb(mp * half), sb(mp * half);
+    for (size_t i = 0; i < half; ++i) {
+      const double theta = pow(static_cast<double>(cfg->rope_base), -2.0 * static_cast<double>(i) / dh);
+      for (size_t p = 0; p < mp; ++p) {
+        const double a = static_cast<double>(p) * theta;
+        cb[p * half + i] = static_cast<float>(cos(a));
+        sb[p * half + i] = static_cast<float>(sin(a));
+      }
+    }
+    HIP_OR_FAIL(hipMemcpyAsync(L->rope_cos, cb.data(), cb.size() * sizeof(float), hipMemcpyHostToDevice, s),
+                "upload rope cos");
+    HIP_OR_FAIL(hipMemcpyAsync(L->rope_sin, sb.data(), sb.size() * sizeof(float), hipMemcpyHostToDevice, s),
+                "upload rope sin");
+    HIP_OR_FAIL(hipStreamSynchronize(s), "synchronize after create");
+  }
+#undef ALLOC_OR_FAIL
+#undef HIP_OR_FAIL
+  *out = L;
+  return LLAMA_OK;
+}
+
+void llama_layer_destroy(llama_layer* L) {
+  if (!L) return;
+  int cur = 0;
+  const bool have = hipGetDevice(&cur) == hipSuccess;
+  if (have && cur != L->device) (void)hipSetDevice(L->device);
+  (void)hipDeviceSynchronize();
+  release(L);
+  if (have && cur != L->device) (void)hipSetDevice(cur);
+  delete L;
+}
+
+static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos, int B, int T,
+                     void* kc, void* vc, hipStream_t s) {
+  const llama_layer_config& c = L->cfg;
+  const int M = B * T;
+  const int d = c.d_model, H = c.n_heads, Hkv = c.n_kv_heads, f = c.d_ff;
+
+  if (c.dtype == LLAMA_F32) {
+    F32Layer F{};
+    F.d = d; F.H = H; F.Hkv = Hkv; F.dh = c.head_dim; F.f = f; F.max_pos = c.max_pos; F.eps = c.rms_eps;
+    F.g1 = static_cast<const float*>(L->g1); F.g2 = static_cast<const float*>(L->g2);
+    F.wqkv = static_cast<const float*>(L->wqkv); F.wo = static_cast<const float*>(L->wo);
+    F.wgu = static_cast<const float*>(L->wgu); F.wd = static_cast<const float*>(L->wd);
+    F.rope_cos = L->rope_cos; F.rope_sin = L->rope_sin;
+    F.xn = static_cast<float*>(L->xn); F.qkv = static_cast<float*>(L->q); F.attn = static_cast<float*>(L->o);
+    F.x1 = L->x1; F.gu = L->gu; F.h = static_cast<float*>(L->h);
+    HIP_OR_RETURN(run_f32_layer(F, static_cast<const float*>(x), static_cast<float*>(y), pos, B, T,
+                                static_cast<float*>(kc), static_cast<float*>(vc), s),
+                  "fp32 layer launch");
+    return LLAMA_OK;
+  }
+
+  const bf16_t* xb = static_cast<const bf16_t*>(x);
+  bf16_t* yb = static_cast<bf16_t*>(y);
+  bf16_t* xn = static_cast<bf16_t*>(L->xn);
+  bf16_t* q = static_cast<bf16_t*>(L->q);
+  bf16_t* o = static_cast<bf16_t*>(L->o);
+  bf16_t* h = static_cast<bf16_t*>(L->h);
+  const bf16_t* wqkv = static_cast<const bf16_t*>(L->wqkv);
+  const bf16_t* wo = static_cast<const bf16_t*>(L->wo);
+  const bf16_t* wgu = static_cast<const bf16_t*>(L->wgu);
+  const bf16_t* wd = static_cast<const bf16_t*>(L->wd);
+  const int nqkv = (H + 2 * Hkv) * 128;
+  const bool skinny = M <= kSkinnyMaxTokens;
+
+  QkvEpilogue ep{};
+  ep.q = q;
+  ep.k_cache = static_cast<bf16_t*>(kc);
+  ep.v_cache = static_cast<bf16_t*>(vc);
+  ep.pos = pos;
+  ep.rope_cos = L->rope_cos;
+  ep.rope_sin = L->rope_sin;
+  ep.T = T;
+  ep.n_heads = H;
+  ep.n_kv_heads = Hkv;
+  ep.max_pos = c.max_pos;
+
+  HIP_OR_RETURN(launch_rmsnorm(xb, 0, L->g1, 0, xn, 0, M, d, c.rms_eps, s), "rmsnorm 1");
+  HIP_OR_RETURN(skinny ? launch_skinny_qkv(xn, wqkv, M, nqkv, d, ep, s)
+                       : launch_gemm_qkv(xn, wqkv, M, nqkv, d, ep, s),
+                "qkv projection");
+  if (T == 1) {
+    const size_t kv_seq = static_cast<size_t>(Hkv) * c.max_pos * 128;
+    for (int b0 = 0; b0 < B; b0 += L->part_seqs) {
+      const int nb = B - b0 < L->part_seqs ? B - b0 : L->part_seqs;
+      const int ns = decode_attn_splits(c.max_pos, nb, Hkv);
+      HIP_OR_RETURN(launch_attn_decode(q + static_cast<size_t>(b0) * H * 128,
+                                       static_cast<const bf16_t*>(kc) + b0 * kv_seq,
+                                       static_cast<const bf16_t*>(vc) + b0 * kv_seq, pos + b0,
+                                       o + static_cast<size_t>(b0) * H * 128, L->part, ns, nb, H, Hkv,
+                                       c.max_pos, s),
+                    "decode attention");
+    }
+  } else {
+    HIP_OR_RETURN(launch_attn_prefill(q, static_cast<const bf16_t*>(kc), static_cast<const bf16_t*>(vc), pos,
+                                      o, B, T, H, Hkv, c.max_pos, s),
+                  "prefill attention");
+  }
+  HIP_OR_RETURN(skinny ? launch_skinny_resid_f32out(o, wo, M, d, H * 128, xb, L->x1, s)
+                       : launch_gemm_resid_f32out(o, wo, M, d, H * 128, xb, L->x1, s),
+                "o_proj");
+  HIP_OR_RETURN(launch_rmsnorm(L->x1, 1, L->g2, 0, xn, 0, M, d, c.rms_eps, s), "rmsnorm 2");
+  HIP_OR_RETURN(skinny ? launch_skinny_swiglu(xn, wgu, M, f, d, h, s)
+                       : launch_gemm_swiglu(xn, wgu, M, 2 * f, d, h, s),
+                "gate/up projection");
+  HIP_OR_RETURN(skinny ? launch_skinny_resid_bf16out(h, wd, M, d, f, L->x1, yb, s)
+                       : launch_gemm_resid_bf16out(h, wd, M, d, f, L->x1, yb, s),
+                "down projection");
+  return LLAMA_OK;
+}
+
+static int checked_call(llama_layer* L, const void* x, void* y, const int32_t* pos, int B, int T,
+                        void* kc, void* vc, void* stream) {
+  g_last_error.clear();
+  if (!L || !x || !y || !pos || !kc || !vc)
+    return fail(LLAMA_ERR_NULL, "layer, x, y, positions and caches must be non-null");
+  if (B < 1 || T < 1) return fail(LLAMA_ERR_INVALID, "B and T must be >= 1 (got %d, %d)", B, T);
+  if (static_cast<long long>(B) * T > L->cfg.max_tokens)
+    return fail(LLAMA_ERR_CAPACITY, "B*T = %lld exceeds max_tokens = %d", static_cast<long long>(B) * T,
+                L->cfg.max_tokens);
+  if (T > L->cfg.max_pos) return fail(LLAMA_ERR_CAPACITY, "T = %d exceeds max_pos = %d", T, L->cfg.max_pos);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(kc) || !aligned16(vc))
+    return fail(LLAMA_ERR_INVALID, "x, y and the caches must be 16-byte aligned");
+  int cur = 0;
+  HIP_OR_RETURN(hipGetDevice(&cur), "hipGetDevice");
+  if (cur != L->device) HIP_OR_RETURN(hipSetDevice(L->device), "hipSetDevice");
+  const int st = run_layer(L, x, y, pos, B, T, kc, vc, static_cast<hipStream_t>(stream));
+  if (cur != L->device) (void)hipSetDevice(cur);
+  return st;
+}
+
+int llama_layer_prefill(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
+                        int32_t T, void* k_cache, void* v_cache, void* stream) {
+  return checked_call(L, x, y, positions, B, T, k_cache, v_cache, stream);
+}
+
+int llama_layer_decode(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
+                       void* k_cache, void* v_cache, void* stream) {
+  return checked_call(L, x, y, positions, B, 1, k_cache, v_cache, stream);
+}
+
+}  // extern "C"

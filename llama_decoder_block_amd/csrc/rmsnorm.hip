@@ -1,0 +1,136 @@
+// RMSNorm over rows: out = g * x / sqrt(mean(x^2) + eps).
+//
+// Source: "LMDrive LLM core inference unit" page, §2.1 LlamaRMSNorm (fp32
+// statistics, eps added to the mean square inside the root, learnable gain),
+// and the "LLM mechanics lecture notes", §02.3 RMSNorm.  The gain multiplies
+// in fp32 and the result is rounded once to the output type.
+//
+// One 64-wide wavefront per row.  Each lane keeps its share of the row in
+// registers (NV vectors of 8 elements, 16-byte bf16 or 32-byte fp32 loads,
+// consecutive lanes on consecutive vectors so a wave reads 1 KB contiguous per
+// load), so HBM sees exactly one read of x and one write of out.  The sum of
+// squares is reduced in fp32 with wavefront shuffles; no LDS, no barriers.
+#include "common.h"
+
+namespace llama {
+namespace {
+
+__device__ __forceinline__ void load8(const bf16_t* p, float v[8]) {
+  uint4 u = *reinterpret_cast<const uint4*>(p);
+  v[0] = lo_bf16(u.x); v[1] = hi_bf16(u.x); v[2] = lo_bf16(u.y); v[3] = hi_bf16(u.y);
+  v[4] = lo_bf16(u.z); v[5] = hi_bf16(u.z); v[6] = lo_bf16(u.w); v[7] = hi_bf16(u.w);
+}
+__device__ __forceinline__ void load8(const float* p, float v[8]) {
+  float4 a = *reinterpret_cast<const float4*>(p);
+  float4 b = *reinterpret_cast<const float4*>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16_t* p, const float v[8]) {
+  uint4 u;
+  u.x = pack_bf16x2(v[0], v[1]); u.y = pack_bf16x2(v[2], v[3]);
+  u.z = pack_bf16x2(v[4], v[5]); u.w = pack_bf16x2(v[6], v[7]);
+  *reinterpret_cast<uint4*>(p) = u;
+}
+__device__ __forceinline__ void store8(float* p, const float v[8]) {
+  *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
+}
+__device__ __forceinline__ float load1(const bf16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ void store1(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+__device__ __forceinline__ void store1(float* p, float v) { *p = v; }
+
+constexpr int kRowsPerBlock = 4;  // 4 waves, one row each
+
+// d % 8 == 0 and d <= NV * 512.
+template <typename TIn, typename TG, typename TOut, int NV>
+__global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const TIn* __restrict__ in,
+                                                          const TG* __restrict__ g,
+                                                          TOut* __restrict__ out, int rows,
+                                                          int d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const TIn* x = in + static_cast<size_t>(row) * d;
+  const int nvec = d >> 3;
+  float v[NV][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int vi = lane + j * kWave;
+    if (vi < nvec) {
+      load8(x + vi * 8, v[j]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
+    }
+  }
+  ss = warp_sum(ss);
+  const float inv = rsqrtf(ss / static_cast<float>(d) + eps);
+  TOut* y = out + static_cast<size_t>(row) * d;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int vi = lane + j * kWave;
+    if (vi < nvec) {
+      float gv[8];
+      load8(g + vi * 8, gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) v[j][e] = gv[e] * (v[j][e] * inv);
+      store8(y + vi * 8, v[j]);
+    }
+  }
+}
+
+// Any d: two passes over the row (the second read hits the cache).
+template <typename TIn, typename TG, typename TOut>
+__global__ __launch_bounds__(256) void rmsnorm_any_kernel(const TIn* __restrict__ in,
+                                                          const TG* __restrict__ g,
+                                                          TOut* __restrict__ out, int rows,
+                                                          int d, float eps) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const TIn* x = in + static_cast<size_t>(row) * d;
+  float ss = 0.f;
+  for (int i = lane; i < d; i += kWave) {
+    const float a = load1(x + i);
+    ss += a * a;
+  }
+  ss = warp_sum(ss);
+  const float inv = rsqrtf(ss / static_cast<float>(d) + eps);
+  TOut* y = out + static_cast<size_t>(row) * d;
+  for (int i = lane; i < d; i += kWave) store1(y + i, load1(g + i) * (load1(x + i) * inv));
+}
+
+template <typename TIn, typename TG, typename TOut>
+hipError_t dispatch(const void* in, const void* g, void* out, int rows, int d, float eps,
+                    hipStream_t s) {
+  const dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
+  const TIn* x = static_cast<const TIn*>(in);
+  const TG* gg = static_cast<const TG*>(g);
+  TOut* y = static_cast<TOut*>(out);
+  const int nv = (d + 511) / 512;
+  if (d % 8 == 0 && nv <= 16) {
+    if (nv <= 8)
+      hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 8>), grid, block, 0, s, x, gg, y, rows, d, eps);
+    else if (nv <= 10)
+      hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 10>), grid, block, 0, s, x, gg, y, rows, d, eps);
+    else
+      hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 16>), grid, block, 0, s, x, gg, y, rows, d, eps);
+  } else {
+    hipLaunchKernelGGL((rmsnorm_any_kernel<TIn, TG, TOut>), grid, block, 0, s, x, gg, y, rows, d, eps);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_rmsnorm(const void* in, int in_f32, const void* gain, int gain_f32, void* out,
+                          int out_f32, int rows, int d, float eps, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (!in_f32 && !gain_f32 && !out_f32) return dispatch<bf16_t, bf16_t, bf16_t>(in, gain, out, rows, d, eps, s);
+  if (in_f32 && !gain_f32 && !out_f32) return dispatch<float, bf16_t, bf16_t>(in, gain, out, rows, d, eps, s);
+  if (in_f32 && gain_f32 && out_f32) return dispatch<float, float, float>(in, gain, out, rows, d, eps, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace llama

@@ -1,0 +1,85 @@
+"""Shared helpers of the GPU parity tests: build a layer from a workload, run
+it through the C ABI, run the oracle on host copies of the very same tensors,
+and compare."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import synth
+from oracle import llama_oracle as O
+
+# bf16 gate: max-abs error <= 2e-2 x RMS of the oracle output (rounding-point oracle)
+BF16_RMS_GATE = 2e-2
+# fp32 gate: max-abs error <= 1e-4 against the plain oracle
+F32_ABS_GATE = 1e-4
+
+
+def f64(t) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def layer_config(lib, wl: synth.Workload, max_tokens: int, max_pos: int | None = None):
+    return lib.make_config(wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff,
+                           max_pos or wl.max_pos, max_tokens, wl.dtype, wl.rms_eps, wl.rope_base)
+
+
+def oracle_weights(w: dict) -> dict:
+    return {k: f64(v) for k, v in w.items()}
+
+
+def oracle_prefill(wl, w64, x, pos, kc, vc, rows=None, bf16_points=None):
+    if bf16_points is None:
+        bf16_points = wl.dtype == "bf16"
+    return O.decoder_layer(f64(x), f64(pos).astype(np.int64), w64, f64(kc), f64(vc),
+                           n_heads=wl.n_heads, n_kv_heads=wl.n_kv_heads, eps=wl.rms_eps,
+                           rope_base=wl.rope_base, bf16_points=bf16_points, rows=rows)
+
+
+def rms(a) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    return float(np.sqrt(np.mean(a * a)))
+
+
+def rel_err(got, ref) -> float:
+    """max |got - ref| / RMS(ref)"""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    return float(np.max(np.abs(got - ref)) / max(rms(ref), 1e-30))
+
+
+def assert_bf16_output(got, ref, what=""):
+    e = rel_err(got, ref)
+    print(f"  {what}: max|err|/rms = {e:.5f} (gate {BF16_RMS_GATE})", flush=True)
+    assert np.all(np.isfinite(got)), what
+    assert e <= BF16_RMS_GATE, f"{what}: {e}"
+
+
+def assert_bf16_storage(got, ref, what=""):
+    """Cache entries are bf16 values: each must be the bf16 rounding of a value
+    within accumulation noise of the oracle's unrounded one, i.e. within one
+    bf16 relative step 2^-8 of it (rounding contributes at most 2^-9), plus an
+    absolute floor for entries near zero."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    r = rms(ref)
+    bound = 2.0**-8 * np.abs(ref) + 2e-3 * r
+    worst = float(np.max(np.abs(got - ref) - bound))
+    print(f"  {what}: max|err|/rms = {rel_err(got, ref):.5f}, worst excess over rounding "
+          f"bound = {worst:.3g}", flush=True)
+    assert worst <= 0.0, f"{what}: exceeds the bf16 storage bound by {worst}"
+
+
+def assert_f32(got, ref, what=""):
+    e = float(np.max(np.abs(np.asarray(got, np.float64) - ref)))
+    print(f"  {what}: max|err| = {e:.3g} (gate {F32_ABS_GATE})", flush=True)
+    assert e <= F32_ABS_GATE, f"{what}: {e}"
+
+
+def sample_rows(B, T, seed, extra=8):
+    """Flat token indices: tile edges, the ends, and a few random rows per sequence."""
+    rng = np.random.default_rng(seed)
+    base = [0, 1, 2, 31, 32, 63, 64, 127, 128, 129, 255, 256, 511, 1000, 2047, 2048, T - 2, T - 1]
+    rows = []
+    for b in range(B):
+        ts = {t for t in base if 0 <= t < T} | set(rng.integers(0, T, size=extra).tolist())
+        rows += [b * T + t for t in sorted(ts)]
+    return rows

@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/llama_layer.h declares, and rejects bad arguments before it touches
+the GPU (every case here returns from argument validation, so no HIP call is
+made).  No GPU is needed."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import llama_decoder_block_amd as lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "llama_layer.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(llama_layer_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert _declared_functions() == sorted(lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (llama_layer_[a-z_]+)\b", out))
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(lib.LIB, name)
+
+
+def test_strerror_covers_every_status():
+    for st in (lib.LLAMA_OK, lib.LLAMA_ERR_NULL, lib.LLAMA_ERR_INVALID, lib.LLAMA_ERR_UNSUPPORTED,
+               lib.LLAMA_ERR_CAPACITY, lib.LLAMA_ERR_HIP, lib.LLAMA_ERR_ALLOC):
+        msg = lib.LIB.llama_layer_strerror(st).decode()
+        assert msg and msg != "unknown status"
+    assert lib.LIB.llama_layer_strerror(12345).decode() == "unknown status"
+
+
+def _weights(ptr=4096):
+    return lib.LlamaLayerWeights(*([ctypes.c_void_p(ptr)] * len(lib.WEIGHT_NAMES)))
+
+
+def _create(cfg, w):
+    h = ctypes.c_void_p()
+    st = lib.LIB.llama_layer_create(ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(h))
+    return st, h
+
+
+def _cfg(**kw):
+    base = dict(d_model=512, n_heads=4, n_kv_heads=2, head_dim=128, d_ff=1408, max_pos=64,
+                max_tokens=64, dtype="bf16")
+    base.update(kw)
+    return lib.make_config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_heads=6, n_kv_heads=4), lib.LLAMA_ERR_INVALID),          # H % Hkv != 0
+    (dict(head_dim=127, dtype="f32"), lib.LLAMA_ERR_INVALID),        # odd head_dim
+    (dict(d_model=0), lib.LLAMA_ERR_INVALID),
+    (dict(max_pos=-1), lib.LLAMA_ERR_INVALID),
+    (dict(head_dim=64), lib.LLAMA_ERR_UNSUPPORTED),                  # bf16 needs dh 128
+    (dict(d_ff=1400), lib.LLAMA_ERR_UNSUPPORTED),                    # bf16 needs f % 128 == 0
+    (dict(d_model=520), lib.LLAMA_ERR_UNSUPPORTED),
+])
+def test_create_rejects_bad_configs(kw, status):
+    st, h = _create(_cfg(**kw), _weights())
+    assert st == status
+    assert not h.value
+    assert lib.LIB.llama_layer_last_error().decode()
+
+
+def test_create_rejects_null_weights_and_bad_eps():
+    w = _weights()
+    w.w_up = None
+    st, _ = _create(_cfg(), w)
+    assert st == lib.LLAMA_ERR_NULL
+    cfg = _cfg()
+    cfg.rms_eps = float("nan")
+    st, _ = _create(cfg, _weights())
+    assert st == lib.LLAMA_ERR_INVALID
+    st = lib.LIB.llama_layer_create(None, None, None, None)
+    assert st == lib.LLAMA_ERR_NULL
+
+
+def test_calls_reject_null_handle():
+    p = ctypes.c_void_p(4096)
+    assert lib.LIB.llama_layer_prefill(None, p, p, p, 1, 1, p, p, None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_decode(None, p, p, p, 1, p, p, None) == lib.LLAMA_ERR_NULL
+    lib.LIB.llama_layer_destroy(None)  # no-op
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    with pytest.raises(ValueError):
+        lib._ptr(torch.zeros(4), "x")

@@ -1,0 +1,207 @@
+"""GPU parity of the HIP decoder layer against the CPU oracle at small shapes
+that still span several tiles and ragged tails, plus edge cases and
+properties.  Every call goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+import llama_decoder_block_amd as lib  # noqa: E402  (fails loudly if the library is not built)
+
+DEV = "cuda"
+
+
+def _wl(name="small", dtype="bf16", d=512, H=4, Hkv=2, f=1408, B=2, T=300, prior=0, steps=0,
+        seed=7):
+    return synth.Workload(name, dtype, d, H, Hkv, 128 if dtype == "bf16" else d // H, f, B, T,
+                          prior=prior, decode_steps=steps, seed=seed)
+
+
+def _setup(wl, random_gains=False, max_tokens=None):
+    w = synth.make_weights(wl, DEV, random_gains=random_gains)
+    x = synth.make_x(wl, (wl.batch, wl.seq), device=DEV)
+    kc, vc = synth.make_cache(wl, DEV)
+    pos = synth.prefill_positions(wl.batch, wl.seq, start=wl.prior, device=DEV)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, max_tokens or wl.batch * wl.seq), w)
+    return w, x, kc, vc, pos, layer
+
+
+def _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc):
+    torch.cuda.synchronize()
+    w64 = G.oracle_weights(w)
+    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)
+    written = slice(wl.prior, wl.prior + wl.seq)
+    kg, vg = G.f64(kc), G.f64(vc)
+    if wl.dtype == "bf16":
+        G.assert_bf16_output(G.f64(y), yo, "y")
+        G.assert_bf16_storage(kg[:, :, written], ko[:, :, written], "K written")
+        G.assert_bf16_storage(vg[:, :, written], vo[:, :, written], "V written")
+        yp, _, _ = G.oracle_prefill(wl, w64, x, pos, kc0, vc0, bf16_points=False)
+        print(f"  (vs plain oracle: y max|err|/rms = {G.rel_err(G.f64(y), yp):.5f})")
+    else:
+        G.assert_f32(G.f64(y), yo, "y")
+        G.assert_f32(kg, ko, "K cache")
+        G.assert_f32(vg, vo, "V cache")
+    # slots this call did not write are untouched
+    np.testing.assert_array_equal(kg[:, :, :wl.prior], G.f64(kc0)[:, :, :wl.prior])
+    np.testing.assert_array_equal(kg[:, :, wl.prior + wl.seq:], G.f64(kc0)[:, :, wl.prior + wl.seq:])
+    np.testing.assert_array_equal(vg[:, :, wl.prior + wl.seq:], G.f64(vc0)[:, :, wl.prior + wl.seq:])
+
+
+def test_tiny_fp32_layer():
+    """The tiny fp32 workload: B=1, T=16, d=64, 4 heads of 16, f=172."""
+    wl = synth.WORKLOADS["tiny_f32"]
+    print(f"case {wl}", flush=True)
+    w, x, kc, vc, pos, layer = _setup(wl)
+    kc0, vc0 = kc.clone(), vc.clone()
+    y = layer.prefill(x, pos, kc, vc)
+    _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(d=512, H=4, Hkv=2, f=1408, B=2, T=300),      # tiled GEMMs, ragged M and query tile
+    dict(d=384, H=3, Hkv=1, f=640, B=1, T=129),       # odd heads, MQA, N not a multiple of 256
+    dict(d=256, H=2, Hkv=2, f=384, B=3, T=5),         # 15 tokens: weight-streaming GEMMs
+    dict(d=1024, H=8, Hkv=2, f=2816, B=1, T=1),       # single token prefill
+    dict(d=512, H=4, Hkv=4, f=1408, B=1, T=64),       # 64 tokens: largest skinny call
+    dict(d=512, H=4, Hkv=4, f=1408, B=1, T=65),       # 65 tokens: smallest tiled call
+])
+def test_bf16_prefill_small(shape):
+    wl = _wl(**shape)
+    print(f"case {shape}", flush=True)
+    w, x, kc, vc, pos, layer = _setup(wl, random_gains=True)
+    kc0, vc0 = kc.clone(), vc.clone()
+    y = layer.prefill(x, pos, kc, vc)
+    _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunked_prefill_over_prior_cache(dtype):
+    """Positions p0..p0+T-1 over a cache whose first p0 slots hold earlier K/V."""
+    if dtype == "bf16":
+        wl = _wl(dtype="bf16", d=512, H=4, Hkv=2, f=1408, B=2, T=100, prior=150)
+    else:
+        wl = _wl(dtype="f32", d=64, H=4, Hkv=2, f=96, B=2, T=7, prior=9)
+    print(f"case {wl}", flush=True)
+    w, x, kc, vc, pos, layer = _setup(wl)
+    kc0, vc0 = kc.clone(), vc.clone()
+    y = layer.prefill(x, pos, kc, vc)
+    _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc)
+
+
+@pytest.mark.parametrize("B,Hkv", [(5, 2), (1, 1), (40, 4)])
+def test_bf16_decode_steps(B, Hkv):
+    """Prefill 37 tokens, then 3 decode steps; each step checked against the
+    oracle continuing from its own cache."""
+    wl = _wl(d=512, H=4, Hkv=Hkv, f=1408, B=B, T=37, steps=3, seed=11)
+    print(f"case B={B} Hkv={Hkv}", flush=True)
+    w, x, kc, vc, pos, layer = _setup(wl, max_tokens=B * 37)
+    w64 = G.oracle_weights(w)
+    kc0, vc0 = kc.clone(), vc.clone()
+    layer.prefill(x, pos, kc, vc)
+    torch.cuda.synchronize()
+    _, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)
+    from oracle import llama_oracle as O
+    for s in range(wl.decode_steps):
+        p = wl.seq + s
+        xs = synth.make_x(wl, (B,), tensor_id=synth.TID_DECODE_BASE + s, device=DEV)
+        ps = torch.full((B,), p, dtype=torch.int32, device=DEV)
+        ys = layer.decode(xs, ps, kc, vc)
+        torch.cuda.synchronize()
+        yo, ko, vo = O.decoder_layer_decode(G.f64(xs), np.full(B, p), w64, ko, vo,
+                                            n_heads=wl.n_heads, n_kv_heads=wl.n_kv_heads,
+                                            bf16_points=True)
+        G.assert_bf16_output(G.f64(ys), yo, f"decode step {s} y")
+        G.assert_bf16_storage(G.f64(kc)[:, :, p], ko[:, :, p], f"decode step {s} K")
+        G.assert_bf16_storage(G.f64(vc)[:, :, p], vo[:, :, p], f"decode step {s} V")
+
+
+def test_decode_matches_prefill_of_one_more_token():
+    """Prefill T, decode token T == row T of a prefill of T+1 (within bf16)."""
+    wl = _wl(d=512, H=4, Hkv=2, f=1408, B=2, T=81, seed=13)
+    w = synth.make_weights(wl, DEV)
+    x = synth.make_x(wl, (2, 82), device=DEV)
+    cfg = G.layer_config(lib, wl, max_tokens=2 * 82, max_pos=82)
+    layer = lib.LlamaLayer(cfg, w)
+    kc1 = torch.zeros((2, 2, 82, 128), dtype=torch.bfloat16, device=DEV)
+    vc1 = torch.zeros_like(kc1)
+    y_full = layer.prefill(x, synth.prefill_positions(2, 82, device=DEV), kc1, vc1)
+    kc2, vc2 = torch.zeros_like(kc1), torch.zeros_like(kc1)
+    layer.prefill(x[:, :81].contiguous(), synth.prefill_positions(2, 81, device=DEV), kc2, vc2)
+    y_dec = layer.decode(x[:, 81].contiguous(), torch.full((2,), 81, dtype=torch.int32, device=DEV),
+                         kc2, vc2)
+    torch.cuda.synchronize()
+    G.assert_bf16_output(G.f64(y_dec), G.f64(y_full[:, 81]), "decode vs prefill row")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_zero_output_projections_give_identity(dtype):
+    wl = _wl(dtype=dtype, d=256 if dtype == "bf16" else 64, H=2 if dtype == "bf16" else 4, Hkv=2,
+             f=384 if dtype == "bf16" else 96, B=2, T=70)
+    w = synth.make_weights(wl, DEV)
+    w["wo"].zero_()
+    w["w_down"].zero_()
+    x = synth.make_x(wl, (2, 70), device=DEV)
+    kc, vc = synth.make_cache(wl, DEV)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, 140), w)
+    y = layer.prefill(x, synth.prefill_positions(2, 70, device=DEV), kc, vc)
+    torch.cuda.synchronize()
+    assert torch.equal(y, x)
+
+
+def test_gqa_equals_mha_with_repeated_kv_weights():
+    """GQA with Hkv=2 computes what MHA computes when each kv head's weights
+    are repeated for its group of query heads."""
+    wl = _wl(d=512, H=4, Hkv=2, f=1408, B=1, T=200, seed=17)
+    w = synth.make_weights(wl, DEV)
+    x = synth.make_x(wl, (1, 200), device=DEV)
+    pos = synth.prefill_positions(1, 200, device=DEV)
+    kc, vc = synth.make_cache(wl, DEV)
+    y_gqa = lib.LlamaLayer(G.layer_config(lib, wl, 200), w).prefill(x, pos, kc, vc)
+    wl_mha = synth.scaled(wl, n_kv_heads=4)
+    w_mha = dict(w)
+    w_mha["wk"] = w["wk"].view(2, 128, 512).repeat_interleave(2, dim=0).reshape(512, 512).contiguous()
+    w_mha["wv"] = w["wv"].view(2, 128, 512).repeat_interleave(2, dim=0).reshape(512, 512).contiguous()
+    kc2, vc2 = synth.make_cache(wl_mha, DEV)
+    y_mha = lib.LlamaLayer(G.layer_config(lib, wl_mha, 200), w_mha).prefill(x, pos, kc2, vc2)
+    torch.cuda.synchronize()
+    assert torch.equal(y_gqa, y_mha)
+    assert torch.equal(kc2[:, 0::2], kc) and torch.equal(kc2[:, 1::2], kc)
+
+
+def test_bitwise_deterministic():
+    wl = _wl(d=512, H=4, Hkv=2, f=1408, B=2, T=300, seed=19)
+    w, x, kc, vc, pos, layer = _setup(wl)
+    y1 = layer.prefill(x, pos, kc, vc).clone()
+    k1 = kc.clone()
+    y2 = layer.prefill(x, pos, kc, vc)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(k1, kc)
+
+
+def test_in_place_output():
+    wl = _wl(d=512, H=4, Hkv=2, f=1408, B=1, T=90, seed=23)
+    w, x, kc, vc, pos, layer = _setup(wl)
+    y = layer.prefill(x, pos, kc, vc)
+    x2 = x.clone()
+    kc.zero_(); vc.zero_()
+    layer.prefill(x2, pos, kc, vc, y=x2)
+    torch.cuda.synchronize()
+    assert torch.equal(x2, y)
+
+
+def test_capacity_and_alignment_errors():
+    wl = _wl(d=256, H=2, Hkv=2, f=384, B=1, T=8)
+    w, x, kc, vc, pos, layer = _setup(wl, max_tokens=8)
+    big = synth.make_x(wl, (2, 8), device=DEV)
+    with pytest.raises(lib.LlamaLayerError) as e:
+        layer.prefill(big, synth.prefill_positions(2, 8, device=DEV), kc, vc)
+    assert e.value.status == lib.LLAMA_ERR_CAPACITY
+    flat = torch.zeros(8 * 256 + 1, dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(lib.LlamaLayerError) as e:
+        lib.llama_layer_prefill(layer.handle, x, flat[1:], pos, 1, 8, kc, vc)
+    assert e.value.status == lib.LLAMA_ERR_INVALID
