@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 decoder-layer library on one MI355X.
+
+Headline: LLaMA-7B-shape single-layer prefill (B=1, T=2048, d=4096, 32 heads
+x 128, f=11008, bf16 with fp32 accumulation), tokens/s of the whole layer.
+One step = one full layer call (RMSNorm, QKV + RoPE + cache append, causal
+attention, o_proj + residual, RMSNorm, gate/up + SwiGLU, down + residual)
+over the batch; inputs and weights are resident in HBM before timing starts.
+
+Also reported on the same line:
+  roofline      the dominant kernel (gate/up projection + SwiGLU, 43% of the
+                layer's flops): algorithmic flops / its average duration,
+                timed live with HIP events on the library's stream during the
+                timed steps, against the 2.5 PFLOP/s dense bf16 MFMA peak;
+  decode        LLaMA-7B-shape decode step (32 sequences at position 4095):
+                algorithmic bytes / step time against 8 TB/s HBM;
+  cpu_baseline  the CPU oracle on a bounded prefix of the same prefill
+                workload, on this host's cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(wl, T, B):
+    """2 N P_lin + causal attention 4 dh H sum_t (t + 1) (positions 0..T-1)."""
+    d, H, Hkv, dh, f = wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff
+    p_lin = d * (H + 2 * Hkv) * dh + H * dh * d + 3 * d * f
+    attn = 4 * dh * H * B * (T * (T + 1) // 2)
+    return 2 * B * T * p_lin + attn
+
+
+def decode_bytes(wl, B, pos):
+    """Weights and gains once, every sequence's prior K/V, the appended K/V,
+    x in and y out (bf16)."""
+    d, H, Hkv, dh, f = wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff
+    es = 2
+    p_lin = d * (H + 2 * Hkv) * dh + H * dh * d + 3 * d * f
+    return es * (p_lin + 2 * d) + es * B * 2 * Hkv * dh * pos + es * B * 2 * Hkv * dh + 2 * es * B * d
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    p = os.path.join(PROFILES, "gate_up_swiglu_llama7b_prefill_pmc.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        prof = json.load(f)
+    if prof.get("source_sha") != source_sha(kernel_src):
+        return None
+    return prof.get("traffic_bytes_per_launch")
+
+
+def bench_prefill(lib, synth, G, steps, warmup):
+    import torch
+    wl = synth.WORKLOADS["llama7b_prefill"]
+    B, T = wl.batch, wl.seq
+    w = synth.make_weights(wl, "cuda")
+    x = synth.make_x(wl, (B, T), device="cuda")
+    pos = synth.prefill_positions(B, T, device="cuda")
+    kc, vc = synth.make_cache(wl, "cuda")
+    y = torch.empty_like(x)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, B * T), w)
+    for _ in range(warmup):
+        layer.prefill(x, pos, kc, vc, y=y)
+    torch.cuda.synchronize()
+    lib.llama_layer_profile(layer.handle, True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        layer.prefill(x, pos, kc, vc, y=y)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    step_ms, calls = lib.llama_layer_profile_read(layer.handle)
+    lib.llama_layer_profile(layer.handle, False)
+    assert calls == steps, (calls, steps)
+    avg = {k: v / calls for k, v in step_ms.items()}
+    host = {"w": w, "x": x, "pos": pos, "kc": kc, "vc": vc}
+    layer.close()
+    return wl, (t1 - t0), avg, host
+
+
+def bench_decode(lib, synth, G, steps, warmup):
+    import torch
+    wl = synth.WORKLOADS["llama7b_decode"]
+    B, p = wl.batch, wl.prior
+    w = synth.make_weights(wl, "cuda")
+    x = synth.make_x(wl, (B,), device="cuda")
+    pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+    kc, vc = synth.make_cache(wl, "cuda")
+    y = torch.empty_like(x)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, B), w)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")  # > L2 + Infinity Cache
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        layer.decode(x, pos, kc, vc, y=y)
+    times = []
+    for _ in range(steps):
+        flush.zero_()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        layer.decode(x, pos, kc, vc, y=y)  # a repeated decode at one position is idempotent
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in times)
+    med = ms[len(ms) // 2]
+    nbytes = decode_bytes(wl, B, p)
+    layer.close()
+    return {"workload": "llama7b_decode", "batch": B, "position": p, "ms_per_step_median": med,
+            "bytes_per_step": nbytes, "GBps": nbytes / med / 1e6,
+            "hbm_frac": nbytes / med / 1e6 / PEAK_HBM_GBPS, "tokens_per_s": B / med * 1e3,
+            "cache_flushed_between_steps": True}
+
+
+def cpu_baseline(wl, host, budget_s):
+    """The oracle as it stands (plain fp64 numpy) on a prefix of the same layer
+    call: tokens 0..T'-1 of the sequence, T' doubled from 64 until one run takes
+    a third of the budget (causal, so these are exactly the first T' outputs)."""
+    import numpy as np
+    from oracle import llama_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count()
+    f64 = lambda t: t.detach().cpu().double().numpy()  # noqa: E731
+    w64 = {k: f64(v) for k, v in host["w"].items()}
+    x, pos, kc, vc = f64(host["x"]), f64(host["pos"]).astype(np.int64), host["kc"], host["vc"]
+    kc0 = np.zeros(tuple(kc.shape))
+    tp, last = 64, None
+    while True:
+        t0 = time.perf_counter()
+        O.decoder_layer(x[:, :tp], pos[:, :tp], w64, kc0, kc0, n_heads=wl.n_heads,
+                        n_kv_heads=wl.n_kv_heads, eps=wl.rms_eps, rope_base=wl.rope_base)
+        dt = time.perf_counter() - t0
+        last = (tp, dt)
+        log(f"cpu oracle: {tp} tokens in {dt:.2f} s")
+        if dt >= budget_s / 3 or tp >= wl.seq:
+            break
+        tp = min(wl.seq, tp * 2)
+    tp, dt = last
+    cpu = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": wl.batch * tp / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {tp} of the {wl.seq} tokens of the llama7b_prefill layer call, plain "
+                      f"fp64 numpy oracle, {dt:.2f} s",
+            "host_cpu": cpu, "host_logical_cpus": os.cpu_count()}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=30)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=30.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): this library "
+              "is a single-GPU decoder layer and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": 1 << 30, "launches": 3}))
+        return
+
+    import llama_decoder_block_amd as lib
+    import synth
+    from tests import gpu_helpers as G
+
+    wl, elapsed, step_avg, host = bench_prefill(lib, synth, G, args.steps, args.warmup)
+    B, T = wl.batch, wl.seq
+    ms_per_step = elapsed / args.steps * 1e3
+    tokens_per_s = B * T * args.steps / elapsed
+    flops = prefill_flops(wl, T, B)
+    gu_flops = 2 * B * T * (2 * wl.d_ff) * wl.d_model
+    gu_ms = step_avg["gate_up_swiglu"]
+    gu_tflops = gu_flops / (gu_ms * 1e-3) / 1e12
+    kernel_src = os.path.join(ROOT, "llama_decoder_block_amd", "csrc", "gemm.hip")
+    out = {
+        "metric": "decoder-layer tokens/s (7B-shape prefill) + decode GB/s; % MFMA/HBM roofline",
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": "llama7b_prefill", "global_batch": B, "seq_len": T,
+                   "d_model": wl.d_model, "n_heads": wl.n_heads, "n_kv_heads": wl.n_kv_heads,
+                   "head_dim": wl.head_dim, "d_ff": wl.d_ff, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "gate_up_swiglu (gemm_bf16_kernel<256,256,SWIGLU>)",
+                     "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gu_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic_from_profile(kernel_src),
+                     "flops_per_launch": gu_flops, "avg_launch_ms": gu_ms},
+        "layer": {"flops_per_step": flops, "tflops": flops / (ms_per_step * 1e-3) / 1e12,
+                  "mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                  "step_ms_by_kernel": step_avg},
+    }
+    if not args.no_decode:
+        out["decode"] = bench_decode(lib, synth, G, args.decode_steps, 3)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -133,6 +133,26 @@ int llama_layer_decode(llama_layer* layer, const void* x, void* y, const int32_t
 /* Free everything the handle owns (waits for the device first).  NULL is a no-op. */
 void llama_layer_destroy(llama_layer* layer);
 
+/* ---- measurement aid: per-step GPU time with HIP events (bf16 layers) ----
+ * A bf16 call runs seven steps, in this order (see llama_layer_step_name):
+ *   0 RMSNorm of x, 1 QKV projection + RoPE + cache append, 2 attention,
+ *   3 o_proj + residual, 4 RMSNorm of X', 5 gate/up projection + SwiGLU,
+ *   6 down projection + residual.
+ * llama_layer_profile(layer, 1) clears the totals and records a HIP event on
+ * the call's stream before each step and after the last one, for every later
+ * call; llama_layer_profile(layer, 0) stops recording.  No device memory is
+ * allocated (events are created lazily on the first enable).  Errors: NULL, HIP. */
+#define LLAMA_LAYER_STEPS 7
+int llama_layer_profile(llama_layer* layer, int enable);
+
+/* Wait for every recorded call to finish, then write, for each step i <
+ * n_steps, the total milliseconds it took over the calls recorded since the
+ * last enable (step_ms[i]), and their number (*calls).  Errors: NULL, HIP. */
+int llama_layer_profile_read(llama_layer* layer, double* step_ms, int n_steps, long long* calls);
+
+/* Name of step i (0 <= i < LLAMA_LAYER_STEPS), or "" for any other i. */
+const char* llama_layer_step_name(int step);
+
 /* Static description of a status code. */
 const char* llama_layer_strerror(int status);
 

@@ -4,7 +4,7 @@ Argument marshalling only: torch tensors are turned into device pointers,
 the current HIP stream is passed through, and status codes become
 exceptions.  Every step of the layer runs in the library's HIP kernels; there
 is no fallback of any kind — importing this package fails if the library has
-not been built (``python -m llama_decoder_block_amd.build``).
+not been built (``python llama_decoder_block_amd/build.py``).
 
 The functions mirror the C ABI in include/llama_layer.h:
 
@@ -33,7 +33,9 @@ LLAMA_F32 = 0
 LLAMA_BF16 = 1
 
 EXPORTED = ("llama_layer_create", "llama_layer_prefill", "llama_layer_decode",
-            "llama_layer_destroy", "llama_layer_strerror", "llama_layer_last_error")
+            "llama_layer_destroy", "llama_layer_strerror", "llama_layer_last_error",
+            "llama_layer_profile", "llama_layer_profile_read", "llama_layer_step_name")
+LLAMA_LAYER_STEPS = 7
 
 
 class LlamaLayerConfig(ctypes.Structure):
@@ -60,7 +62,7 @@ class LlamaLayerError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m llama_decoder_block_amd.build` (hipcc, gfx950)")
+                          "`python llama_decoder_block_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     lib.llama_layer_create.argtypes = [ctypes.POINTER(LlamaLayerConfig),
@@ -76,6 +78,13 @@ def _load():
     lib.llama_layer_strerror.restype = ctypes.c_char_p
     lib.llama_layer_last_error.argtypes = []
     lib.llama_layer_last_error.restype = ctypes.c_char_p
+    lib.llama_layer_profile.argtypes = [vp, ctypes.c_int]
+    lib.llama_layer_profile.restype = ctypes.c_int
+    lib.llama_layer_profile_read.argtypes = [vp, ctypes.POINTER(ctypes.c_double), ctypes.c_int,
+                                             ctypes.POINTER(ctypes.c_longlong)]
+    lib.llama_layer_profile_read.restype = ctypes.c_int
+    lib.llama_layer_step_name.argtypes = [ctypes.c_int]
+    lib.llama_layer_step_name.restype = ctypes.c_char_p
     return lib
 
 
@@ -143,6 +152,20 @@ def llama_layer_decode(handle, x, y, positions, B, k_cache, v_cache, stream=None
 
 def llama_layer_destroy(handle):
     LIB.llama_layer_destroy(handle)
+
+
+def llama_layer_profile(handle, enable: bool):
+    _check(LIB.llama_layer_profile(handle, 1 if enable else 0))
+
+
+def llama_layer_profile_read(handle):
+    """{step name: total ms} over the calls recorded since profiling was
+    enabled, and the number of those calls."""
+    arr = (ctypes.c_double * LLAMA_LAYER_STEPS)()
+    calls = ctypes.c_longlong()
+    _check(LIB.llama_layer_profile_read(handle, arr, LLAMA_LAYER_STEPS, ctypes.byref(calls)))
+    names = [LIB.llama_layer_step_name(i).decode() for i in range(LLAMA_LAYER_STEPS)]
+    return dict(zip(names, list(arr))), int(calls.value)
 
 
 class LlamaLayer:

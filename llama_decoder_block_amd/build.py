@@ -1,6 +1,6 @@
 """Build libllama_layer.so for gfx950 with hipcc, in-tree.
 
-    python -m llama_decoder_block_amd.build
+    python llama_decoder_block_amd/build.py
 
 Every source under csrc/ is compiled to an object (in parallel) and linked
 into llama_decoder_block_amd/libllama_layer.so.

@@ -79,11 +79,40 @@ struct llama_layer {
   float* gu = nullptr;    // fp32 path: [max_tokens, 2f]
   float* part = nullptr;  // split-K partials
   int part_seqs = 0;      // sequences the partial buffer holds at once
+  // per-step event timing (measurement aid)
+  static constexpr int kRing = 256;
+  bool prof_on = false;
+  bool prof_events = false;
+  hipEvent_t ev[kRing][LLAMA_LAYER_STEPS + 1];
+  long long prof_next = 0, prof_done = 0;  // calls recorded / harvested
+  double prof_ms[LLAMA_LAYER_STEPS] = {};
 };
 
 namespace {
 
+const char* const kStepNames[LLAMA_LAYER_STEPS] = {
+    "rmsnorm_attn", "qkv_rope_cache", "attention", "o_proj_residual",
+    "rmsnorm_mlp", "gate_up_swiglu", "down_residual"};
+
+// add the step times of the oldest recorded call to the totals
+hipError_t harvest_one(llama_layer* L) {
+  hipEvent_t* e = L->ev[L->prof_done % llama_layer::kRing];
+  hipError_t r = hipEventSynchronize(e[LLAMA_LAYER_STEPS]);
+  if (r != hipSuccess) return r;
+  for (int i = 0; i < LLAMA_LAYER_STEPS; ++i) {
+    float ms = 0.f;
+    r = hipEventElapsedTime(&ms, e[i], e[i + 1]);
+    if (r != hipSuccess) return r;
+    L->prof_ms[i] += ms;
+  }
+  ++L->prof_done;
+  return hipSuccess;
+}
+
 void release(llama_layer* L) {
+  if (L->prof_events)
+    for (auto& row : L->ev)
+      for (auto& e : row) (void)hipEventDestroy(e);
   void* bufs[] = {L->wqkv, L->wo, L->wgu, L->wd, L->g1, L->g2, L->rope_cos, L->rope_sin,
                   L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part};
   for (void* p : bufs)
@@ -314,10 +343,20 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
   ep.n_kv_heads = Hkv;
   ep.max_pos = c.max_pos;
 
+  hipEvent_t* ev = nullptr;
+  if (L->prof_on) {
+    if (L->prof_next - L->prof_done == llama_layer::kRing) HIP_OR_RETURN(harvest_one(L), "profile harvest");
+    ev = L->ev[L->prof_next % llama_layer::kRing];
+  }
+  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+
+  HIP_OR_RETURN(mark(0), "event record");
   HIP_OR_RETURN(launch_rmsnorm(xb, 0, L->g1, 0, xn, 0, M, d, c.rms_eps, s), "rmsnorm 1");
+  HIP_OR_RETURN(mark(1), "event record");
   HIP_OR_RETURN(skinny ? launch_skinny_qkv(xn, wqkv, M, nqkv, d, ep, s)
                        : launch_gemm_qkv(xn, wqkv, M, nqkv, d, ep, s),
                 "qkv projection");
+  HIP_OR_RETURN(mark(2), "event record");
   if (T == 1) {
     const size_t kv_seq = static_cast<size_t>(Hkv) * c.max_pos * 128;
     for (int b0 = 0; b0 < B; b0 += L->part_seqs) {
@@ -335,16 +374,22 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
                                       o, B, T, H, Hkv, c.max_pos, s),
                   "prefill attention");
   }
+  HIP_OR_RETURN(mark(3), "event record");
   HIP_OR_RETURN(skinny ? launch_skinny_resid_f32out(o, wo, M, d, H * 128, xb, L->x1, s)
                        : launch_gemm_resid_f32out(o, wo, M, d, H * 128, xb, L->x1, s),
                 "o_proj");
+  HIP_OR_RETURN(mark(4), "event record");
   HIP_OR_RETURN(launch_rmsnorm(L->x1, 1, L->g2, 0, xn, 0, M, d, c.rms_eps, s), "rmsnorm 2");
+  HIP_OR_RETURN(mark(5), "event record");
   HIP_OR_RETURN(skinny ? launch_skinny_swiglu(xn, wgu, M, f, d, h, s)
                        : launch_gemm_swiglu(xn, wgu, M, 2 * f, d, h, s),
                 "gate/up projection");
+  HIP_OR_RETURN(mark(6), "event record");
   HIP_OR_RETURN(skinny ? launch_skinny_resid_bf16out(h, wd, M, d, f, L->x1, yb, s)
                        : launch_gemm_resid_bf16out(h, wd, M, d, f, L->x1, yb, s),
                 "down projection");
+  HIP_OR_RETURN(mark(7), "event record");
+  if (ev) ++L->prof_next;
   return LLAMA_OK;
 }
 
@@ -366,6 +411,36 @@ static int checked_call(llama_layer* L, const void* x, void* y, const int32_t* p
   const int st = run_layer(L, x, y, pos, B, T, kc, vc, static_cast<hipStream_t>(stream));
   if (cur != L->device) (void)hipSetDevice(cur);
   return st;
+}
+
+int llama_layer_profile(llama_layer* L, int enable) {
+  g_last_error.clear();
+  if (!L) return fail(LLAMA_ERR_NULL, "layer must be non-null");
+  if (enable) {
+    if (!L->prof_events) {
+      for (auto& row : L->ev)
+        for (auto& e : row) HIP_OR_RETURN(hipEventCreate(&e), "hipEventCreate");
+      L->prof_events = true;
+    }
+    while (L->prof_done < L->prof_next) HIP_OR_RETURN(harvest_one(L), "profile harvest");
+    for (double& v : L->prof_ms) v = 0.0;
+    L->prof_next = L->prof_done = 0;
+  }
+  L->prof_on = enable != 0;
+  return LLAMA_OK;
+}
+
+int llama_layer_profile_read(llama_layer* L, double* step_ms, int n_steps, long long* calls) {
+  g_last_error.clear();
+  if (!L || !step_ms || !calls) return fail(LLAMA_ERR_NULL, "layer, step_ms and calls must be non-null");
+  while (L->prof_done < L->prof_next) HIP_OR_RETURN(harvest_one(L), "profile harvest");
+  for (int i = 0; i < n_steps && i < LLAMA_LAYER_STEPS; ++i) step_ms[i] = L->prof_ms[i];
+  *calls = L->prof_done;
+  return LLAMA_OK;
+}
+
+const char* llama_layer_step_name(int step) {
+  return step >= 0 && step < LLAMA_LAYER_STEPS ? kStepNames[step] : "";
 }
 
 int llama_layer_prefill(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
