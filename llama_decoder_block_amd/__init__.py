@@ -63,6 +63,9 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
                           "`python llama_decoder_block_amd/build.py` (hipcc, gfx950)")
+    # torch first: the library then binds to the HIP runtime torch loaded
+    # (one runtime per process, so torch streams and memory are valid here)
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32 = ctypes.c_void_p, ctypes.c_int32
     lib.llama_layer_create.argtypes = [ctypes.POINTER(LlamaLayerConfig),

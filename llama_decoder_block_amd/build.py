@@ -28,6 +28,16 @@ FLAGS = [
 ]
 
 
+def torch_lib_dir() -> str | None:
+    """Directory of the HIP runtime PyTorch ships (torch/lib), found without importing torch."""
+    import importlib.util
+    spec = importlib.util.find_spec("torch")
+    if spec is None or not spec.submodule_search_locations:
+        return None
+    d = os.path.join(list(spec.submodule_search_locations)[0], "lib")
+    return d if os.path.exists(os.path.join(d, "libamdhip64.so")) else None
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
@@ -50,7 +60,17 @@ def build(verbose: bool = True) -> str:
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # One HIP runtime per process: the library records a dependency on the
+    # unversioned libamdhip64.so, which the loader resolves to the copy PyTorch
+    # has already loaded (torch/lib) when torch is imported first, so streams,
+    # events and memory are shared with it; a plain C caller gets ROCm's.
+    tdir = torch_lib_dir()
+    hip_dir = tdir or "/opt/rocm/lib"
+    clangxx = os.path.join(os.path.dirname(os.path.realpath(HIPCC)), "..", "lib", "llvm", "bin", "clang++")
+    if not os.path.exists(clangxx):
+        clangxx = "/opt/rocm/lib/llvm/bin/clang++"
+    cmd = [clangxx, "-shared", "-fPIC", *objs, "-o", tmp, f"-L{hip_dir}", "-l:libamdhip64.so",
+           "-Wl,-rpath,/opt/rocm/lib", "-Wl,--no-undefined"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

@@ -99,3 +99,13 @@ def test_binding_refuses_host_tensors():
     import torch
     with pytest.raises(ValueError):
         lib._ptr(torch.zeros(4), "x")
+
+
+def test_one_hip_runtime_in_the_process():
+    """The library binds to the HIP runtime torch loaded (torch streams, events
+    and memory are then valid inside it): exactly one libamdhip64 is mapped."""
+    import re
+    import torch  # noqa: F401
+    maps = open("/proc/self/maps").read()
+    runtimes = sorted(set(re.findall(r"/\S*libamdhip64\.so\S*", maps)))
+    assert len(runtimes) == 1, runtimes
