@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
     float l = 0.f;
     for (int j = lane; j < n; j += 64) {
-      const float e = exp2f(sc[r][j] - m);
+      const float e = fast_exp2(sc[r][j] - m);
       sc[r][j] = e;
       l += e;
     }
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(128) void attn_decode_combine_kernel(const float* _
   if (M != -INFINITY) {
     for (int s = 0; s < n_split; ++s) {
       const float* e = pp + s * (DH + 2);
-      const float w = exp2f(e[0] - M);  // exactly 0 for empty splits (m = -inf)
+      const float w = fast_exp2(e[0] - M);  // exactly 0 for empty splits (m = -inf)
       den += w * e[1];
       num += w * e[2 + d];
     }

@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float m_new = fmaxf(m_run, mt);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
+      const float alpha = fast_exp2(m_run - m_use);
       m_run = m_new;
       float lsum = 0.f;
       uint32_t phi[2][2][4], plo[2][2][4];  // [kb][half][packed pair]
@@ -189,8 +189,8 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2f(sacc[kb][r] - m_use);
-          const float p1 = exp2f(sacc[kb][r + 1] - m_use);
+          const float p0 = fast_exp2(sacc[kb][r] - m_use);
+          const float p1 = fast_exp2(sacc[kb][r + 1] - m_use);
           lsum += p0 + p1;
           const uint32_t hp = pack_bf16x2(p0, p1);
           phi[kb][r >> 3][(r & 7) >> 1] = hp;

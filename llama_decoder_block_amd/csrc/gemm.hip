@@ -118,34 +118,78 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(const bf16_t* __res
   };
 
   const int nk = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-
   const int a_row = (wm * TL::TM + (lane & 31)) * SK + (lane >> 5) * 8;
   const int b_row = (wn * TL::TN + (lane & 31)) * SK + (lane >> 5) * 8;
+  bf16x8 fa[2][TL::FM], fb[2][TL::FN];
+  auto frag_a = [&](int st, int kk, int i) {
+    return *reinterpret_cast<const bf16x8*>(&As[st][a_row + i * 32 * SK + kk * 16]);
+  };
+  auto frag_b = [&](int st, int kk, int j) {
+    return *reinterpret_cast<const bf16x8*>(&Bs[st][b_row + j * 32 * SK + kk * 16]);
+  };
+  // staging chunk c (A chunks first, then B): LDS write of slab kt+1 from the
+  // registers, then the load of slab kt+2 into the same registers
+  auto stage_chunk = [&](int c, int st_w, int k0_next) {
+    const uint32_t sk = static_cast<uint32_t>(k0_next) * 2u;
+    if (c < TL::A_CH) {
+      *reinterpret_cast<uint4*>(&As[st_w][st_base + c * 32 * SK]) = ra[c];
+      ra[c] = buf_load16(a_rs, a_off[c], sk);
+    } else {
+      const int cb = c - TL::A_CH;
+      *reinterpret_cast<uint4*>(&Bs[st_w][st_base + cb * 32 * SK]) = rb[cb];
+      rb[cb] = buf_load16(b_rs, b_off[cb], sk);
+    }
+  };
+
+  // Software pipeline, fixed instruction order.  While LDS stage kt&1 feeds
+  // the MFMAs of slab kt: the registers (loaded during the previous slab) are
+  // written to the other stage and refilled with slab kt+2, spread over the
+  // first three 16-wide k steps; each MFMA slot also reads one fragment of the
+  // next k step.  The barrier sits before the last k step, whose MFMA slots
+  // then read the first fragments of slab kt+1.  Past the last slab the loads
+  // read in-range data of the next row or zeros and that stage is never used.
+  constexpr int kSlots = TL::FM * TL::FN;
+  constexpr int kChunks = TL::A_CH + TL::B_CH;
+  constexpr int kPerStep = (kChunks + 2) / 3;
+  gload(0);
+  lstore(0);
+  gload(BK);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i) fa[0][i] = frag_a(0, 0, i);
+#pragma unroll
+  for (int j = 0; j < TL::FN; ++j) fb[0][j] = frag_b(0, 0, j);
 
   for (int kt = 0; kt < nk; ++kt) {
     const int st = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+    const int k_next2 = (kt + 2) * BK;
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[TL::FM], bfr[TL::FN];
+      const int cur = kk & 1;
+      const int rd_st = kk < 3 ? st : st ^ 1;
+      const int rd_kk = kk < 3 ? kk + 1 : 0;
+      if (kk == 3) __syncthreads();
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(&As[st][a_row + i * 32 * SK + kk * 16]);
+      for (int m = 0; m < kSlots; ++m) {
+        const int i = m / TL::FN, j = m % TL::FN;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j], acc[i][j], 0, 0, 0);
+        if (m < TL::FM)
+          fa[cur ^ 1][m] = frag_a(rd_st, rd_kk, m);
+        else if (m < TL::FM + TL::FN)
+          fb[cur ^ 1][m - TL::FM] = frag_b(rd_st, rd_kk, m - TL::FM);
+        if (kk < 3) {
+          // chunk placed in slot m: spread kPerStep chunks over the slots
 #pragma unroll
-      for (int j = 0; j < TL::FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(&Bs[st][b_row + j * 32 * SK + kk * 16]);
-#pragma unroll
-      for (int i = 0; i < TL::FM; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          for (int q = 0; q < kPerStep; ++q) {
+            const int c = kk * kPerStep + q;
+            if (c < kChunks && (q * kSlots) / kPerStep == m) stage_chunk(c, st ^ 1, k_next2);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-    if (kt + 1 < nk) lstore(st ^ 1);
-    __syncthreads();
   }
+  __syncthreads();
 
   // ---------------------------------------------------------------- epilogue
   // accumulator register r of tile (i, j) holds row 8*(r/4) + 4*(lane/32) + r%4
