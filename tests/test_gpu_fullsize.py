@@ -35,8 +35,9 @@ def _prefill_case(name, seed):
     yg = G.f64(y).reshape(B * T, -1)[rows]
     G.assert_bf16_output(yg, yo.reshape(B * T, -1)[rows], f"y ({len(rows)} sampled rows)")
     kg, vg = G.f64(kc), G.f64(vc)
-    G.assert_bf16_storage(kg[:, :, :T], ko[:, :, :T], "K written")
-    G.assert_bf16_storage(vg[:, :, :T], vo[:, :, :T], "V written")
+    fk, fv = G.kv_floors(x, w)
+    G.assert_bf16_storage(kg[:, :, :T], ko[:, :, :T], "K written", fk)
+    G.assert_bf16_storage(vg[:, :, :T], vo[:, :, :T], "V written", fv)
     return wl, w, w64, layer, kc, vc, ko, vo
 
 
@@ -67,8 +68,9 @@ def test_llama7b_decode():
                                         G.f64(kc0[idx]), G.f64(vc0[idx]), n_heads=wl.n_heads,
                                         n_kv_heads=wl.n_kv_heads, bf16_points=True)
     G.assert_bf16_output(G.f64(y)[idx], yo, "y (4 sampled sequences)")
-    G.assert_bf16_storage(G.f64(kc[idx])[:, :, p], ko[:, :, p], "K appended")
-    G.assert_bf16_storage(G.f64(vc[idx])[:, :, p], vo[:, :, p], "V appended")
+    fk, fv = G.kv_floors(x[idx], w)
+    G.assert_bf16_storage(G.f64(kc[idx])[:, :, p], ko[:, :, p], "K appended", fk)
+    G.assert_bf16_storage(G.f64(vc[idx])[:, :, p], vo[:, :, p], "V appended", fv)
     # prior slots untouched
     assert torch.equal(kc[:, :, :p], kc0[:, :, :p]) and torch.equal(vc[:, :, :p], vc0[:, :, :p])
 
@@ -88,5 +90,8 @@ def test_llama70b_gqa_prefill_then_64_decode_steps():
             G.assert_bf16_output(G.f64(ys), yo, f"decode step {s} y")
         else:
             assert G.rel_err(G.f64(ys), yo) <= G.BF16_RMS_GATE, s
-    G.assert_bf16_storage(G.f64(kc)[:, :, T:], ko[:, :, T:], "K appended by 64 steps")
-    G.assert_bf16_storage(G.f64(vc)[:, :, T:], vo[:, :, T:], "V appended by 64 steps")
+    xs_all = torch.stack([synth.make_x(wl, (1,), tensor_id=synth.TID_DECODE_BASE + s, device=DEV)
+                          for s in range(wl.decode_steps)])
+    fk, fv = G.kv_floors(xs_all, w)
+    G.assert_bf16_storage(G.f64(kc)[:, :, T:], ko[:, :, T:], "K appended by 64 steps", fk)
+    G.assert_bf16_storage(G.f64(vc)[:, :, T:], vo[:, :, T:], "V appended by 64 steps", fv)

@@ -38,8 +38,9 @@ def _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc):
     kg, vg = G.f64(kc), G.f64(vc)
     if wl.dtype == "bf16":
         G.assert_bf16_output(G.f64(y), yo, "y")
-        G.assert_bf16_storage(kg[:, :, written], ko[:, :, written], "K written")
-        G.assert_bf16_storage(vg[:, :, written], vo[:, :, written], "V written")
+        fk, fv = G.kv_floors(x, w)
+        G.assert_bf16_storage(kg[:, :, written], ko[:, :, written], "K written", fk)
+        G.assert_bf16_storage(vg[:, :, written], vo[:, :, written], "V written", fv)
         yp, _, _ = G.oracle_prefill(wl, w64, x, pos, kc0, vc0, bf16_points=False)
         print(f"  (vs plain oracle: y max|err|/rms = {G.rel_err(G.f64(y), yp):.5f})")
     else:
@@ -116,8 +117,9 @@ def test_bf16_decode_steps(B, Hkv):
                                             n_heads=wl.n_heads, n_kv_heads=wl.n_kv_heads,
                                             bf16_points=True)
         G.assert_bf16_output(G.f64(ys), yo, f"decode step {s} y")
-        G.assert_bf16_storage(G.f64(kc)[:, :, p], ko[:, :, p], f"decode step {s} K")
-        G.assert_bf16_storage(G.f64(vc)[:, :, p], vo[:, :, p], f"decode step {s} V")
+        fk, fv = G.kv_floors(xs, w)
+        G.assert_bf16_storage(G.f64(kc)[:, :, p], ko[:, :, p], f"decode step {s} K", fk)
+        G.assert_bf16_storage(G.f64(vc)[:, :, p], vo[:, :, p], f"decode step {s} V", fv)
 
 
 def test_decode_matches_prefill_of_one_more_token():
