@@ -24,8 +24,8 @@
 // is transposed to [dd][slot] while it is written to LDS.  P stays in fp32 in
 // the online softmax and is fed to the PV product as bf16 hi + bf16 lo (two
 // MFMAs), so the product sees P to about 16 bits instead of bf16's 8.
-// Query tiles are launched heaviest first (the causal workload grows with the
-// tile index).  Tiles that lie wholly above a wave's diagonal are skipped, and
+// Query tiles are launched heaviest first across all heads and sequences (the
+// causal workload grows with the tile index).  Tiles that lie wholly above a wave's diagonal are skipped, and
 // the -inf mask is applied only on tiles that cross it.
 #include "common.h"
 
@@ -49,12 +49,15 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ pos, bf16_t* __restrict__ o,
-    int T, int H, int Hkv, int max_pos, float scale_log2) {
+    int n_seq, int T, int H, int Hkv, int max_pos, float scale_log2) {
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BKV * KSTR];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DH * VSTR];
 
-  const int qt = gridDim.x - 1 - blockIdx.x;  // heaviest tiles first
-  const int h = blockIdx.y, b = blockIdx.z;
+  // 1-D grid, heaviest query tiles of every (sequence, head) first
+  const int n_qt = (T + BQ - 1) / BQ;
+  const int per_qt = H * n_seq;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
+  const int h = static_cast<int>(blockIdx.x) % per_qt % H, b = static_cast<int>(blockIdx.x) % per_qt / H;
   const int g = h / (H / Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, lq = lane & 31;
@@ -92,41 +95,46 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     }
   }
 
-  // ---- K / V tile staging (buffer loads over this (b, g) cache slice)
+  // ---- K / V tile staging (buffer loads over this (b, g) cache slice).
+  // Waves 0-1 stage V, waves 2-3 stage K, 8 loads of 16 bytes per thread each.
+  // V: thread (kg, dg) loads slots 8 kg .. 8 kg + 7 at dims 8 dg .. 8 dg + 7 and
+  // writes them transposed as 8 rows (dims) of 8 slots, 16 bytes per row; with
+  // the 144-byte row stride a 16-lane group (8 slot groups x 2 dim groups) hits
+  // 64 distinct banks.
   const size_t slice = (static_cast<size_t>(b) * Hkv + g) * max_pos * DH;
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k_cache + slice, static_cast<uint32_t>(max_pos) * DH * 2u);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v_cache + slice, static_cast<uint32_t>(max_pos) * DH * 2u);
-  // K: 64 rows x 16 chunks; thread handles chunks tid + 256 i
-  const int kr = tid >> 4, kc = tid & 15;
-  // V: thread handles slots 4*vg .. +3 at dims 8*vd .. +7
-  const int vg = tid >> 4, vd = tid & 15;
-  uint4 kreg[4], vreg[4];
+  const bool stage_v = tid < 128;
+  const int st_t = tid & 127;
+  const int vkg = st_t & 7, vdg = st_t >> 3;      // V: slot group, dim group (16 of 8 dims)
+  const int kr = st_t >> 4, kc = st_t & 15;        // K: row (of 8 per pass), 16-byte chunk
+  uint4 sreg[8];
   auto gload = [&](int j0) {
     const uint32_t so = static_cast<uint32_t>(j0) * DH * 2u;
+    if (stage_v) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(k_rs, ((kr + 16 * i) * DH + kc * 8) * 2u, so);
+      for (int i = 0; i < 8; ++i) sreg[i] = buf_load16(v_rs, ((8 * vkg + i) * DH + vdg * 8) * 2u, so);
+    } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(v_rs, ((4 * vg + i) * DH + vd * 8) * 2u, so);
+      for (int i = 0; i < 8; ++i) sreg[i] = buf_load16(k_rs, ((kr + 8 * i) * DH + kc * 8) * 2u, so);
+    }
   };
   auto lstore = [&](int st) {
+    if (stage_v) {
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(sreg);  // w[4 * slot + dim/2]
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(&Ks[st][(kr + 16 * i) * KSTR + kc * 8]) = kreg[i];
-    // transpose 4 slots x 8 dims -> 8 rows (dims) of 4 slots
-    const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vreg[0]);
-    const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vreg[1]);
-    const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vreg[2]);
-    const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vreg[3]);
+      for (int d = 0; d < 8; ++d) {
+        const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
+        uint4 o;
+        o.x = __builtin_amdgcn_perm(w[4 * 1 + (d >> 1)], w[4 * 0 + (d >> 1)], sel);
+        o.y = __builtin_amdgcn_perm(w[4 * 3 + (d >> 1)], w[4 * 2 + (d >> 1)], sel);
+        o.z = __builtin_amdgcn_perm(w[4 * 5 + (d >> 1)], w[4 * 4 + (d >> 1)], sel);
+        o.w = __builtin_amdgcn_perm(w[4 * 7 + (d >> 1)], w[4 * 6 + (d >> 1)], sel);
+        *reinterpret_cast<uint4*>(&Vt[st][(vdg * 8 + d) * VSTR + 8 * vkg]) = o;
+      }
+    } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      // dims 2e (low halves) and 2e+1 (high halves)
-      uint2 lo, hi;
-      lo.x = __builtin_amdgcn_perm(v1[e], v0[e], 0x05040100);  // slot0.lo | slot1.lo << 16
-      lo.y = __builtin_amdgcn_perm(v3[e], v2[e], 0x05040100);
-      hi.x = __builtin_amdgcn_perm(v1[e], v0[e], 0x07060302);
-      hi.y = __builtin_amdgcn_perm(v3[e], v2[e], 0x07060302);
-      *reinterpret_cast<uint2*>(&Vt[st][(vd * 8 + 2 * e) * VSTR + 4 * vg]) = lo;
-      *reinterpret_cast<uint2*>(&Vt[st][(vd * 8 + 2 * e + 1) * VSTR + 4 * vg]) = hi;
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&Ks[st][(kr + 8 * i) * KSTR + kc * 8]) = sreg[i];
     }
   };
 
@@ -242,9 +250,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
 hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                                const int32_t* pos, bf16_t* o, int B, int T, int n_heads,
                                int n_kv_heads, int max_pos, hipStream_t s) {
-  const dim3 grid((T + BQ - 1) / BQ, n_heads, B);
+  const dim3 grid(static_cast<unsigned>((T + BQ - 1) / BQ) * n_heads * B);
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
-  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, o, T,
+  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, o, B, T,
                      n_heads, n_kv_heads, max_pos, scale_log2);
   return hipGetLastError();
 }
