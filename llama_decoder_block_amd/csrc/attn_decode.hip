@@ -172,8 +172,8 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
 
 // Merge the splits: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 __global__ __launch_bounds__(128) void attn_decode_combine_kernel(const float* __restrict__ part,
-                                                                  bf16_t* __restrict__ o, int H,
-                                                                  int n_split) {
+                                                                  bf16_t* __restrict__ o, int o_frag,
+                                                                  int H, int n_split) {
   const int bh = blockIdx.x;  // b * H + h
   const int d = threadIdx.x;
   const float* pp = part + static_cast<size_t>(bh) * n_split * (DH + 2);
@@ -188,7 +188,8 @@ __global__ __launch_bounds__(128) void attn_decode_combine_kernel(const float* _
       num += w * e[2 + d];
     }
   }
-  o[static_cast<size_t>(bh) * DH + d] = f32_to_bf16(den > 0.f ? num / den : 0.f);
+  const size_t at = o_frag ? frag_index(bh / H, (bh % H) * DH + d, H * DH) : static_cast<size_t>(bh) * DH + d;
+  o[at] = f32_to_bf16(den > 0.f ? num / den : 0.f);
 }
 
 int split_len(int max_pos, int B, int Hkv) {
@@ -215,8 +216,9 @@ int decode_attn_splits(int max_pos, int B, int n_kv_heads) {
 }
 
 hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
-                              const int32_t* pos, bf16_t* o, float* part, int n_split, int B,
-                              int n_heads, int n_kv_heads, int max_pos, hipStream_t s) {
+                              const int32_t* pos, bf16_t* o, int o_frag, float* part, int n_split,
+                              int B, int n_heads, int n_kv_heads, int max_pos, hipStream_t s) {
+  if (o_frag && B > kSkinnyMaxTokens) return hipErrorInvalidValue;
   const int L = split_len(max_pos, B, n_kv_heads);
   if ((max_pos + L - 1) / L != n_split) return hipErrorInvalidValue;
   const int n_rep = n_heads / n_kv_heads;
@@ -236,7 +238,7 @@ hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(B * n_heads), dim3(DH), 0, s, part, o, n_heads,
+  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(B * n_heads), dim3(DH), 0, s, part, o, o_frag, n_heads,
                      n_split);
   return hipGetLastError();
 }

@@ -49,7 +49,7 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast
 __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ pos, bf16_t* __restrict__ o,
-    int n_seq, int T, int H, int Hkv, int max_pos, float scale_log2) {
+    int o_frag, int n_seq, int T, int H, int Hkv, int max_pos, float scale_log2) {
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BKV * KSTR];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DH * VSTR];
 
@@ -241,18 +241,22 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
       uint2 w;
       w.x = pack_bf16x2(oacc[fd][4 * rq] * inv, oacc[fd][4 * rq + 1] * inv);
       w.y = pack_bf16x2(oacc[fd][4 * rq + 2] * inv, oacc[fd][4 * rq + 3] * inv);
-      *reinterpret_cast<uint2*>(orow + fd * 32 + 8 * rq + 4 * hl) = w;
+      // four consecutive dims stay contiguous in fragment order as well
+      const int col = fd * 32 + 8 * rq + 4 * hl;
+      bf16_t* dst = o_frag ? o + frag_index(static_cast<int>(row), h * DH + col, static_cast<int>(qstride)) : orow + col;
+      *reinterpret_cast<uint2*>(dst) = w;
     }
 }
 
 }  // namespace
 
 hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
-                               const int32_t* pos, bf16_t* o, int B, int T, int n_heads,
+                               const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
                                int n_kv_heads, int max_pos, hipStream_t s) {
+  if (o_frag && B * T > kSkinnyMaxTokens) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>((T + BQ - 1) / BQ) * n_heads * B);
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
-  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, o, B, T,
+  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, o, o_frag, B, T,
                      n_heads, n_kv_heads, max_pos, scale_log2);
   return hipGetLastError();
 }

@@ -55,6 +55,19 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// Fragment order of a bf16 matrix [R, K] (K % 16 == 0): the operand layout of
+// v_mfma_f32_32x32x16_bf16.  The matrix is cut into 1 KB chunks of 32 rows x
+// 16 k; chunk (rb, kb) sits at element (rb * K/16 + kb) * 512, and inside it
+// lane l's 16 bytes hold row 32 rb + l % 32, k = 16 kb + 8 (l / 32) + 0..7.  A
+// wavefront reads one chunk with one contiguous 1 KB load, and rows
+// [32 rb, 32 rb + n) of the matrix occupy elements [32 rb K, (32 rb + n) K),
+// exactly where they sit in row-major order.  The weights of every bf16 layer
+// are stored this way, and so are the activations of calls with <= 64 tokens.
+__device__ __forceinline__ uint32_t frag_index(int row, int k, int K) {
+  return ((static_cast<uint32_t>(row >> 5) * static_cast<uint32_t>(K >> 4) + static_cast<uint32_t>(k >> 4)) << 9) +
+         (static_cast<uint32_t>((row & 31) + ((k >> 3) & 1) * 32) << 3) + static_cast<uint32_t>(k & 7);
+}
+
 __device__ __forceinline__ float warp_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -69,10 +82,19 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z));
 
 // RMSNorm rows: out[r, :] = g * in[r, :] / sqrt(mean(in[r,:]^2) + eps).
 // in is bf16 (in_f32 = 0) or fp32 (in_f32 = 1); out is bf16 or fp32.
+// out_frag = 1 writes a bf16 out in fragment order (d % 128 == 0).
 hipError_t launch_rmsnorm(const void* in, int in_f32, const void* gain, int gain_f32, void* out,
-                          int out_f32, int rows, int d, float eps, hipStream_t s);
+                          int out_f32, int out_frag, int rows, int d, float eps, hipStream_t s);
 
-// Tiled bf16 MFMA GEMM, C = A[M,K] . B[N,K]^T with a fused epilogue.
+// Row-major bf16 src [rows, K] -> fragment order.  Source row r lands on row
+// (r / group) * group_stride + r % group of the fragment-ordered dst
+// (group = rows for a plain copy); rows and group are multiples of 32 and
+// K % 16 == 0.
+hipError_t launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int group,
+                            int group_stride, hipStream_t s);
+
+// Tiled bf16 MFMA GEMM, C = A[M,K] . W[N,K]^T with a fused epilogue; A
+// row-major, W in fragment order (K % 128 == 0).
 struct QkvEpilogue {
   bf16_t* q;               // [M, H*dh]
   bf16_t* k_cache;         // [B, Hkv, max_pos, dh]
@@ -91,12 +113,16 @@ hipError_t launch_gemm_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int
 // out_bf16[M,N] = bf16(A.W^T + resid_f32[M,N])
 hipError_t launch_gemm_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
                                      const float* resid, bf16_t* out, hipStream_t s);
-// W is the gate/up matrix packed in blocks of 64 rows [gate 64 | up 64]
+// W is the gate/up matrix interleaved in blocks of 64 rows [gate 64 | up 64]
 // (N = 2f); out[M, f] = bf16(SiLU(gate) * up)
 hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, int K,
                               bf16_t* out, hipStream_t s);
 
-// Skinny (M <= 64 tokens) weight-streaming versions of the same four GEMMs.
+// Weight-streaming versions of the same four GEMMs for M <= 64 tokens: A and
+// W both in fragment order (A holds ceil(M/32)*32 rows; rows >= M are never
+// written out, whatever they hold).  The SwiGLU output h is written in
+// fragment order, ready to be the A operand of the down projection.
+constexpr int kSkinnyMaxTokens = 64;
 hipError_t launch_skinny_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,
                              const QkvEpilogue& ep, hipStream_t s);
 hipError_t launch_skinny_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
@@ -108,17 +134,18 @@ hipError_t launch_skinny_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int f
 
 // Causal flash attention over the cache for prefill (bf16, dh = 128).
 // q/o [B*T, H*128]; the query of token m sees cache slots 0..pos[m].
+// o_frag = 1 writes o in fragment order instead of row-major.
 hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
-                               const int32_t* pos, bf16_t* o, int B, int T, int n_heads,
+                               const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
                                int n_kv_heads, int max_pos, hipStream_t s);
 
 // Split-K decode attention (bf16, dh = 128) for one query per sequence,
 // followed by the combine of the splits.  part holds
-// B*H*n_split*(128+2) floats.
+// B*H*n_split*(128+2) floats; o_frag as for the prefill kernel.
 int decode_attn_splits(int max_pos, int B, int n_kv_heads);
 hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
-                              const int32_t* pos, bf16_t* o, float* part, int n_split, int B,
-                              int n_heads, int n_kv_heads, int max_pos, hipStream_t s);
+                              const int32_t* pos, bf16_t* o, int o_frag, float* part, int n_split,
+                              int B, int n_heads, int n_kv_heads, int max_pos, hipStream_t s);
 
 // fp32 path (any shape).
 struct F32Layer {

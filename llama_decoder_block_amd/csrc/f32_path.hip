@@ -125,7 +125,7 @@ hipError_t run_f32_layer(const F32Layer& L, const float* x, float* y, const int3
   hipError_t e;
 #define LLAMA_TRY(expr) \
   if ((e = (expr)) != hipSuccess) return e
-  LLAMA_TRY(launch_rmsnorm(x, 1, L.g1, 1, L.xn, 1, M, L.d, L.eps, s));
+  LLAMA_TRY(launch_rmsnorm(x, 1, L.g1, 1, L.xn, 1, 0, M, L.d, L.eps, s));
   LLAMA_TRY(gemm(L.xn, L.wqkv, nullptr, L.qkv, M, nqkv, L.d, s));
   hipLaunchKernelGGL(f32_rope_scatter_kernel, dim3(M), dim3(256), 0, s, L.qkv, k_cache, v_cache, pos,
                      L.rope_cos, L.rope_sin, T, L.H, L.Hkv, L.dh, L.max_pos);
@@ -134,7 +134,7 @@ hipError_t run_f32_layer(const F32Layer& L, const float* x, float* y, const int3
                      L.attn, T, L.H, L.Hkv, L.dh, L.max_pos);
   LLAMA_TRY(hipGetLastError());
   LLAMA_TRY(gemm(L.attn, L.wo, x, L.x1, M, L.d, L.H * L.dh, s));
-  LLAMA_TRY(launch_rmsnorm(L.x1, 1, L.g2, 1, L.xn, 1, M, L.d, L.eps, s));
+  LLAMA_TRY(launch_rmsnorm(L.x1, 1, L.g2, 1, L.xn, 1, 0, M, L.d, L.eps, s));
   LLAMA_TRY(gemm(L.xn, L.wgu, nullptr, L.gu, M, 2 * L.f, L.d, s));
   {
     const long long n = static_cast<long long>(M) * L.f;

@@ -13,7 +13,10 @@
 //   6  SiLU(xn Wg^T) * (xn Wu^T)         -> h           (bf16)
 //   7  h Wd^T + X'                       -> y           (bf16)
 // Steps 2, 4, 6, 7 use the tiled MFMA GEMMs when the call has more than 64
-// tokens and the weight-streaming GEMMs otherwise.
+// tokens and the weight-streaming GEMMs otherwise; in the latter case the
+// activations xn, o and h are written in fragment order by their producers
+// (steps 1, 3, 5, 6), which is the operand layout the streaming GEMMs load.
+// bf16 weights are converted to fragment order once, at creation.
 #include "common.h"
 #include "../../include/llama_layer.h"
 
@@ -50,7 +53,6 @@ int hip_fail(hipError_t e, const char* what) {
     if (e_ != hipSuccess) return hip_fail(e_, what); \
   } while (0)
 
-constexpr int kSkinnyMaxTokens = 64;
 constexpr int kDecodeChunk = 64;  // sequences per split-K attention launch
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -62,6 +64,7 @@ struct llama_layer {
   int device = 0;
   size_t es = 2;  // element size of the layer dtype
   // weights (owned)
+  // (bf16: fragment order; fp32: row-major)
   void* wqkv = nullptr;  // [(H + 2 Hkv) dh, d]
   void* wo = nullptr;    // [d, H dh]
   void* wgu = nullptr;   // bf16: [2f, d] in 64-row blocks [gate | up]; fp32: [gate; up]
@@ -70,7 +73,8 @@ struct llama_layer {
   void* g2 = nullptr;
   float* rope_cos = nullptr;  // [max_pos, dh/2]
   float* rope_sin = nullptr;
-  // scratch (owned)
+  // scratch (owned); bf16 activations hold max(max_tokens, 64) rows so that
+  // the fragment-order form (whole 32-row blocks) always fits
   void* xn = nullptr;     // [max_tokens, d]
   void* q = nullptr;      // bf16: [max_tokens, H dh]; fp32: qkv [max_tokens, (H+2Hkv) dh]
   void* o = nullptr;      // [max_tokens, H dh]
@@ -195,6 +199,8 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
     if (!p) return fail(LLAMA_ERR_NULL, "every weight pointer must be non-null");
   int st = check_config(cfg);
   if (st != LLAMA_OK) return st;
+  for (const void* p : wp)
+    if (!aligned16(p)) return fail(LLAMA_ERR_INVALID, "weight pointers must be 16-byte aligned");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   llama_layer* L = new (std::nothrow) llama_layer();
@@ -206,7 +212,9 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
 
   const size_t es = L->es;
   const size_t d = cfg->d_model, H = cfg->n_heads, Hkv = cfg->n_kv_heads, dh = cfg->head_dim,
-               f = cfg->d_ff, mt = cfg->max_tokens, mp = cfg->max_pos;
+               f = cfg->d_ff, mp = cfg->max_pos;
+  const size_t mt = cfg->dtype == LLAMA_BF16 && cfg->max_tokens < kSkinnyMaxTokens ? kSkinnyMaxTokens
+                                                                                   : cfg->max_tokens;
   const size_t nq = H * dh, nkv = Hkv * dh;
 #define ALLOC_OR_FAIL(ptr, bytes)                               \
   do {                                                          \
@@ -241,22 +249,33 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
   }
 
   const hipMemcpyKind dd = hipMemcpyDeviceToDevice;
-  char* qkv = static_cast<char*>(L->wqkv);
-  HIP_OR_FAIL(hipMemcpyAsync(qkv, w->wq, nq * d * es, dd, s), "copy wq");
-  HIP_OR_FAIL(hipMemcpyAsync(qkv + nq * d * es, w->wk, nkv * d * es, dd, s), "copy wk");
-  HIP_OR_FAIL(hipMemcpyAsync(qkv + (nq + nkv) * d * es, w->wv, nkv * d * es, dd, s), "copy wv");
-  HIP_OR_FAIL(hipMemcpyAsync(L->wo, w->wo, d * nq * es, dd, s), "copy wo");
-  HIP_OR_FAIL(hipMemcpyAsync(L->wd, w->w_down, d * f * es, dd, s), "copy w_down");
   HIP_OR_FAIL(hipMemcpyAsync(L->g1, w->attn_norm, d * es, dd, s), "copy attn_norm");
   HIP_OR_FAIL(hipMemcpyAsync(L->g2, w->ffn_norm, d * es, dd, s), "copy ffn_norm");
   if (cfg->dtype == LLAMA_BF16) {
-    // 64-row blocks: packed rows [128 j, 128 j + 64) = gate rows [64 j, 64 j + 64),
-    // packed rows [128 j + 64, 128 j + 128) = up rows [64 j, 64 j + 64)
-    const size_t blk = 64 * d * es;
-    char* gu = static_cast<char*>(L->wgu);
-    HIP_OR_FAIL(hipMemcpy2DAsync(gu, 2 * blk, w->w_gate, blk, blk, f / 64, dd, s), "pack w_gate");
-    HIP_OR_FAIL(hipMemcpy2DAsync(gu + blk, 2 * blk, w->w_up, blk, blk, f / 64, dd, s), "pack w_up");
+    // fragment order; rows of a 32-row-aligned range sit where they would in
+    // row-major order, so q, k and v rows are converted straight into their
+    // place in the concatenated matrix
+    const int di = static_cast<int>(d), fi = static_cast<int>(f), nqi = static_cast<int>(nq),
+              nkvi = static_cast<int>(nkv);
+    auto* wqkv = static_cast<bf16_t*>(L->wqkv);
+    auto* wgu = static_cast<bf16_t*>(L->wgu);
+    auto src = [](const void* p) { return static_cast<const bf16_t*>(p); };
+    HIP_OR_FAIL(launch_pack_rows(src(w->wq), nqi, di, wqkv, nqi, nqi, s), "convert wq");
+    HIP_OR_FAIL(launch_pack_rows(src(w->wk), nkvi, di, wqkv + nq * d, nkvi, nkvi, s), "convert wk");
+    HIP_OR_FAIL(launch_pack_rows(src(w->wv), nkvi, di, wqkv + (nq + nkv) * d, nkvi, nkvi, s), "convert wv");
+    HIP_OR_FAIL(launch_pack_rows(src(w->wo), di, nqi, static_cast<bf16_t*>(L->wo), di, di, s), "convert wo");
+    HIP_OR_FAIL(launch_pack_rows(src(w->w_down), di, fi, static_cast<bf16_t*>(L->wd), di, di, s), "convert w_down");
+    // 64-row blocks: rows [128 j, 128 j + 64) = gate rows [64 j, 64 j + 64),
+    // rows [128 j + 64, 128 j + 128) = up rows [64 j, 64 j + 64)
+    HIP_OR_FAIL(launch_pack_rows(src(w->w_gate), fi, di, wgu, 64, 128, s), "convert w_gate");
+    HIP_OR_FAIL(launch_pack_rows(src(w->w_up), fi, di, wgu + 64 * d, 64, 128, s), "convert w_up");
   } else {
+    char* qkv = static_cast<char*>(L->wqkv);
+    HIP_OR_FAIL(hipMemcpyAsync(qkv, w->wq, nq * d * es, dd, s), "copy wq");
+    HIP_OR_FAIL(hipMemcpyAsync(qkv + nq * d * es, w->wk, nkv * d * es, dd, s), "copy wk");
+    HIP_OR_FAIL(hipMemcpyAsync(qkv + (nq + nkv) * d * es, w->wv, nkv * d * es, dd, s), "copy wv");
+    HIP_OR_FAIL(hipMemcpyAsync(L->wo, w->wo, d * nq * es, dd, s), "copy wo");
+    HIP_OR_FAIL(hipMemcpyAsync(L->wd, w->w_down, d * f * es, dd, s), "copy w_down");
     HIP_OR_FAIL(hipMemcpyAsync(L->wgu, w->w_gate, f * d * es, dd, s), "copy w_gate");
     HIP_OR_FAIL(hipMemcpyAsync(static_cast<char*>(L->wgu) + f * d * es, w->w_up, f * d * es, dd, s),
                 "copy w_up");
@@ -351,7 +370,7 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
   auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
 
   HIP_OR_RETURN(mark(0), "event record");
-  HIP_OR_RETURN(launch_rmsnorm(xb, 0, L->g1, 0, xn, 0, M, d, c.rms_eps, s), "rmsnorm 1");
+  HIP_OR_RETURN(launch_rmsnorm(xb, 0, L->g1, 0, xn, 0, skinny, M, d, c.rms_eps, s), "rmsnorm 1");
   HIP_OR_RETURN(mark(1), "event record");
   HIP_OR_RETURN(skinny ? launch_skinny_qkv(xn, wqkv, M, nqkv, d, ep, s)
                        : launch_gemm_qkv(xn, wqkv, M, nqkv, d, ep, s),
@@ -365,13 +384,13 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
       HIP_OR_RETURN(launch_attn_decode(q + static_cast<size_t>(b0) * H * 128,
                                        static_cast<const bf16_t*>(kc) + b0 * kv_seq,
                                        static_cast<const bf16_t*>(vc) + b0 * kv_seq, pos + b0,
-                                       o + static_cast<size_t>(b0) * H * 128, L->part, ns, nb, H, Hkv,
+                                       o + static_cast<size_t>(b0) * H * 128, skinny, L->part, ns, nb, H, Hkv,
                                        c.max_pos, s),
                     "decode attention");
     }
   } else {
     HIP_OR_RETURN(launch_attn_prefill(q, static_cast<const bf16_t*>(kc), static_cast<const bf16_t*>(vc), pos,
-                                      o, B, T, H, Hkv, c.max_pos, s),
+                                      o, skinny, B, T, H, Hkv, c.max_pos, s),
                   "prefill attention");
   }
   HIP_OR_RETURN(mark(3), "event record");
@@ -379,7 +398,7 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
                        : launch_gemm_resid_f32out(o, wo, M, d, H * 128, xb, L->x1, s),
                 "o_proj");
   HIP_OR_RETURN(mark(4), "event record");
-  HIP_OR_RETURN(launch_rmsnorm(L->x1, 1, L->g2, 0, xn, 0, M, d, c.rms_eps, s), "rmsnorm 2");
+  HIP_OR_RETURN(launch_rmsnorm(L->x1, 1, L->g2, 0, xn, 0, skinny, M, d, c.rms_eps, s), "rmsnorm 2");
   HIP_OR_RETURN(mark(5), "event record");
   HIP_OR_RETURN(skinny ? launch_skinny_swiglu(xn, wgu, M, f, d, h, s)
                        : launch_gemm_swiglu(xn, wgu, M, 2 * f, d, h, s),

@@ -1,0 +1,32 @@
+// Weight layout conversion at layer creation: row-major bf16 -> fragment
+// order (the v_mfma_f32_32x32x16_bf16 operand layout, one contiguous 1 KB
+// wavefront load per 32 x 16 chunk).  Runs once per layer; not on the hot path.
+#include "common.h"
+
+namespace llama {
+namespace {
+
+// one thread per 16-byte vector (8 consecutive k of one row)
+__global__ __launch_bounds__(256) void pack_rows_kernel(const uint4* __restrict__ src, int rows, int K,
+                                                        bf16_t* __restrict__ dst, int group, int group_stride) {
+  const size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  const int kv = K >> 3;
+  if (i >= static_cast<size_t>(rows) * kv) return;
+  const int r = static_cast<int>(i / kv), k = static_cast<int>(i % kv) * 8;
+  const int dr = (r / group) * group_stride + r % group;
+  *reinterpret_cast<uint4*>(dst + frag_index(dr, k, K)) = src[i];
+}
+
+}  // namespace
+
+hipError_t launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int group, int group_stride,
+                            hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (rows % 32 || group % 32 || K % 16 || group <= 0) return hipErrorInvalidValue;
+  const size_t n = static_cast<size_t>(rows) * (K / 8);
+  hipLaunchKernelGGL(pack_rows_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
+                     reinterpret_cast<const uint4*>(src), rows, K, dst, group, group_stride);
+  return hipGetLastError();
+}
+
+}  // namespace llama

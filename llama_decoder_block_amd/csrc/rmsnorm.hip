@@ -42,8 +42,9 @@ __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 
 constexpr int kRowsPerBlock = 4;  // 4 waves, one row each
 
-// d % 8 == 0 and d <= NV * 512.
-template <typename TIn, typename TG, typename TOut, int NV>
+// d % 8 == 0 and d <= NV * 512.  FRAG: bf16 out in fragment order (the
+// 16-byte vector of k = 8 vi .. 8 vi + 7 stays contiguous there).
+template <typename TIn, typename TG, typename TOut, int NV, bool FRAG>
 __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const TIn* __restrict__ in,
                                                           const TG* __restrict__ g,
                                                           TOut* __restrict__ out, int rows,
@@ -66,7 +67,7 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const TIn* __restrict_
   }
   ss = warp_sum(ss);
   const float inv = rsqrtf(ss / static_cast<float>(d) + eps);
-  TOut* y = out + static_cast<size_t>(row) * d;
+  TOut* y = out + (FRAG ? 0 : static_cast<size_t>(row) * d);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int vi = lane + j * kWave;
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const TIn* __restrict_
       load8(g + vi * 8, gv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) v[j][e] = gv[e] * (v[j][e] * inv);
-      store8(y + vi * 8, v[j]);
+      store8(y + (FRAG ? frag_index(row, vi * 8, d) : vi * 8), v[j]);
     }
   }
 }
@@ -101,7 +102,7 @@ __global__ __launch_bounds__(256) void rmsnorm_any_kernel(const TIn* __restrict_
   for (int i = lane; i < d; i += kWave) store1(y + i, load1(g + i) * (load1(x + i) * inv));
 }
 
-template <typename TIn, typename TG, typename TOut>
+template <typename TIn, typename TG, typename TOut, bool FRAG = false>
 hipError_t dispatch(const void* in, const void* g, void* out, int rows, int d, float eps,
                     hipStream_t s) {
   const dim3 grid((rows + kRowsPerBlock - 1) / kRowsPerBlock), block(256);
@@ -111,12 +112,13 @@ hipError_t dispatch(const void* in, const void* g, void* out, int rows, int d, f
   const int nv = (d + 511) / 512;
   if (d % 8 == 0 && nv <= 16) {
     if (nv <= 8)
-      hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 8>), grid, block, 0, s, x, gg, y, rows, d, eps);
+      hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 8, FRAG>), grid, block, 0, s, x, gg, y, rows, d, eps);
     else if (nv <= 10)
-      hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 10>), grid, block, 0, s, x, gg, y, rows, d, eps);
+      hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 10, FRAG>), grid, block, 0, s, x, gg, y, rows, d, eps);
     else
-      hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 16>), grid, block, 0, s, x, gg, y, rows, d, eps);
+      hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 16, FRAG>), grid, block, 0, s, x, gg, y, rows, d, eps);
   } else {
+    if (FRAG) return hipErrorInvalidValue;
     hipLaunchKernelGGL((rmsnorm_any_kernel<TIn, TG, TOut>), grid, block, 0, s, x, gg, y, rows, d, eps);
   }
   return hipGetLastError();
@@ -125,8 +127,13 @@ hipError_t dispatch(const void* in, const void* g, void* out, int rows, int d, f
 }  // namespace
 
 hipError_t launch_rmsnorm(const void* in, int in_f32, const void* gain, int gain_f32, void* out,
-                          int out_f32, int rows, int d, float eps, hipStream_t s) {
+                          int out_f32, int out_frag, int rows, int d, float eps, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
+  if (out_frag) {
+    if (out_f32 || gain_f32 || d % 128 != 0) return hipErrorInvalidValue;
+    return in_f32 ? dispatch<float, bf16_t, bf16_t, true>(in, gain, out, rows, d, eps, s)
+                  : dispatch<bf16_t, bf16_t, bf16_t, true>(in, gain, out, rows, d, eps, s);
+  }
   if (!in_f32 && !gain_f32 && !out_f32) return dispatch<bf16_t, bf16_t, bf16_t>(in, gain, out, rows, d, eps, s);
   if (in_f32 && !gain_f32 && !out_f32) return dispatch<float, bf16_t, bf16_t>(in, gain, out, rows, d, eps, s);
   if (in_f32 && gain_f32 && out_f32) return dispatch<float, float, float>(in, gain, out, rows, d, eps, s);
