@@ -7,18 +7,24 @@
 // softmax, weighted sum of values; repeat_kv grouped-query attention, here
 // kv-head indexing so a K/V row read serves all query heads of its group).
 //
-// gfx950 design: the cache is streamed once at HBM rate.
-//   * split-K: workgroup (split s, kv head g, sequence b) takes slots
-//     [s L, (s+1) L) ∩ [0, p]; L is chosen so the grid holds well over 256
-//     workgroups even at batch 1 with 8 kv heads;
+// gfx950 design: the cache is streamed once at HBM rate, K and V together.
+//   * workgroup (split s, kv head g, sequence b) takes slots
+//     [s L, (s+1) L) ∩ [0, p]; the split length is chosen so the grid holds
+//     about 1024 workgroups (4 per CU).  With that many (sequence, kv head)
+//     pairs already, there is one split and the workgroup writes the
+//     normalised output itself; otherwise each split writes (max, sum,
+//     unnormalised o[128]) per head and a second kernel merges them (the
+//     standard split-softmax merge);
 //   * a K or V row (128 dims = 256 B) is read by 16 lanes with 16-byte loads,
-//     so a wavefront reads 4 consecutive rows = 1 KB contiguous per load;
-//   * scores: each lane dots its 8 dims with the query slice of every head of
-//     the group, then a 16-lane shuffle reduction; scores live in LDS;
-//   * a local softmax (max and sum in fp32, base-2 exponent with the scale
-//     folded in), then P V accumulated per lane over 8 dims x heads;
-//   * each split writes (max, sum, unnormalised o[128]) per head; a second
-//     kernel rescales and adds the splits (the standard split-softmax merge).
+//     so a wavefront reads 4 consecutive rows = 1 KB contiguous per load; each
+//     lane keeps 4 K and 4 V loads in flight;
+//   * 16 row groups of 16 lanes each own the slots of one residue mod 16 and
+//     run an online softmax over them (running max and sum in fp32, base-2
+//     exponent with the scale folded into q): per 4 slots, the scores come
+//     from a 16-lane shuffle reduction, the running output (8 dims x heads per
+//     lane) is rescaled once and the 4 weighted V rows are added;
+//   * the 16 row-group states are merged with the same rule (shuffles within a
+//     wave, LDS across the 4 waves).
 #include "common.h"
 
 #include <math.h>
@@ -27,17 +33,28 @@ namespace llama {
 namespace {
 
 constexpr int DH = 128;
-constexpr int kMaxRep = 8;    // query heads handled per workgroup
-constexpr int kMaxL = 512;    // slots per split (upper bound)
+constexpr int kMaxRep = 8;  // query heads handled per workgroup
+constexpr int kTargetWGs = 1024;
+
+// (m1, l1, a1) <- merge with (m2, l2, a2): both scaled to the larger max
+__device__ __forceinline__ void softmax_merge(float& m1, float& l1, float* a1, float m2, float l2,
+                                              const float* a2, int n) {
+  const float m = fmaxf(m1, m2);
+  const float mu = m == -INFINITY ? 0.f : m;
+  const float c1 = fast_exp2(m1 - mu), c2 = fast_exp2(m2 - mu);
+  l1 = l1 * c1 + l2 * c2;
+  for (int e = 0; e < n; ++e) a1[e] = a1[e] * c1 + a2[e] * c2;
+  m1 = m;
+}
 
 template <int R>
-__global__ __launch_bounds__(256) void attn_decode_split_kernel(
+__global__ __launch_bounds__(256) void attn_decode_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ pos, float* __restrict__ part,
-    int H, int Hkv, int max_pos, int L, int n_split, float scale_log2) {
-  __shared__ float sc[R][kMaxL];
-  __shared__ float red[4][R][DH];
-  __shared__ float stat[R][2];
+    bf16_t* __restrict__ o, int o_frag, int H, int Hkv, int max_pos, int L, int n_split,
+    float scale_log2) {
+  __shared__ float red_ml[4][R][2];
+  __shared__ float red_o[4][R][DH];
 
   const int s = blockIdx.x, hg = blockIdx.y, b = blockIdx.z;
   const int n_rep = H / Hkv;
@@ -46,14 +63,14 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
   const int h0 = g * n_rep + (hg % chunks) * R;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int dc = lane & 15;                // 8-dim chunk of a row
-  const int sub = wave * 4 + (lane >> 4);  // 16 row groups per workgroup
+  const int sub = wave * 4 + (lane >> 4);  // row group: slots = sub (mod 16)
 
   const int p = min(pos[b], max_pos - 1);
   const int j_begin = s * L;
   const int j_end = min(j_begin + L, p + 1);
   const int n = j_end - j_begin;
   float* out = part + ((static_cast<size_t>(b) * H + h0) * n_split + s) * (DH + 2);
-  if (n <= 0) {  // nothing visible in this split
+  if (n <= 0) {  // nothing visible in this split (only with several splits)
     for (int i = tid; i < R * (DH + 2); i += 256) {
       const int r = i / (DH + 2), e = i % (DH + 2);
       out[static_cast<size_t>(r) * n_split * (DH + 2) + e] = e == 0 ? -INFINITY : 0.f;
@@ -61,26 +78,39 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
     return;
   }
 
-  // query slices: 8 dims per lane for each of the R heads
+  // query slices, 8 dims per lane per head, pre-scaled so scores are in log2 units
   float qv[R][8];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const uint4 u = *reinterpret_cast<const uint4*>(q + (static_cast<size_t>(b) * H + h0 + r) * DH + dc * 8);
     qv[r][0] = lo_bf16(u.x); qv[r][1] = hi_bf16(u.x); qv[r][2] = lo_bf16(u.y); qv[r][3] = hi_bf16(u.y);
     qv[r][4] = lo_bf16(u.z); qv[r][5] = hi_bf16(u.z); qv[r][6] = lo_bf16(u.w); qv[r][7] = hi_bf16(u.w);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qv[r][e] *= scale_log2;
   }
 
   const size_t slice = (static_cast<size_t>(b) * Hkv + g) * max_pos * DH;
   const bf16_t* K = k_cache + slice + static_cast<size_t>(j_begin) * DH + dc * 8;
   const bf16_t* V = v_cache + slice + static_cast<size_t>(j_begin) * DH + dc * 8;
 
-  // ---- scores
-  for (int j = sub; j < n; j += 16 * 4) {
-    uint4 ku[4];
+  float m[R], l[R], acc[R][8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      ku[u] = (j + 16 * u < n) ? *reinterpret_cast<const uint4*>(K + static_cast<size_t>(j + 16 * u) * DH)
-                               : make_uint4(0, 0, 0, 0);
+  for (int r = 0; r < R; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
+  }
+
+  for (int j = sub; j < n; j += 64) {
+    uint4 ku[4], vu[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool ok = j + 16 * u < n;
+      ku[u] = ok ? *reinterpret_cast<const uint4*>(K + static_cast<size_t>(j + 16 * u) * DH) : make_uint4(0, 0, 0, 0);
+      vu[u] = ok ? *reinterpret_cast<const uint4*>(V + static_cast<size_t>(j + 16 * u) * DH) : make_uint4(0, 0, 0, 0);
+    }
+    float sc[R][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       float kf[8];
@@ -95,78 +125,67 @@ __global__ __launch_bounds__(256) void attn_decode_split_kernel(
         d += __shfl_xor(d, 2, 64);
         d += __shfl_xor(d, 4, 64);
         d += __shfl_xor(d, 8, 64);
-        if (dc == 0 && j + 16 * u < n) sc[r][j + 16 * u] = d * scale_log2;
+        sc[r][u] = j + 16 * u < n ? d : -INFINITY;  // slots past the split are masked
       }
     }
-  }
-  __syncthreads();
-
-  // ---- local softmax per head (one wave per head, heads strided by 4)
-  for (int r = wave; r < R; r += 4) {
-    float m = -INFINITY;
-    for (int j = lane; j < n; j += 64) m = fmaxf(m, sc[r][j]);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    float l = 0.f;
-    for (int j = lane; j < n; j += 64) {
-      const float e = fast_exp2(sc[r][j] - m);
-      sc[r][j] = e;
-      l += e;
+    for (int r = 0; r < R; ++r) {
+      const float mx = fmaxf(fmaxf(sc[r][0], sc[r][1]), fmaxf(sc[r][2], sc[r][3]));
+      const float m_new = fmaxf(m[r], mx);  // finite: slot j itself is visible
+      const float c = fast_exp2(m[r] - m_new);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) sc[r][u] = fast_exp2(sc[r][u] - m_new);  // weights; 0 where masked
+      l[r] = l[r] * c + ((sc[r][0] + sc[r][1]) + (sc[r][2] + sc[r][3]));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[r][e] *= c;
+      m[r] = m_new;
     }
-    l = warp_sum(l);
-    if (lane == 0) { stat[r][0] = m; stat[r][1] = l; }
-  }
-  __syncthreads();
-
-  // ---- P V: lane accumulates 8 dims x R heads over its rows
-  float acc[R][8];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
-  for (int j = sub; j < n; j += 16 * 4) {
-    uint4 vu[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      vu[u] = (j + 16 * u < n) ? *reinterpret_cast<const uint4*>(V + static_cast<size_t>(j + 16 * u) * DH)
-                               : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      if (j + 16 * u >= n) break;
       float vf[8];
       vf[0] = lo_bf16(vu[u].x); vf[1] = hi_bf16(vu[u].x); vf[2] = lo_bf16(vu[u].y); vf[3] = hi_bf16(vu[u].y);
       vf[4] = lo_bf16(vu[u].z); vf[5] = hi_bf16(vu[u].z); vf[6] = lo_bf16(vu[u].w); vf[7] = hi_bf16(vu[u].w);
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const float pr = sc[r][j + 16 * u];
+      for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] += pr * vf[e];
-      }
+        for (int e = 0; e < 8; ++e) acc[r][e] += sc[r][u] * vf[e];
     }
   }
-  // reduce the 4 row groups of a wave (lanes 16 apart), then the 4 waves via LDS
+
+  // merge the 4 row groups of a wave (lanes 16 and 32 apart), then the 4 waves
 #pragma unroll
-  for (int r = 0; r < R; ++r)
+  for (int x = 16; x <= 32; x <<= 1)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      float v = acc[r][e];
-      v += __shfl_xor(v, 16, 64);
-      v += __shfl_xor(v, 32, 64);
-      acc[r][e] = v;
+    for (int r = 0; r < R; ++r) {
+      const float m2 = __shfl_xor(m[r], x, 64), l2 = __shfl_xor(l[r], x, 64);
+      float a2[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a2[e] = __shfl_xor(acc[r][e], x, 64);
+      softmax_merge(m[r], l[r], acc[r], m2, l2, a2, 8);
     }
   if (lane < 16) {
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) red[wave][r][dc * 8 + e] = acc[r][e];
+      for (int e = 0; e < 8; ++e) red_o[wave][r][dc * 8 + e] = acc[r][e];
+      if (dc == 0) { red_ml[wave][r][0] = m[r]; red_ml[wave][r][1] = l[r]; }
+    }
   }
   __syncthreads();
   for (int i = tid; i < R * DH; i += 256) {
     const int r = i / DH, d = i % DH;
-    const float v = red[0][r][d] + red[1][r][d] + red[2][r][d] + red[3][r][d];
-    float* o = out + static_cast<size_t>(r) * n_split * (DH + 2);
-    o[2 + d] = v;
-    if (d == 0) { o[0] = stat[r][0]; o[1] = stat[r][1]; }
+    float mm = red_ml[0][r][0], ll = red_ml[0][r][1], aa = red_o[0][r][d];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) softmax_merge(mm, ll, &aa, red_ml[w][r][0], red_ml[w][r][1], &red_o[w][r][d], 1);
+    if (n_split == 1) {
+      const int hh = h0 + r;
+      const size_t at = o_frag ? frag_index(b, hh * DH + d, H * DH) : (static_cast<size_t>(b) * H + hh) * DH + d;
+      o[at] = f32_to_bf16(ll > 0.f ? aa / ll : 0.f);
+    } else {
+      float* po = out + static_cast<size_t>(r) * n_split * (DH + 2);
+      po[2 + d] = aa;
+      if (d == 0) { po[0] = mm; po[1] = ll; }
+    }
   }
 }
 
@@ -192,13 +211,15 @@ __global__ __launch_bounds__(128) void attn_decode_combine_kernel(const float* _
   o[at] = f32_to_bf16(den > 0.f ? num / den : 0.f);
 }
 
-int split_len(int max_pos, int B, int Hkv) {
-  // aim for >= ~2048 split workgroups in all
-  const long long rows = static_cast<long long>(max_pos) * B * Hkv;
-  long long L = (rows + 2047) / 2048;
+// slots per split: one split when the (sequence, kv head, head chunk)
+// workgroups already number kTargetWGs, else enough splits to get there
+int split_len(int max_pos, int B, int Hkv, int chunks) {
+  const long long wgs = static_cast<long long>(B) * Hkv * chunks;
+  if (wgs >= kTargetWGs) return max_pos;
+  long long L = (static_cast<long long>(max_pos) * wgs + kTargetWGs - 1) / kTargetWGs;
   L = (L + 63) / 64 * 64;
   if (L < 64) L = 64;
-  if (L > kMaxL) L = kMaxL;
+  if (L > max_pos) L = max_pos;
   return static_cast<int>(L);
 }
 
@@ -210,8 +231,9 @@ int heads_per_block(int n_rep) {
 
 }  // namespace
 
-int decode_attn_splits(int max_pos, int B, int n_kv_heads) {
-  const int L = split_len(max_pos, B, n_kv_heads);
+int decode_attn_splits(int max_pos, int B, int n_heads, int n_kv_heads) {
+  const int n_rep = n_heads / n_kv_heads;
+  const int L = split_len(max_pos, B, n_kv_heads, n_rep / heads_per_block(n_rep));
   return (max_pos + L - 1) / L;
 }
 
@@ -219,17 +241,17 @@ hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16
                               const int32_t* pos, bf16_t* o, int o_frag, float* part, int n_split,
                               int B, int n_heads, int n_kv_heads, int max_pos, hipStream_t s) {
   if (o_frag && B > kSkinnyMaxTokens) return hipErrorInvalidValue;
-  const int L = split_len(max_pos, B, n_kv_heads);
-  if ((max_pos + L - 1) / L != n_split) return hipErrorInvalidValue;
   const int n_rep = n_heads / n_kv_heads;
   const int R = heads_per_block(n_rep);
+  const int L = split_len(max_pos, B, n_kv_heads, n_rep / R);
+  if ((max_pos + L - 1) / L != n_split) return hipErrorInvalidValue;
   const dim3 grid(n_split, n_kv_heads * (n_rep / R), B);
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
   switch (R) {
 #define LLAMA_DEC_CASE(RR)                                                                              \
   case RR:                                                                                              \
-    hipLaunchKernelGGL(attn_decode_split_kernel<RR>, grid, dim3(256), 0, s, q, k_cache, v_cache, pos,  \
-                       part, n_heads, n_kv_heads, max_pos, L, n_split, scale_log2);                     \
+    hipLaunchKernelGGL(attn_decode_kernel<RR>, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, part,  \
+                       o, o_frag, n_heads, n_kv_heads, max_pos, L, n_split, scale_log2);                \
     break;
     LLAMA_DEC_CASE(1) LLAMA_DEC_CASE(2) LLAMA_DEC_CASE(3) LLAMA_DEC_CASE(4)
     LLAMA_DEC_CASE(5) LLAMA_DEC_CASE(6) LLAMA_DEC_CASE(7) LLAMA_DEC_CASE(8)
@@ -237,7 +259,7 @@ hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || n_split == 1) return e;
   hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(B * n_heads), dim3(DH), 0, s, part, o, o_frag, n_heads,
                      n_split);
   return hipGetLastError();

@@ -139,10 +139,11 @@ hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf1
                                const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
                                int n_kv_heads, int max_pos, hipStream_t s);
 
-// Split-K decode attention (bf16, dh = 128) for one query per sequence,
-// followed by the combine of the splits.  part holds
-// B*H*n_split*(128+2) floats; o_frag as for the prefill kernel.
-int decode_attn_splits(int max_pos, int B, int n_kv_heads);
+// Decode attention (bf16, dh = 128) for one query per sequence, split over
+// the cache when the grid would otherwise be small, followed by the merge of
+// the splits (n_split > 1 only).  part holds B*H*n_split*(128+2) floats;
+// o_frag as for the prefill kernel.
+int decode_attn_splits(int max_pos, int B, int n_heads, int n_kv_heads);
 hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                               const int32_t* pos, bf16_t* o, int o_frag, float* part, int n_split,
                               int B, int n_heads, int n_kv_heads, int max_pos, hipStream_t s);

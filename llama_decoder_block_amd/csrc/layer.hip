@@ -163,7 +163,7 @@ int part_floats(const llama_layer_config& c, int* seqs) {
   const int s = c.max_tokens < kDecodeChunk ? c.max_tokens : kDecodeChunk;
   long long best = 0;
   for (int b = 1; b <= s; ++b) {
-    const long long n = static_cast<long long>(b) * c.n_heads * decode_attn_splits(c.max_pos, b, c.n_kv_heads) * 130;
+    const long long n = static_cast<long long>(b) * c.n_heads * decode_attn_splits(c.max_pos, b, c.n_heads, c.n_kv_heads) * 130;
     if (n > best) best = n;
   }
   *seqs = s;
@@ -380,7 +380,7 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
     const size_t kv_seq = static_cast<size_t>(Hkv) * c.max_pos * 128;
     for (int b0 = 0; b0 < B; b0 += L->part_seqs) {
       const int nb = B - b0 < L->part_seqs ? B - b0 : L->part_seqs;
-      const int ns = decode_attn_splits(c.max_pos, nb, Hkv);
+      const int ns = decode_attn_splits(c.max_pos, nb, H, Hkv);
       HIP_OR_RETURN(launch_attn_decode(q + static_cast<size_t>(b0) * H * 128,
                                        static_cast<const bf16_t*>(kc) + b0 * kv_seq,
                                        static_cast<const bf16_t*>(vc) + b0 * kv_seq, pos + b0,
