@@ -122,15 +122,27 @@ hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, 
 // W both in fragment order (A holds ceil(M/32)*32 rows; rows >= M are never
 // written out, whatever they hold).  The SwiGLU output h is written in
 // fragment order, ready to be the A operand of the down projection.
+// Scratch for column groups split between workgroups: part holds
+// skinny_scratch_floats() floats, cnt one counter per column group (N / 32
+// at most), all zero before the first call; each call leaves them zero.
+// Calls that share a scratch must not overlap.
 constexpr int kSkinnyMaxTokens = 64;
+constexpr int kSkinnyGrid = 512;  // workgroups per call, at most
+struct SkinnyScratch {
+  float* part;
+  unsigned* cnt;
+};
+size_t skinny_scratch_floats();
 hipError_t launch_skinny_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,
-                             const QkvEpilogue& ep, hipStream_t s);
+                             const QkvEpilogue& ep, const SkinnyScratch& sc, hipStream_t s);
 hipError_t launch_skinny_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
-                                      const bf16_t* resid, float* out, hipStream_t s);
+                                      const bf16_t* resid, float* out, const SkinnyScratch& sc,
+                                      hipStream_t s);
 hipError_t launch_skinny_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
-                                       const float* resid, bf16_t* out, hipStream_t s);
+                                       const float* resid, bf16_t* out, const SkinnyScratch& sc,
+                                       hipStream_t s);
 hipError_t launch_skinny_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int f, int K,
-                                bf16_t* out, hipStream_t s);
+                                bf16_t* out, const SkinnyScratch& sc, hipStream_t s);
 
 // Causal flash attention over the cache for prefill (bf16, dh = 128).
 // q/o [B*T, H*128]; the query of token m sees cache slots 0..pos[m].

@@ -24,6 +24,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -83,6 +84,7 @@ struct llama_layer {
   float* gu = nullptr;    // fp32 path: [max_tokens, 2f]
   float* part = nullptr;  // split-K partials
   int part_seqs = 0;      // sequences the partial buffer holds at once
+  SkinnyScratch sk{};     // split column groups of the weight-streaming GEMMs
   // per-step event timing (measurement aid)
   static constexpr int kRing = 256;
   bool prof_on = false;
@@ -118,7 +120,7 @@ void release(llama_layer* L) {
     for (auto& row : L->ev)
       for (auto& e : row) (void)hipEventDestroy(e);
   void* bufs[] = {L->wqkv, L->wo, L->wgu, L->wd, L->g1, L->g2, L->rope_cos, L->rope_sin,
-                  L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part};
+                  L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->sk.part, L->sk.cnt};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
 }
@@ -243,6 +245,10 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
     ALLOC_OR_FAIL(L->q, mt * nq * es);
     const int pf = part_floats(*cfg, &L->part_seqs);
     ALLOC_OR_FAIL(L->part, static_cast<size_t>(pf) * sizeof(float));
+    ALLOC_OR_FAIL(L->sk.part, skinny_scratch_floats() * sizeof(float));
+    const size_t groups = std::max({(nq + 2 * nkv) / 64, 2 * f / 64, d / 32});
+    ALLOC_OR_FAIL(L->sk.cnt, groups * sizeof(unsigned));
+    HIP_OR_FAIL(hipMemsetAsync(L->sk.cnt, 0, groups * sizeof(unsigned), s), "clear counters");
   } else {
     ALLOC_OR_FAIL(L->q, mt * (nq + 2 * nkv) * es);
     ALLOC_OR_FAIL(L->gu, mt * 2 * f * sizeof(float));
@@ -372,7 +378,7 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
   HIP_OR_RETURN(mark(0), "event record");
   HIP_OR_RETURN(launch_rmsnorm(xb, 0, L->g1, 0, xn, 0, skinny, M, d, c.rms_eps, s), "rmsnorm 1");
   HIP_OR_RETURN(mark(1), "event record");
-  HIP_OR_RETURN(skinny ? launch_skinny_qkv(xn, wqkv, M, nqkv, d, ep, s)
+  HIP_OR_RETURN(skinny ? launch_skinny_qkv(xn, wqkv, M, nqkv, d, ep, L->sk, s)
                        : launch_gemm_qkv(xn, wqkv, M, nqkv, d, ep, s),
                 "qkv projection");
   HIP_OR_RETURN(mark(2), "event record");
@@ -394,17 +400,17 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
                   "prefill attention");
   }
   HIP_OR_RETURN(mark(3), "event record");
-  HIP_OR_RETURN(skinny ? launch_skinny_resid_f32out(o, wo, M, d, H * 128, xb, L->x1, s)
+  HIP_OR_RETURN(skinny ? launch_skinny_resid_f32out(o, wo, M, d, H * 128, xb, L->x1, L->sk, s)
                        : launch_gemm_resid_f32out(o, wo, M, d, H * 128, xb, L->x1, s),
                 "o_proj");
   HIP_OR_RETURN(mark(4), "event record");
   HIP_OR_RETURN(launch_rmsnorm(L->x1, 1, L->g2, 0, xn, 0, skinny, M, d, c.rms_eps, s), "rmsnorm 2");
   HIP_OR_RETURN(mark(5), "event record");
-  HIP_OR_RETURN(skinny ? launch_skinny_swiglu(xn, wgu, M, f, d, h, s)
+  HIP_OR_RETURN(skinny ? launch_skinny_swiglu(xn, wgu, M, f, d, h, L->sk, s)
                        : launch_gemm_swiglu(xn, wgu, M, 2 * f, d, h, s),
                 "gate/up projection");
   HIP_OR_RETURN(mark(6), "event record");
-  HIP_OR_RETURN(skinny ? launch_skinny_resid_bf16out(h, wd, M, d, f, L->x1, yb, s)
+  HIP_OR_RETURN(skinny ? launch_skinny_resid_bf16out(h, wd, M, d, f, L->x1, yb, L->sk, s)
                        : launch_gemm_resid_bf16out(h, wd, M, d, f, L->x1, yb, s),
                 "down projection");
   HIP_OR_RETURN(mark(7), "event record");

@@ -8,13 +8,24 @@
 // gfx950 design.  Both operands are in fragment order, so every load is one
 // contiguous 1 KB wavefront load straight into registers: a 32 x 16 weight
 // fragment (A operand of v_mfma_f32_32x32x16_bf16, rows = output features)
-// and a 32-token x 16 activation fragment (B operand, columns = tokens).  A
-// workgroup owns NB 32-row blocks of W and all tokens; its NW wavefronts take
-// the 16-wide k steps round-robin and keep DEPTH steps of loads in flight in
-// a register ring (branch-free: steps past the end point the load past the
-// buffer's range, which reads zeros).  The partial tiles of the waves are
-// added through LDS at the end.  Each weight byte is read exactly once; the
-// activations (<= 64 x K bf16) are re-read by every workgroup from L2.
+// and a 32-token x 16 activation fragment (B operand, columns = tokens).
+//
+// Work split.  A column group is NB 32-row blocks of W; its work is K/16 k
+// steps.  The groups' k steps are laid end to end and the grid's G workgroups
+// take equal contiguous ranges of them (G = groups x S: each group cut into S
+// ranges when there are too few groups to cover the CUs).  Inside a workgroup the NW
+// wavefronts take the k steps of a group round-robin and keep DEPTH steps of
+// loads in flight in a register ring (branch-free: steps past the end point
+// the load past the buffer's range, which reads zeros); their partial tiles
+// are added through LDS.  A group that lies wholly in one workgroup's range is
+// finished there.  A group cut between workgroups is finished by whichever
+// of them arrives last: each writes its partial tile with agent-scope atomic
+// stores (coherent across the XCDs' L2s without an L2 write-back), waits for
+// them to complete, and counts itself in on the group's counter; the last
+// one reads all partials back, adds them in range order (so the result does
+// not depend on arrival order) and runs the epilogue, then re-arms the
+// counter.  Each weight byte is read exactly once; the activations (<= 64 x
+// K bf16) are re-read by every workgroup from L2.
 //
 // Pairing: with NB = 2 the blocks are nb and nb + 2, so one lane holds
 // feature i and feature i + 64 of the same 128-row group for the same token
@@ -32,94 +43,42 @@ struct SkinnyArgs {
   QkvEpilogue qkv;
   const void* resid;
   void* out;
+  float* part;     // 2 G partial slots of NB * TB * 1024 floats
+  unsigned* cnt;   // per column group, zero between launches
 };
 
 template <int NB, int TB, int NW, int DEPTH, int EPI>
 __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restrict__ Xp,
                                                          const bf16_t* __restrict__ Wp, int M, int N,
-                                                         int K, SkinnyArgs ep) {
-  __shared__ float red[NW][NB * TB][64][17];
+                                                         int K, int G, SkinnyArgs ep) {
+  constexpr int NT = NB * TB;  // 32 x 32 tiles per column group
+  __shared__ float red[NW][NT][64][17];
+  __shared__ unsigned s_last;
   const int tid = threadIdx.x, lane = tid & 63;
   // wave index as a scalar, so that everything derived from it stays uniform
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int KB = K >> 4;
-  const int grp = blockIdx.x;
-  const int nb0 = NB == 2 ? (grp >> 1) * 4 + (grp & 1) : grp;
+  const long long W = static_cast<long long>(N / (32 * NB)) * KB;  // k steps of all groups
+  auto start_of = [&](int w) -> long long { return W * w / G; };
+  auto owner = [&](long long x) -> int {  // the workgroup whose range holds step x
+    int w = static_cast<int>(x * G / W);
+    while (w + 1 < G && start_of(w + 1) <= x) ++w;
+    return w;
+  };
+  const int wg = blockIdx.x;
+  const long long u0 = start_of(wg), u1 = start_of(wg + 1);
   const uint32_t w_bytes = static_cast<uint32_t>(N) * K * 2u;
   const uint32_t x_bytes = static_cast<uint32_t>(TB) * 32u * K * 2u;
   const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(Wp, w_bytes);
   const __amdgpu_buffer_rsrc_t x_rs = make_rsrc(Xp, x_bytes);
 
-  f32x16 acc[NB][TB];
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][t][r] = 0.f;
-
-  const int nsteps = (KB - wave + NW - 1) / NW;  // k steps wave, wave + NW, ...
-  uint4 wv[DEPTH][NB], xv[DEPTH][TB];
-  auto issue = [&](int slot, int st) {
-    const uint32_t kb = static_cast<uint32_t>(wave + st * NW);
-    const bool ok = st < nsteps;
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-      const uint32_t off = ((static_cast<uint32_t>(nb0 + 2 * j) * KB + kb) << 10) + lane * 16u;
-      wv[slot][j] = buf_load16(w_rs, ok ? off : w_bytes, 0);
-    }
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      const uint32_t off = ((static_cast<uint32_t>(t) * KB + kb) << 10) + lane * 16u;
-      xv[slot][t] = buf_load16(x_rs, ok ? off : x_bytes, 0);
-    }
-  };
-  // the sched barriers keep every step's loads in issue order, which lets
-  // the compiler wait for exactly the oldest step instead of draining the ring
-#pragma unroll
-  for (int d = 0; d < DEPTH; ++d) {
-    issue(d, d);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  for (int st = 0; st < nsteps; st += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-          acc[j][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv[d][j]),
-                                                              __builtin_bit_cast(bf16x8, xv[d][t]),
-                                                              acc[j][t], 0, 0, 0);
-      issue(d, st + d + DEPTH);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-
-#pragma unroll
-  for (int j = 0; j < NB; ++j)
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) red[wave][j * TB + t][lane][r] = acc[j][t][r];
-  __syncthreads();
-
-  // epilogue: wave t finishes token block t.  Accumulator slot r of a lane
-  // is feature 8 (r/4) + 4 (lane/32) + r%4 of its block, token lane % 32, so
-  // four consecutive slots are four consecutive features.
-  for (int t = wave; t < TB; t += NW) {
-    float v[NB][16];
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float a = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) a += red[w][j * TB + t][lane][r];
-        v[j][r] = a;
-      }
+  // the epilogue of token block t of group g, from the finished sums v[j][r]
+  auto finish = [&](int g, int t, const float (&v)[NB][16]) {
+    const int nb0 = NB == 2 ? (g >> 1) * 4 + (g & 1) : g;
     const int tok = t * 32 + (lane & 31);
-    if (tok >= M) continue;
+    if (tok >= M) return;
+    // accumulator slot r of a lane is feature 8 (r/4) + 4 (lane/32) + r%4 of
+    // its block, token lane % 32: four consecutive slots, four consecutive features
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const int fib = 8 * r4 + 4 * (lane >> 5);  // first of the 4 features in the block
@@ -186,60 +145,205 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
         }
       }
     }
+  };
+
+  // partial slot of workgroup w's segment of group g: 2w if w's range starts
+  // inside g, 2w + 1 if g is where it ends
+  auto slot_of = [&](int w, int g) { return 2 * w + (start_of(w) >= static_cast<long long>(g) * KB ? 0 : 1); };
+
+  for (long long u = u0; u < u1;) {
+    const int g = static_cast<int>(u / KB);
+    const int k0 = static_cast<int>(u - static_cast<long long>(g) * KB);
+    const int k1 = static_cast<int>(min(static_cast<long long>(KB), u1 - static_cast<long long>(g) * KB));
+    u = static_cast<long long>(g) * KB + k1;
+    const int nb0 = NB == 2 ? (g >> 1) * 4 + (g & 1) : g;
+
+    f32x16 acc[NB][TB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[j][t][r] = 0.f;
+
+    const int nsteps = max(0, (k1 - k0 - wave + NW - 1) / NW);  // k steps k0 + wave, + NW, ...
+    uint4 wv[DEPTH][NB], xv[DEPTH][TB];
+    auto issue = [&](int slot, int st) {
+      const uint32_t kb = static_cast<uint32_t>(k0 + wave + st * NW);
+      const bool ok = st < nsteps;
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint32_t off = ((static_cast<uint32_t>(nb0 + 2 * j) * KB + kb) << 10) + lane * 16u;
+        wv[slot][j] = buf_load16(w_rs, ok ? off : w_bytes, 0);
+      }
+#pragma unroll
+      for (int t = 0; t < TB; ++t) {
+        const uint32_t off = ((static_cast<uint32_t>(t) * KB + kb) << 10) + lane * 16u;
+        xv[slot][t] = buf_load16(x_rs, ok ? off : x_bytes, 0);
+      }
+    };
+    // the sched barriers keep every step's loads in issue order, which lets
+    // the compiler wait for exactly the oldest step instead of draining the ring
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      issue(d, d);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int st = 0; st < nsteps; st += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int t = 0; t < TB; ++t)
+            acc[j][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv[d][j]),
+                                                                __builtin_bit_cast(bf16x8, xv[d][t]),
+                                                                acc[j][t], 0, 0, 0);
+        issue(d, st + d + DEPTH);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+
+    __syncthreads();  // the previous segment's reads of red are done
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int t = 0; t < TB; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[wave][j * TB + t][lane][r] = acc[j][t][r];
+    __syncthreads();
+
+    // wave t owns token block t: the sum over waves of its NB tiles
+    auto wave_sum = [&](int t, float (&v)[NB][16]) {
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float a = 0.f;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) a += red[w][j * TB + t][lane][r];
+          v[j][r] = a;
+        }
+    };
+    if (k0 == 0 && k1 == KB) {
+      for (int t = wave; t < TB; t += NW) {
+        float v[NB][16];
+        wave_sum(t, v);
+        finish(g, t, v);
+      }
+      continue;
+    }
+
+    // group g is shared with other workgroups
+    float* mine = ep.part + static_cast<size_t>(slot_of(wg, g)) * (NT * 1024);
+    for (int t = wave; t < TB; t += NW) {
+      float v[NB][16];
+      wave_sum(t, v);
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __hip_atomic_store(mine + ((j * TB + t) * 16 + r) * 64 + lane, v[j][r], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the partial has reached the coherent level
+    __syncthreads();
+    const int w_first = owner(static_cast<long long>(g) * KB);
+    const int w_last = owner(static_cast<long long>(g + 1) * KB - 1);
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(ep.cnt + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               static_cast<unsigned>(w_last - w_first);
+    __syncthreads();
+    if (!s_last) continue;
+    for (int t = wave; t < TB; t += NW) {
+      float v[NB][16];
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[j][r] = 0.f;
+      for (int w = w_first; w <= w_last; ++w) {
+        const float* src = ep.part + static_cast<size_t>(slot_of(w, g)) * (NT * 1024);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            v[j][r] += __hip_atomic_load(src + ((j * TB + t) * 16 + r) * 64 + lane, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      }
+      finish(g, t, v);
+    }
+    if (tid == 0) __hip_atomic_store(ep.cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// Paired epilogues (QKV, SwiGLU) stream two blocks per workgroup; the
-// residual GEMMs one, which doubles the workgroups for the narrow N = d.
+constexpr int kNW = 2;  // wavefronts per workgroup
+
+// Grid size: each column group is split into S equal k ranges, S = 256 /
+// groups (at least 1, at most 8, each range at least 8 k steps), so narrow
+// projections still cover every CU; measured on the 7B shapes, splitting the
+// wide ones (>= 192 groups) only adds fixup cost.
+int grid_for(int groups, int KB) {
+  int S = 256 / groups;
+  if (S > 8) S = 8;
+  while (S > 1 && KB / S < 8) --S;
+  if (S < 1) S = 1;
+  return groups * S;
+}
+
 template <int EPI>
-hipError_t launch(const bf16_t* X, const bf16_t* W, int M, int N, int K, const SkinnyArgs& ep,
-                  hipStream_t s) {
+hipError_t launch(const bf16_t* X, const bf16_t* W, int M, int N, int K, SkinnyArgs ep, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (M > kSkinnyMaxTokens || K % 16 || N % 128) return hipErrorInvalidValue;
   constexpr bool paired = EPI == SK_QKV || EPI == SK_SWIGLU;
-  constexpr int NW = 2;
-  if constexpr (paired) {
-    const dim3 grid(N / 64);
-    if (M <= 32)
-      hipLaunchKernelGGL((skinny_kernel<2, 1, NW, 12, EPI>), grid, dim3(NW * 64), 0, s, X, W, M, N, K, ep);
-    else
-      hipLaunchKernelGGL((skinny_kernel<2, 2, NW, 8, EPI>), grid, dim3(NW * 64), 0, s, X, W, M, N, K, ep);
-  } else {
-    const dim3 grid(N / 32);
-    if (M <= 32)
-      hipLaunchKernelGGL((skinny_kernel<1, 1, NW, 16, EPI>), grid, dim3(NW * 64), 0, s, X, W, M, N, K, ep);
-    else
-      hipLaunchKernelGGL((skinny_kernel<1, 2, NW, 12, EPI>), grid, dim3(NW * 64), 0, s, X, W, M, N, K, ep);
-  }
+  constexpr int NB = paired ? 2 : 1;
+  const int groups = N / (32 * NB);
+  const int G = grid_for(groups, K / 16);
+  if (G != groups && G > kSkinnyGrid) return hipErrorInvalidValue;  // split groups need 2 G partial slots
+  if (M <= 32)
+    hipLaunchKernelGGL((skinny_kernel<NB, 1, kNW, paired ? 12 : 16, EPI>), dim3(G), dim3(kNW * 64), 0, s, X, W, M,
+                       N, K, G, ep);
+  else
+    hipLaunchKernelGGL((skinny_kernel<NB, 2, kNW, paired ? 8 : 12, EPI>), dim3(G), dim3(kNW * 64), 0, s, X, W, M,
+                       N, K, G, ep);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_skinny_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,
-                             const QkvEpilogue& q, hipStream_t s) {
+size_t skinny_scratch_floats() { return static_cast<size_t>(2) * kSkinnyGrid * 4 * 1024; }
+
+hipError_t launch_skinny_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, const QkvEpilogue& q,
+                             const SkinnyScratch& sc, hipStream_t s) {
   SkinnyArgs ep{};
   ep.qkv = q;
+  ep.part = sc.part;
+  ep.cnt = sc.cnt;
   return launch<SK_QKV>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_skinny_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
-                                      const bf16_t* resid, float* out, hipStream_t s) {
+                                      const bf16_t* resid, float* out, const SkinnyScratch& sc, hipStream_t s) {
   SkinnyArgs ep{};
   ep.resid = resid;
   ep.out = out;
+  ep.part = sc.part;
+  ep.cnt = sc.cnt;
   return launch<SK_RESID32>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_skinny_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
-                                       const float* resid, bf16_t* out, hipStream_t s) {
+                                       const float* resid, bf16_t* out, const SkinnyScratch& sc, hipStream_t s) {
   SkinnyArgs ep{};
   ep.resid = resid;
   ep.out = out;
+  ep.part = sc.part;
+  ep.cnt = sc.cnt;
   return launch<SK_RESID16>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_skinny_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int f, int K, bf16_t* out,
-                                hipStream_t s) {
+                                const SkinnyScratch& sc, hipStream_t s) {
   SkinnyArgs ep{};
   ep.out = out;
+  ep.part = sc.part;
+  ep.cnt = sc.cnt;
   return launch<SK_SWIGLU>(A, Wgu, M, 2 * f, K, ep, s);
 }
 
