@@ -13,6 +13,7 @@ typedef uint16_t bf16_t;  // bf16 bit pattern as stored in memory
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
 

@@ -75,8 +75,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   constexpr int BM = 256;
   constexpr int FM = 4, FN = BN / 64;          // wave tile 128 x (BN/2)
   constexpr int STAGE = BM * 128;               // bytes per LDS stage (256 rows x 64 k)
-  __shared__ __attribute__((aligned(1024))) unsigned char As0[STAGE];
-  __shared__ __attribute__((aligned(1024))) unsigned char As1[STAGE];
+  constexpr int TN = BN / 2;                    // wave tile width
+  // epilogue: a wave's 32-row block in fp32, rows TN + 8 floats apart, so
+  // rows r and r + 4 (the two halves of a wavefront store) start 32 banks apart
+  constexpr int TNP = TN + 8;
+  constexpr int EPI_WAVE = 32 * TNP * 4;
+  constexpr int LDS_STAGE = STAGE > 2 * EPI_WAVE ? STAGE : 2 * EPI_WAVE;
+  __shared__ __attribute__((aligned(1024))) unsigned char As0[LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char As1[LDS_STAGE];
   auto stage_base = [&](int st) -> unsigned char* { return st == 0 ? As0 : As1; };
   int m0, n0;
   tile_coords(M, N, BM, BN, m0, n0);
@@ -182,83 +188,99 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   __builtin_amdgcn_s_waitcnt(0);
 
   // ---------------------------------------------------------------- epilogue
-  constexpr int TM = 128, TN = BN / 2;
-  const int row_base = m0 + wm * TM + 4 * (lane >> 5);
-  const int col0 = n0 + wn * TN;
-  const int lc = lane & 31;
+  // Each wave moves its tile through LDS one 32-row block at a time, so the
+  // elementwise work and the global traffic run on row-contiguous data:
+  // 8 consecutive columns per task, 16/32-byte loads and stores.
+  __syncthreads();  // every wave is done with the A stages
+  float* ebuf = reinterpret_cast<float*>((wave < 2 ? As0 : As1) + (wave & 1) * EPI_WAVE);
+  const int lc = lane & 31, hr = 4 * (lane >> 5);
+  const int col0 = n0 + wn * TN;  // first column of this wave's tile
   if (col0 >= N) return;
-  if constexpr (EPI == EPI_QKV) {
-    static_assert(TN == 128, "QKV epilogue needs one 128-wide head per wave");
-    const QkvEpilogue& q = ep.qkv;
-    const int head = col0 >> 7;
-    const int kind = head < q.n_heads ? 0 : (head < q.n_heads + q.n_kv_heads ? 1 : 2);
-    const int hh = kind == 0 ? head : (kind == 1 ? head - q.n_heads : head - q.n_heads - q.n_kv_heads);
+  auto ld8 = [&](int R, int c) {  // 8 fp32 of row R from column c
+    const float4 a = *reinterpret_cast<const float4*>(ebuf + R * TNP + c);
+    const float4 b = *reinterpret_cast<const float4*>(ebuf + R * TNP + c + 4);
+    return f32x8{a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  };
+  auto bf8 = [](const f32x8& v) {
+    return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                      pack_bf16x2(v[6], v[7]));
+  };
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    // registers -> LDS: acc[i][j][r] is row 8 (r/4) + hr + r%4, column 32 j + lc
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ebuf[(8 * (r >> 2) + hr + (r & 3)) * TNP + 32 * j + lc] = acc[i][j][r];
+    // the same wave reads the block back: its LDS accesses complete in order
+    const int row0 = m0 + wm * 128 + i * 32;
+    if constexpr (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
+      static_assert(TN == 128, "QKV / SwiGLU tiles are one 128-wide head / [gate 64 | up 64] block per wave");
+      // task: row R, columns 8c .. 8c + 7 and their partners 64 + 8c ..
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int task = lane + 64 * k, R = task >> 3, c = 8 * (task & 7);
+        const int row = row0 + R;
         if (row >= M) continue;
-        const int p = q.pos[row];
-        const int pt = min(max(p, 0), q.max_pos - 1);
-        float v[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = acc[i][j][r];
-        if (kind != 2) {
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int dd = j * 32 + lc;
-            const float c = q.rope_cos[static_cast<size_t>(pt) * 64 + dd];
-            const float s = q.rope_sin[static_cast<size_t>(pt) * 64 + dd];
-            const float x1 = v[j], x2 = v[j + 2];
-            v[j] = x1 * c - x2 * s;
-            v[j + 2] = x2 * c + x1 * s;
+        f32x8 x1 = ld8(R, c), x2 = ld8(R, c + 64);
+        if constexpr (EPI == EPI_QKV) {
+          const QkvEpilogue& q = ep.qkv;
+          const int head = col0 >> 7;
+          const int kind = head < q.n_heads ? 0 : (head < q.n_heads + q.n_kv_heads ? 1 : 2);
+          const int hh = kind == 0 ? head : (kind == 1 ? head - q.n_heads : head - q.n_heads - q.n_kv_heads);
+          const int p = q.pos[row];
+          if (kind != 2) {
+            const int pt = min(max(p, 0), q.max_pos - 1);
+            const float4* cp = reinterpret_cast<const float4*>(q.rope_cos + static_cast<size_t>(pt) * 64 + c);
+            const float4* sp = reinterpret_cast<const float4*>(q.rope_sin + static_cast<size_t>(pt) * 64 + c);
+            const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+            const f32x8 cs = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+            const f32x8 sn = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+            const f32x8 y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+            x1 = y1;
+            x2 = y2;
           }
-        }
-        bf16_t* dst;
-        if (kind == 0) {
-          dst = q.q + static_cast<size_t>(row) * (q.n_heads * 128) + hh * 128;
+          bf16_t* dst;
+          if (kind == 0) {
+            dst = q.q + static_cast<size_t>(row) * (q.n_heads * 128) + hh * 128;
+          } else {
+            if (p < 0 || p >= q.max_pos) continue;
+            const int b = row / q.T;
+            bf16_t* cache = kind == 1 ? q.k_cache : q.v_cache;
+            dst = cache + (static_cast<size_t>(b * q.n_kv_heads + hh) * q.max_pos + p) * 128;
+          }
+          *reinterpret_cast<uint4*>(dst + c) = bf8(x1);
+          *reinterpret_cast<uint4*>(dst + c + 64) = bf8(x2);
         } else {
-          if (p < 0 || p >= q.max_pos) continue;
-          const int b = row / q.T;
-          bf16_t* cache = kind == 1 ? q.k_cache : q.v_cache;
-          dst = cache + (static_cast<size_t>(b * q.n_kv_heads + hh) * q.max_pos + p) * 128;
-        }
+          f32x8 h;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dst[j * 32 + lc] = f32_to_bf16(v[j]);
-      }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    static_assert(TN == 128, "SwiGLU epilogue needs a [gate 64 | up 64] block per wave");
-    bf16_t* out = static_cast<bf16_t*>(ep.out);
-    const int f = N >> 1;
-    const int hcol0 = (col0 >> 7) * 64;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (row >= M) continue;
-        bf16_t* dst = out + static_cast<size_t>(row) * f + hcol0;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dst[j * 32 + lc] = f32_to_bf16(silu(acc[i][j][r]) * acc[i][j + 2][r]);
-      }
-  } else {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row_base + i * 32 + 8 * (r >> 2) + (r & 3);
-        if (row >= M) continue;
-        const size_t base = static_cast<size_t>(row) * N + col0 + lc;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          if (col0 + j * 32 >= N) break;
-          if constexpr (EPI == EPI_RESID32)
-            static_cast<float*>(ep.out)[base + j * 32] = acc[i][j][r] + bf16_to_f32(static_cast<const bf16_t*>(ep.resid)[base + j * 32]);
-          else
-            static_cast<bf16_t*>(ep.out)[base + j * 32] = f32_to_bf16(acc[i][j][r] + static_cast<const float*>(ep.resid)[base + j * 32]);
+          for (int e = 0; e < 8; ++e) h[e] = silu(x1[e]) * x2[e];
+          const int f = N >> 1;
+          *reinterpret_cast<uint4*>(static_cast<bf16_t*>(ep.out) + static_cast<size_t>(row) * f + (col0 >> 7) * 64 + c) = bf8(h);
         }
       }
+    } else {
+      // task: row R, columns 8c .. 8c + 7
+#pragma unroll
+      for (int k = 0; k < TN / 16; ++k) {
+        const int task = lane + 64 * k, R = task / (TN / 8), c = 8 * (task % (TN / 8));
+        const int row = row0 + R, col = col0 + c;
+        if (row >= M || col >= N) continue;
+        const f32x8 a = ld8(R, c);
+        const size_t at = static_cast<size_t>(row) * N + col;
+        if constexpr (EPI == EPI_RESID32) {
+          const uint4 rb = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(ep.resid) + at);
+          float* o = static_cast<float*>(ep.out) + at;
+          *reinterpret_cast<float4*>(o) = make_float4(a[0] + lo_bf16(rb.x), a[1] + hi_bf16(rb.x), a[2] + lo_bf16(rb.y), a[3] + hi_bf16(rb.y));
+          *reinterpret_cast<float4*>(o + 4) = make_float4(a[4] + lo_bf16(rb.z), a[5] + hi_bf16(rb.z), a[6] + lo_bf16(rb.w), a[7] + hi_bf16(rb.w));
+        } else {
+          const float* rp = static_cast<const float*>(ep.resid) + at;
+          const float4 r0 = *reinterpret_cast<const float4*>(rp), r1 = *reinterpret_cast<const float4*>(rp + 4);
+          const f32x8 rs = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+          *reinterpret_cast<uint4*>(static_cast<bf16_t*>(ep.out) + at) = bf8(a + rs);
+        }
+      }
+    }
   }
 }
 
