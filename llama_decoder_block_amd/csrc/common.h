@@ -90,12 +90,15 @@ hipError_t launch_rmsnorm(const void* in, int in_f32, const void* gain, int gain
 // Row-major bf16 src [rows, K] -> fragment order.  Source row r lands on row
 // (r / group) * group_stride + r % group of the fragment-ordered dst
 // (group = rows for a plain copy); rows and group are multiples of 32 and
-// K % 16 == 0.
+// K % 16 == 0.  group = 0 is the rotary-pair order of projection heads: in
+// every 128-row head, dims x and x + 64 land on rows 2x and 2x + 1.
 hipError_t launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int group,
                             int group_stride, hipStream_t s);
 
 // Tiled bf16 MFMA GEMM, C = A[M,K] . W[N,K]^T with a fused epilogue; A
-// row-major, W in fragment order (K % 128 == 0).
+// row-major, W in fragment order (K % 128 == 0).  The QKV weight is in
+// rotary-pair order (see launch_pack_rows), the gate/up weight interleaved in
+// 64-row blocks; the epilogues write q, the cache and h in the natural order.
 struct QkvEpilogue {
   bf16_t* q;               // [M, H*dh]
   bf16_t* k_cache;         // [B, Hkv, max_pos, dh]
@@ -124,14 +127,16 @@ hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, 
 // written out, whatever they hold).  The SwiGLU output h is written in
 // fragment order, ready to be the A operand of the down projection.
 // Scratch for column groups split between workgroups: part holds
-// skinny_scratch_floats() floats, cnt one counter per column group (N / 32
-// at most), all zero before the first call; each call leaves them zero.
+// skinny_scratch_floats() floats, cnt cnt_len counters (one per column
+// group: N / 32 or N / 64 for the paired SwiGLU), all zero before the first
+// call; each call leaves them zero.
 // Calls that share a scratch must not overlap.
 constexpr int kSkinnyMaxTokens = 64;
 constexpr int kSkinnyGrid = 512;  // workgroups per call, at most
 struct SkinnyScratch {
   float* part;
   unsigned* cnt;
+  int cnt_len;  // counters available
 };
 size_t skinny_scratch_floats();
 hipError_t launch_skinny_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,

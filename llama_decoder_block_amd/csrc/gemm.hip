@@ -2,10 +2,12 @@
 // with the layer's elementwise work fused into the epilogue:
 //   QKV     rotate-half RoPE of q and k at each token's position, bf16 round,
 //           q -> scratch, k and v -> their cache slot (no concatenation pass);
+//           the weight's heads are in rotary-pair order (dims x and x + 64 on
+//           neighbouring rows), so every even-width tile holds whole pairs;
 //   RESID32 X' = x + O Wo^T kept in fp32 (the residual add of the attention half);
 //   SWIGLU  h = SiLU(gate) * up from one GEMM over the gate/up matrix
-//           interleaved in 64-row blocks [gate 64 | up 64], so a lane holds
-//           gate column j and up column j in the same accumulator slot;
+//           interleaved in 64-row blocks [gate 64 | up 64], so a 128-wide wave
+//           tile holds gate column j and up column j;
 //   RESID16 y = bf16(X' + h Wdown^T) (the residual add of the MLP half).
 //
 // Sources: "LMDrive LLM core inference unit" page, §2.3 LlamaAttention (q/k/v
@@ -52,6 +54,10 @@ struct EpiArgs {
 constexpr int BK = 64;
 constexpr int kGroupM = 8;
 constexpr int kResidBN = 128;  // N = d_model is narrow: smaller tiles, more of them
+// QKV: N = 128 (H + 2 Hkv); 192-wide tiles make 64 column tiles at 32 heads
+// (512 tiles at 2048 tokens: two full rounds of 256 CUs, where 256-wide
+// tiles leave the second round half empty)
+constexpr int kQkvBN = 192;
 
 __device__ __forceinline__ void tile_coords(int M, int N, int BM, int BN, int& m0, int& n0) {
   const int nt_m = (M + BM - 1) / BM, nt_n = (N + BN - 1) / BN;
@@ -214,50 +220,56 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
       for (int r = 0; r < 16; ++r) ebuf[(8 * (r >> 2) + hr + (r & 3)) * TNP + 32 * j + lc] = acc[i][j][r];
     // the same wave reads the block back: its LDS accesses complete in order
     const int row0 = m0 + wm * 128 + i * 32;
-    if constexpr (EPI == EPI_QKV || EPI == EPI_SWIGLU) {
-      static_assert(TN == 128, "QKV / SwiGLU tiles are one 128-wide head / [gate 64 | up 64] block per wave");
-      // task: row R, columns 8c .. 8c + 7 and their partners 64 + 8c ..
+    if constexpr (EPI == EPI_QKV) {
+      // rotary-pair order: column 2x of a head is dim x, column 2x + 1 dim
+      // x + 64.  Task: row R, 8 columns = dims x0 .. x0 + 3 and their partners.
+      const QkvEpilogue& q = ep.qkv;
+#pragma unroll
+      for (int k = 0; k < TN / 16; ++k) {
+        const int task = lane + 64 * k, R = task / (TN / 8), c = 8 * (task % (TN / 8));
+        const int row = row0 + R, col = col0 + c;
+        if (row >= M || col >= N) continue;
+        const f32x8 a = ld8(R, c);
+        f32x4 x1 = {a[0], a[2], a[4], a[6]}, x2 = {a[1], a[3], a[5], a[7]};
+        const int head = col >> 7, x0 = (col & 127) >> 1;
+        const int kind = head < q.n_heads ? 0 : (head < q.n_heads + q.n_kv_heads ? 1 : 2);
+        const int hh = kind == 0 ? head : (kind == 1 ? head - q.n_heads : head - q.n_heads - q.n_kv_heads);
+        const int p = q.pos[row];
+        if (kind != 2) {
+          const int pt = min(max(p, 0), q.max_pos - 1);
+          const float4 c4 = *reinterpret_cast<const float4*>(q.rope_cos + static_cast<size_t>(pt) * 64 + x0);
+          const float4 s4 = *reinterpret_cast<const float4*>(q.rope_sin + static_cast<size_t>(pt) * 64 + x0);
+          const f32x4 cs = {c4.x, c4.y, c4.z, c4.w}, sn = {s4.x, s4.y, s4.z, s4.w};
+          const f32x4 y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+          x1 = y1;
+          x2 = y2;
+        }
+        bf16_t* dst;
+        if (kind == 0) {
+          dst = q.q + static_cast<size_t>(row) * (q.n_heads * 128) + hh * 128;
+        } else {
+          if (p < 0 || p >= q.max_pos) continue;
+          const int b = row / q.T;
+          bf16_t* cache = kind == 1 ? q.k_cache : q.v_cache;
+          dst = cache + (static_cast<size_t>(b * q.n_kv_heads + hh) * q.max_pos + p) * 128;
+        }
+        *reinterpret_cast<uint2*>(dst + x0) = make_uint2(pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]));
+        *reinterpret_cast<uint2*>(dst + x0 + 64) = make_uint2(pack_bf16x2(x2[0], x2[1]), pack_bf16x2(x2[2], x2[3]));
+      }
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      static_assert(TN == 128, "SwiGLU tiles are one [gate 64 | up 64] block per wave");
+      // task: row R, gate columns 8c .. 8c + 7 and the up columns 64 later
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const int task = lane + 64 * k, R = task >> 3, c = 8 * (task & 7);
         const int row = row0 + R;
         if (row >= M) continue;
-        f32x8 x1 = ld8(R, c), x2 = ld8(R, c + 64);
-        if constexpr (EPI == EPI_QKV) {
-          const QkvEpilogue& q = ep.qkv;
-          const int head = col0 >> 7;
-          const int kind = head < q.n_heads ? 0 : (head < q.n_heads + q.n_kv_heads ? 1 : 2);
-          const int hh = kind == 0 ? head : (kind == 1 ? head - q.n_heads : head - q.n_heads - q.n_kv_heads);
-          const int p = q.pos[row];
-          if (kind != 2) {
-            const int pt = min(max(p, 0), q.max_pos - 1);
-            const float4* cp = reinterpret_cast<const float4*>(q.rope_cos + static_cast<size_t>(pt) * 64 + c);
-            const float4* sp = reinterpret_cast<const float4*>(q.rope_sin + static_cast<size_t>(pt) * 64 + c);
-            const float4 c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
-            const f32x8 cs = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-            const f32x8 sn = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
-            const f32x8 y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
-            x1 = y1;
-            x2 = y2;
-          }
-          bf16_t* dst;
-          if (kind == 0) {
-            dst = q.q + static_cast<size_t>(row) * (q.n_heads * 128) + hh * 128;
-          } else {
-            if (p < 0 || p >= q.max_pos) continue;
-            const int b = row / q.T;
-            bf16_t* cache = kind == 1 ? q.k_cache : q.v_cache;
-            dst = cache + (static_cast<size_t>(b * q.n_kv_heads + hh) * q.max_pos + p) * 128;
-          }
-          *reinterpret_cast<uint4*>(dst + c) = bf8(x1);
-          *reinterpret_cast<uint4*>(dst + c + 64) = bf8(x2);
-        } else {
-          f32x8 h;
+        const f32x8 x1 = ld8(R, c), x2 = ld8(R, c + 64);
+        f32x8 h;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) h[e] = silu(x1[e]) * x2[e];
-          const int f = N >> 1;
-          *reinterpret_cast<uint4*>(static_cast<bf16_t*>(ep.out) + static_cast<size_t>(row) * f + (col0 >> 7) * 64 + c) = bf8(h);
-        }
+        for (int e = 0; e < 8; ++e) h[e] = silu(x1[e]) * x2[e];
+        const int f = N >> 1;
+        *reinterpret_cast<uint4*>(static_cast<bf16_t*>(ep.out) + static_cast<size_t>(row) * f + (col0 >> 7) * 64 + c) = bf8(h);
       }
     } else {
       // task: row R, columns 8c .. 8c + 7
@@ -293,7 +305,7 @@ hipError_t launch_tiled(const bf16_t* A, const bf16_t* Wp, int M, int N, int K, 
 }  // namespace
 
 hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, const QkvEpilogue& q, hipStream_t s) {
-  EpiArgs ep{}; ep.qkv = q; return launch_tiled<256, EPI_QKV>(A, W, M, N, K, ep, s);
+  EpiArgs ep{}; ep.qkv = q; return launch_tiled<kQkvBN, EPI_QKV>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_gemm_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K, const bf16_t* resid, float* out, hipStream_t s) {
   EpiArgs ep{}; ep.resid = resid; ep.out = out; return launch_tiled<kResidBN, EPI_RESID32>(A, W, M, N, K, ep, s);

@@ -246,8 +246,11 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
     const int pf = part_floats(*cfg, &L->part_seqs);
     ALLOC_OR_FAIL(L->part, static_cast<size_t>(pf) * sizeof(float));
     ALLOC_OR_FAIL(L->sk.part, skinny_scratch_floats() * sizeof(float));
-    const size_t groups = std::max({(nq + 2 * nkv) / 64, 2 * f / 64, d / 32});
+    // one counter per column group: 32-row blocks (QKV, o_proj, down) or
+    // pairs of them (gate/up)
+    const size_t groups = std::max({(nq + 2 * nkv) / 32, 2 * f / 64, d / 32});
     ALLOC_OR_FAIL(L->sk.cnt, groups * sizeof(unsigned));
+    L->sk.cnt_len = static_cast<int>(groups);
     HIP_OR_FAIL(hipMemsetAsync(L->sk.cnt, 0, groups * sizeof(unsigned), s), "clear counters");
   } else {
     ALLOC_OR_FAIL(L->q, mt * (nq + 2 * nkv) * es);
@@ -260,15 +263,16 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
   if (cfg->dtype == LLAMA_BF16) {
     // fragment order; rows of a 32-row-aligned range sit where they would in
     // row-major order, so q, k and v rows are converted straight into their
-    // place in the concatenated matrix
+    // place in the concatenated matrix (each head in rotary-pair order, so
+    // that a rotation's two inputs are neighbouring output columns)
     const int di = static_cast<int>(d), fi = static_cast<int>(f), nqi = static_cast<int>(nq),
               nkvi = static_cast<int>(nkv);
     auto* wqkv = static_cast<bf16_t*>(L->wqkv);
     auto* wgu = static_cast<bf16_t*>(L->wgu);
     auto src = [](const void* p) { return static_cast<const bf16_t*>(p); };
-    HIP_OR_FAIL(launch_pack_rows(src(w->wq), nqi, di, wqkv, nqi, nqi, s), "convert wq");
-    HIP_OR_FAIL(launch_pack_rows(src(w->wk), nkvi, di, wqkv + nq * d, nkvi, nkvi, s), "convert wk");
-    HIP_OR_FAIL(launch_pack_rows(src(w->wv), nkvi, di, wqkv + (nq + nkv) * d, nkvi, nkvi, s), "convert wv");
+    HIP_OR_FAIL(launch_pack_rows(src(w->wq), nqi, di, wqkv, 0, 0, s), "convert wq");
+    HIP_OR_FAIL(launch_pack_rows(src(w->wk), nkvi, di, wqkv + nq * d, 0, 0, s), "convert wk");
+    HIP_OR_FAIL(launch_pack_rows(src(w->wv), nkvi, di, wqkv + (nq + nkv) * d, 0, 0, s), "convert wv");
     HIP_OR_FAIL(launch_pack_rows(src(w->wo), di, nqi, static_cast<bf16_t*>(L->wo), di, di, s), "convert wo");
     HIP_OR_FAIL(launch_pack_rows(src(w->w_down), di, fi, static_cast<bf16_t*>(L->wd), di, di, s), "convert w_down");
     // 64-row blocks: rows [128 j, 128 j + 64) = gate rows [64 j, 64 j + 64),

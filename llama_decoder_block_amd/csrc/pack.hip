@@ -13,7 +13,13 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const uint4* __restrict_
   const int kv = K >> 3;
   if (i >= static_cast<size_t>(rows) * kv) return;
   const int r = static_cast<int>(i / kv), k = static_cast<int>(i % kv) * 8;
-  const int dr = (r / group) * group_stride + r % group;
+  int dr;
+  if (group == 0) {  // heads of 128 rows, dims x and x + 64 to rows 2x and 2x + 1
+    const int d = r & 127;
+    dr = (r & ~127) + (d < 64 ? 2 * d : 2 * (d - 64) + 1);
+  } else {
+    dr = (r / group) * group_stride + r % group;
+  }
   *reinterpret_cast<uint4*>(dst + frag_index(dr, k, K)) = src[i];
 }
 
@@ -22,7 +28,7 @@ __global__ __launch_bounds__(256) void pack_rows_kernel(const uint4* __restrict_
 hipError_t launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int group, int group_stride,
                             hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  if (rows % 32 || group % 32 || K % 16 || group <= 0) return hipErrorInvalidValue;
+  if (rows % 32 || group % 32 || K % 16 || group < 0 || (group == 0 && rows % 128)) return hipErrorInvalidValue;
   const size_t n = static_cast<size_t>(rows) * (K / 8);
   hipLaunchKernelGGL(pack_rows_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s,
                      reinterpret_cast<const uint4*>(src), rows, K, dst, group, group_stride);

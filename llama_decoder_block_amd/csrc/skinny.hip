@@ -27,11 +27,11 @@
 // counter.  Each weight byte is read exactly once; the activations (<= 64 x
 // K bf16) are re-read by every workgroup from L2.
 //
-// Pairing: with NB = 2 the blocks are nb and nb + 2, so one lane holds
-// feature i and feature i + 64 of the same 128-row group for the same token
-// in the same accumulator slot — the RoPE partners of one head (dims i and
-// i + dh/2) and, over the [gate 64 | up 64] interleaved gate/up matrix, gate
-// column j and up column j.
+// Pairing: the QKV weight's heads are in rotary-pair order (dims x and x + 64
+// on rows 2x and 2x + 1), so a rotation's two inputs are neighbouring
+// accumulator slots of one lane.  For SwiGLU, NB = 2 with blocks nb and
+// nb + 2 of the [gate 64 | up 64] interleaved gate/up matrix puts gate
+// column j and up column j in the same slot of the two blocks.
 #include "common.h"
 
 namespace llama {
@@ -45,6 +45,7 @@ struct SkinnyArgs {
   void* out;
   float* part;     // 2 G partial slots of NB * TB * 1024 floats
   unsigned* cnt;   // per column group, zero between launches
+  int cnt_len;
 };
 
 template <int NB, int TB, int NW, int DEPTH, int EPI>
@@ -83,23 +84,22 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
     for (int r4 = 0; r4 < 4; ++r4) {
       const int fib = 8 * r4 + 4 * (lane >> 5);  // first of the 4 features in the block
       if constexpr (EPI == SK_QKV) {
-        static_assert(NB == 2, "RoPE needs the partner block");
+        // rotary-pair order: feature 2x of a head is dim x, 2x + 1 dim x + 64;
+        // the 4 features are dims x0, x0 + 64, x0 + 1, x0 + 65
         const QkvEpilogue& q = ep.qkv;
         const int head = nb0 >> 2;
-        const int i = (nb0 & 3) * 32 + fib;  // dim in the head, < 64; partner i + 64
+        const int x0 = ((nb0 & 3) * 32 + fib) >> 1;
         const int kind = head < q.n_heads ? 0 : (head < q.n_heads + q.n_kv_heads ? 1 : 2);
         const int hh = kind == 0 ? head : (kind == 1 ? head - q.n_heads : head - q.n_heads - q.n_kv_heads);
         const int p = q.pos[tok];
         const int pt = min(max(p, 0), q.max_pos - 1);
-        float lo[4], hi[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { lo[e] = v[0][4 * r4 + e]; hi[e] = v[1][4 * r4 + e]; }
+        float lo[2] = {v[0][4 * r4], v[0][4 * r4 + 2]}, hi[2] = {v[0][4 * r4 + 1], v[0][4 * r4 + 3]};
         if (kind != 2) {
-          const float4 c = *reinterpret_cast<const float4*>(q.rope_cos + static_cast<size_t>(pt) * 64 + i);
-          const float4 s = *reinterpret_cast<const float4*>(q.rope_sin + static_cast<size_t>(pt) * 64 + i);
-          const float cc[4] = {c.x, c.y, c.z, c.w}, ss[4] = {s.x, s.y, s.z, s.w};
+          const float2 c = *reinterpret_cast<const float2*>(q.rope_cos + static_cast<size_t>(pt) * 64 + x0);
+          const float2 s = *reinterpret_cast<const float2*>(q.rope_sin + static_cast<size_t>(pt) * 64 + x0);
+          const float cc[2] = {c.x, c.y}, ss[2] = {s.x, s.y};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
+          for (int e = 0; e < 2; ++e) {
             const float x1 = lo[e], x2 = hi[e];
             lo[e] = x1 * cc[e] - x2 * ss[e];
             hi[e] = x2 * cc[e] + x1 * ss[e];
@@ -114,8 +114,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
           bf16_t* cache = kind == 1 ? q.k_cache : q.v_cache;
           dst = cache + (static_cast<size_t>(b * q.n_kv_heads + hh) * q.max_pos + p) * 128;
         }
-        *reinterpret_cast<uint2*>(dst + i) = make_uint2(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]));
-        *reinterpret_cast<uint2*>(dst + i + 64) = make_uint2(pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3]));
+        *reinterpret_cast<uint32_t*>(dst + x0) = pack_bf16x2(lo[0], lo[1]);
+        *reinterpret_cast<uint32_t*>(dst + x0 + 64) = pack_bf16x2(hi[0], hi[1]);
       } else if constexpr (EPI == SK_SWIGLU) {
         static_assert(NB == 2, "SwiGLU needs the up block");
         const int f = N >> 1;
@@ -294,11 +294,12 @@ template <int EPI>
 hipError_t launch(const bf16_t* X, const bf16_t* W, int M, int N, int K, SkinnyArgs ep, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   if (M > kSkinnyMaxTokens || K % 16 || N % 128) return hipErrorInvalidValue;
-  constexpr bool paired = EPI == SK_QKV || EPI == SK_SWIGLU;
+  constexpr bool paired = EPI == SK_SWIGLU;
   constexpr int NB = paired ? 2 : 1;
   const int groups = N / (32 * NB);
   const int G = grid_for(groups, K / 16);
-  if (G != groups && G > kSkinnyGrid) return hipErrorInvalidValue;  // split groups need 2 G partial slots
+  // split groups need 2 G partial slots and a counter each
+  if (G != groups && (G > kSkinnyGrid || groups > ep.cnt_len)) return hipErrorInvalidValue;
   if (M <= 32)
     hipLaunchKernelGGL((skinny_kernel<NB, 1, kNW, paired ? 12 : 16, EPI>), dim3(G), dim3(kNW * 64), 0, s, X, W, M,
                        N, K, G, ep);
@@ -318,6 +319,7 @@ hipError_t launch_skinny_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int
   ep.qkv = q;
   ep.part = sc.part;
   ep.cnt = sc.cnt;
+  ep.cnt_len = sc.cnt_len;
   return launch<SK_QKV>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_skinny_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
@@ -327,6 +329,7 @@ hipError_t launch_skinny_resid_f32out(const bf16_t* A, const bf16_t* W, int M, i
   ep.out = out;
   ep.part = sc.part;
   ep.cnt = sc.cnt;
+  ep.cnt_len = sc.cnt_len;
   return launch<SK_RESID32>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_skinny_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
@@ -336,6 +339,7 @@ hipError_t launch_skinny_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, 
   ep.out = out;
   ep.part = sc.part;
   ep.cnt = sc.cnt;
+  ep.cnt_len = sc.cnt_len;
   return launch<SK_RESID16>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_skinny_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int f, int K, bf16_t* out,
@@ -344,6 +348,7 @@ hipError_t launch_skinny_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int f
   ep.out = out;
   ep.part = sc.part;
   ep.cnt = sc.cnt;
+  ep.cnt_len = sc.cnt_len;
   return launch<SK_SWIGLU>(A, Wgu, M, 2 * f, K, ep, s);
 }
 
