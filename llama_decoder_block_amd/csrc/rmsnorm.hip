@@ -54,13 +54,21 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const TIn* __restrict_
   if (row >= rows) return;
   const TIn* x = in + static_cast<size_t>(row) * d;
   const int nvec = d >> 3;
-  float v[NV][8];
-  float ss = 0.f;
+  // the row and the gain are fetched together (one memory round trip)
+  float v[NV][8], gv[NV][8];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int vi = lane + j * kWave;
     if (vi < nvec) {
       load8(x + vi * 8, v[j]);
+      load8(g + vi * 8, gv[j]);
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int vi = lane + j * kWave;
+    if (vi < nvec) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
     }
@@ -72,10 +80,8 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const TIn* __restrict_
   for (int j = 0; j < NV; ++j) {
     const int vi = lane + j * kWave;
     if (vi < nvec) {
-      float gv[8];
-      load8(g + vi * 8, gv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) v[j][e] = gv[e] * (v[j][e] * inv);
+      for (int e = 0; e < 8; ++e) v[j][e] = gv[j][e] * (v[j][e] * inv);
       store8(y + (FRAG ? frag_index(row, vi * 8, d) : vi * 8), v[j]);
     }
   }
