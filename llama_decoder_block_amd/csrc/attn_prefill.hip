@@ -21,10 +21,12 @@
 // fed to the MFMA are permuted (bits 2 and 3 of the row index swapped) so that
 // a lane's 16 score registers are two runs of 8 consecutive keys — exactly the
 // B operand of the next MFMA, O^T += V^T P^T, with no register shuffling.  V
-// is transposed to [dd][slot] while it is written to LDS.  The online softmax
-// runs in fp32 (max, sum, rescale); P enters the PV product rounded to bf16.
-// Tiles that lie wholly above a wave's diagonal are skipped, and the -inf
-// mask is applied only on tiles that cross it.
+// is transposed to [dd][slot] while it is written to LDS.  P stays in fp32 in
+// the online softmax and is fed to the PV product as bf16 hi + bf16 lo (two
+// MFMAs), so the product sees P to about 16 bits instead of bf16's 8.
+// Query tiles are launched heaviest first across all heads and sequences (the
+// causal workload grows with the tile index).  Tiles that lie wholly above a wave's diagonal are skipped, and
+// the -inf mask is applied only on tiles that cross it.
 #include "common.h"
 
 #include <math.h>
@@ -51,15 +53,10 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BKV * KSTR];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DH * VSTR];
 
-  // 1-D grid over (query tile, sequence, head).  The causal work of tile qt
-  // grows with qt; the first half of the grid takes the heavy tiles heaviest
-  // first and the second half the light ones lightest first, so the two
-  // workgroups that share a CU (the grid is resident at once at 7B shapes)
-  // carry about the same total.
+  // 1-D grid, heaviest query tiles of every (sequence, head) first
   const int n_qt = (T + BQ - 1) / BQ;
   const int per_qt = H * n_seq;
-  const int slot = static_cast<int>(blockIdx.x) / per_qt, heavy = (n_qt + 1) / 2;
-  const int qt = slot < heavy ? n_qt - 1 - slot : slot - heavy;
+  const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
   const int h = static_cast<int>(blockIdx.x) % per_qt % H, b = static_cast<int>(blockIdx.x) % per_qt / H;
   const int g = h / (H / Hkv);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -173,35 +170,39 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
         }
       }
-      // mask and tile max on the raw scores (the scale is positive). Register
-      // r of block kb is slot j0 + 32 kb + 16 (r/8) + 8 hl + r%8.
+      // scale, mask, tile max. Register r of block kb is slot
+      // j0 + 32 kb + 16 (r/8) + 8 hl + r%8.
       const bool need_mask = j0 + BKV - 1 > wmin;
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
+          float v = sacc[kb][r] * scale_log2;
           if (need_mask) {
             const int j = j0 + 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
-            if (j > pq) sacc[kb][r] = -INFINITY;
+            if (j > pq) v = -INFINITY;
           }
-          mt = fmaxf(mt, sacc[kb][r]);
+          sacc[kb][r] = v;
+          mt = fmaxf(mt, v);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64)) * scale_log2;  // running max in log2 units
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
       const float m_new = fmaxf(m_run, mt);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
       m_run = m_new;
       float lsum = 0.f;
-      uint32_t pk[2][2][4];  // [kb][half][packed pair]: P in bf16
+      uint32_t phi[2][2][4], plo[2][2][4];  // [kb][half][packed pair]
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_use));
-          const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], scale_log2, -m_use));
+          const float p0 = fast_exp2(sacc[kb][r] - m_use);
+          const float p1 = fast_exp2(sacc[kb][r + 1] - m_use);
           lsum += p0 + p1;
-          pk[kb][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0, p1);
+          const uint32_t hp = pack_bf16x2(p0, p1);
+          phi[kb][r >> 3][(r & 7) >> 1] = hp;
+          plo[kb][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0 - lo_bf16(hp), p1 - hi_bf16(hp));
         }
       l_run = l_run * alpha + lsum;
 #pragma unroll
@@ -213,12 +214,14 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const bf16x8 bp = as_bf16x8(make_uint4(pk[kb][half][0], pk[kb][half][1], pk[kb][half][2], pk[kb][half][3]));
+          const bf16x8 bh = as_bf16x8(make_uint4(phi[kb][half][0], phi[kb][half][1], phi[kb][half][2], phi[kb][half][3]));
+          const bf16x8 bl = as_bf16x8(make_uint4(plo[kb][half][0], plo[kb][half][1], plo[kb][half][2], plo[kb][half][3]));
           const int kcol = (kb * 2 + half) * 16;
 #pragma unroll
           for (int fd = 0; fd < 4; ++fd) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[st][v_row0 + fd * 32 * VSTR + kcol]);
-            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bp, oacc[fd], 0, 0, 0);
+            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, oacc[fd], 0, 0, 0);
+            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, oacc[fd], 0, 0, 0);
           }
         }
     }

@@ -48,10 +48,19 @@ def rel_err(got, ref) -> float:
 
 
 def assert_bf16_output(got, ref, what=""):
+    """The bf16 gate: every element within 0.02 x RMS(ref) of the unrounded
+    oracle value, beyond the half bf16 ulp that rounding the output itself
+    must cost.  A correctly rounded exact result is off by up to half an ulp
+    of |ref|, which alone reaches 0.0165 x RMS on the 70B-shape sample (max|y|
+    of 40 at RMS 7.6), so the gate bounds the compute error on top of that."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
     e = rel_err(got, ref)
-    print(f"  {what}: max|err|/rms = {e:.5f} (gate {BF16_RMS_GATE})", flush=True)
+    r = max(rms(ref), 1e-30)
+    beyond = float(np.max(np.maximum(np.abs(got - ref) - bf16_ulp(ref) / 2, 0.0)) / r)
+    print(f"  {what}: max|err|/rms = {e:.5f}; beyond the output's half ulp {beyond:.5f} (gate {BF16_RMS_GATE})",
+          flush=True)
     assert np.all(np.isfinite(got)), what
-    assert e <= BF16_RMS_GATE, f"{what}: {e}"
+    assert beyond <= BF16_RMS_GATE, f"{what}: {beyond} beyond half an ulp ({e} in all)"
 
 
 def bf16_ulp(a):
