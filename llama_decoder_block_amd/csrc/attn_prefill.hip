@@ -13,8 +13,12 @@
 // (= position) with the query's position, which equals the notes' index mask
 // when positions are 0..T-1 and extends it to a prefill that continues a cache.
 //
-// gfx950 design.  One workgroup = 4 wavefronts = 128 queries of one head;
-// each wave owns 32 queries.  K/V tiles of 64 slots are staged in LDS (two
+// gfx950 design.  One workgroup = 128 queries of one head; each of its 4
+// query wavefronts owns 32 queries.  When the whole grid fits in one round of
+// two workgroups per CU, the causal work is dominated by the longest query
+// tile's serial chain, so a second group of 4 wavefronts takes every other
+// K/V tile and the two running states (max, sum, O) are merged through LDS at
+// the end.  K/V tiles of 64 slots are staged in LDS (two
 // stages, register prefetch of the next tile).  Scores are computed
 // transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so each lane owns
 // one query: its row max / row sum need only a lane-pair exchange.  The K rows
@@ -31,6 +35,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace llama {
 namespace {
 
@@ -46,12 +52,17 @@ __device__ __forceinline__ int kappa(int m) {  // swap bits 2 and 3
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-__global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
+// NGRP wave groups of 4 share the query tile and take every NGRP-th K/V tile
+// (NGRP = 2 halves the longest serial chain when the grid is a single round
+// of workgroups; with several rounds, two independent workgroups per CU
+// overlap better)
+template <int NGRP>
+__global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ pos, bf16_t* __restrict__ o,
     int o_frag, int n_seq, int T, int H, int Hkv, int max_pos, float scale_log2) {
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[2][BKV * KSTR];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[2][DH * VSTR];
+  __shared__ __attribute__((aligned(16))) bf16_t Ks[NGRP][2][BKV * KSTR];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[NGRP][2][DH * VSTR];
 
   // 1-D grid, heaviest query tiles of every (sequence, head) first
   const int n_qt = (T + BQ - 1) / BQ;
@@ -59,7 +70,12 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   const int qt = n_qt - 1 - static_cast<int>(blockIdx.x) / per_qt;
   const int h = static_cast<int>(blockIdx.x) % per_qt % H, b = static_cast<int>(blockIdx.x) % per_qt / H;
   const int g = h / (H / Hkv);
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // group grp takes tiles grp, grp + NGRP, ...; wave w of either group owns
+  // queries 32 w .. 32 w + 31 of the tile
+  // (group and wave as scalars, so that what derives from them stays uniform)
+  const int grp = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 8);
+  const int tid = threadIdx.x & 255, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, lq = lane & 31;
 
   // ---- this lane's query
@@ -77,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     wmin = min(wmin, __shfl_xor(wmin, s, 64));
   }
   __shared__ int s_max[4];
-  if (lane == 0) s_max[wave] = wmax;
+  if (lane == 0 && grp == 0) s_max[wave] = wmax;
   __syncthreads();
   const int gmax = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
   if (gmax < 0) return;  // no valid query in the whole tile (uniform)
@@ -95,8 +111,9 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     }
   }
 
-  // ---- K / V tile staging (buffer loads over this (b, g) cache slice).
-  // Waves 0-1 stage V, waves 2-3 stage K, 8 loads of 16 bytes per thread each.
+  // ---- K / V tile staging (buffer loads over this (b, g) cache slice), each
+  // group for its own tiles.  Waves 0-1 of a group stage V, waves 2-3 stage K,
+  // 8 loads of 16 bytes per thread each.
   // V: thread (kg, dg) loads slots 8 kg .. 8 kg + 7 at dims 8 dg .. 8 dg + 7 and
   // writes them transposed as 8 rows (dims) of 8 slots, 16 bytes per row; with
   // the 144-byte row stride a 16-lane group (8 slot groups x 2 dim groups) hits
@@ -110,7 +127,7 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
   const int kr = st_t >> 4, kc = st_t & 15;        // K: row (of 8 per pass), 16-byte chunk
   uint4 sreg[8];
   auto gload = [&](int j0) {
-    const uint32_t so = static_cast<uint32_t>(j0) * DH * 2u;
+    const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j0) * DH * 2u);  // tile offset, uniform
     if (stage_v) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) sreg[i] = buf_load16(v_rs, ((8 * vkg + i) * DH + vdg * 8) * 2u, so);
@@ -130,11 +147,11 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
         o.y = __builtin_amdgcn_perm(w[4 * 3 + (d >> 1)], w[4 * 2 + (d >> 1)], sel);
         o.z = __builtin_amdgcn_perm(w[4 * 5 + (d >> 1)], w[4 * 4 + (d >> 1)], sel);
         o.w = __builtin_amdgcn_perm(w[4 * 7 + (d >> 1)], w[4 * 6 + (d >> 1)], sel);
-        *reinterpret_cast<uint4*>(&Vt[st][(vdg * 8 + d) * VSTR + 8 * vkg]) = o;
+        *reinterpret_cast<uint4*>(&Vt[grp][st][(vdg * 8 + d) * VSTR + 8 * vkg]) = o;
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&Ks[st][(kr + 8 * i) * KSTR + kc * 8]) = sreg[i];
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&Ks[grp][st][(kr + 8 * i) * KSTR + kc * 8]) = sreg[i];
     }
   };
 
@@ -145,20 +162,26 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  gload(0);
-  lstore(0);
+  if (grp < ntiles) {
+    gload(grp * BKV);
+    lstore(0);
+  }
   __syncthreads();
 
   const int k_row0 = kappa(lq) * KSTR + hl * 8;
   const int v_row0 = lq * VSTR + hl * 8;
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int st = it & 1;
+  // the trip count is the same for both groups (they share the barrier)
+  for (int i = 0; i * NGRP < ntiles; ++i) {
+    const int it = i * NGRP + grp;
+    const int st = i & 1;
     const int j0 = it * BKV;
-    if (it + 1 < ntiles) gload(j0 + BKV);
+    if (it + NGRP < ntiles) gload(j0 + NGRP * BKV);
 
-    if (j0 <= wmax) {  // wave-uniform: skip tiles wholly above this wave's diagonal
-      // S^T for 2 blocks of 32 slots
+    // one 64-slot tile; MASK: the tile crosses the diagonal of some query of this wave
+    auto tile = [&](auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      // S^T for 2 blocks of 32 slots (unscaled scores)
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -166,28 +189,26 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[st][k_row0 + kb * 32 * KSTR + s * 16]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[grp][st][k_row0 + kb * 32 * KSTR + s * 16]);
           sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc[kb], 0, 0, 0);
         }
       }
-      // scale, mask, tile max. Register r of block kb is slot
+      // mask and tile max.  Register r of block kb is slot
       // j0 + 32 kb + 16 (r/8) + 8 hl + r%8.
-      const bool need_mask = j0 + BKV - 1 > wmin;
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float v = sacc[kb][r] * scale_log2;
-          if (need_mask) {
+          if constexpr (MASK) {
             const int j = j0 + 32 * kb + 16 * (r >> 3) + 8 * hl + (r & 7);
-            if (j > pq) v = -INFINITY;
+            if (j > pq) sacc[kb][r] = -INFINITY;
           }
-          sacc[kb][r] = v;
-          mt = fmaxf(mt, v);
+          mt = fmaxf(mt, sacc[kb][r]);
         }
       mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      const float m_new = fmaxf(m_run, mt);
+      // running max in log2 units; the scale is positive, so max and scaling commute
+      const float m_new = fmaxf(m_run, mt * scale_log2);
       const float m_use = m_new == -INFINITY ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
       m_run = m_new;
@@ -197,18 +218,21 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(sacc[kb][r] - m_use);
-          const float p1 = fast_exp2(sacc[kb][r + 1] - m_use);
+          const float p0 = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_use));
+          const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], scale_log2, -m_use));
           lsum += p0 + p1;
           const uint32_t hp = pack_bf16x2(p0, p1);
           phi[kb][r >> 3][(r & 7) >> 1] = hp;
           plo[kb][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0 - lo_bf16(hp), p1 - hi_bf16(hp));
         }
       l_run = l_run * alpha + lsum;
+      // once the running max settles alpha is 1 for the whole wave
+      if (!__all(alpha == 1.f)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+      }
       // O^T += V^T P^T over 4 blocks of 16 slots
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -219,15 +243,49 @@ __global__ __launch_bounds__(256, 2) void attn_prefill_kernel(
           const int kcol = (kb * 2 + half) * 16;
 #pragma unroll
           for (int fd = 0; fd < 4; ++fd) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[st][v_row0 + fd * 32 * VSTR + kcol]);
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[grp][st][v_row0 + fd * 32 * VSTR + kcol]);
             oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, oacc[fd], 0, 0, 0);
             oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, oacc[fd], 0, 0, 0);
           }
         }
+    };
+    if (it < ntiles && j0 <= wmax) {  // wave-uniform: skip tiles wholly above this wave's diagonal
+      if (j0 + BKV - 1 > wmin)
+        tile(std::true_type{});
+      else
+        tile(std::false_type{});
     }
-    if (it + 1 < ntiles) lstore(st ^ 1);
+    if (it + NGRP < ntiles) lstore(st ^ 1);
     __syncthreads();
   }
+
+  // ---- merge group 1's running state (max, sum, O) into group 0's.  The K
+  // stages are free after the loop's last barrier.
+  if constexpr (NGRP == 2) {
+    static_assert(sizeof(Ks) >= 4 * 66 * 64 * sizeof(float), "merge buffer");
+    float* mb = reinterpret_cast<float*>(&Ks[0][0][0]) + wave * 66 * 64 + lane;  // [wave][66][lane]
+    if (grp == 1) {
+      mb[0] = m_run;
+      mb[64] = l_run;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mb[(2 + 16 * i + r) * 64] = oacc[i][r];
+    }
+    __syncthreads();
+    if (grp == 1) return;
+    {
+      const float m1 = mb[0], l1 = mb[64];
+      const float m = fmaxf(m_run, m1);
+      const float mu = m == -INFINITY ? 0.f : m;
+      const float a0 = fast_exp2(m_run - mu), a1 = fast_exp2(m1 - mu);
+      l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[i][r] = oacc[i][r] * a0 + mb[(2 + 16 * i + r) * 64] * a1;
+    }
+    }
 
   // ---- normalise and store: oacc[fd] register r is dim fd*32 + 8(r/4) + 4 hl + r%4
   if (!valid) return;
@@ -254,10 +312,18 @@ hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf1
                                const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
                                int n_kv_heads, int max_pos, hipStream_t s) {
   if (o_frag && B * T > kSkinnyMaxTokens) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>((T + BQ - 1) / BQ) * n_heads * B);
+  const int n_wg = (T + BQ - 1) / BQ * n_heads * B;
+  const dim3 grid(static_cast<unsigned>(n_wg));
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return hipErrorInvalidDevice;
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
-  hipLaunchKernelGGL(attn_prefill_kernel, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, o, o_frag, B, T,
-                     n_heads, n_kv_heads, max_pos, scale_log2);
+  if (n_wg <= 2 * n_cu)  // one round of two workgroups per CU
+    hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(512), 0, s, q, k_cache, v_cache, pos, o, o_frag, B, T,
+                       n_heads, n_kv_heads, max_pos, scale_log2);
+  else
+    hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, o, o_frag, B, T,
+                       n_heads, n_kv_heads, max_pos, scale_log2);
   return hipGetLastError();
 }
 
