@@ -10,18 +10,19 @@
 // gfx950 design: the cache is streamed once at HBM rate, K and V together.
 //   * workgroup (split s, kv head g, sequence b) takes slots
 //     [s L, (s+1) L) ∩ [0, p]; the split length is chosen so the grid holds
-//     about 1024 workgroups (4 per CU).  With that many (sequence, kv head)
-//     pairs already, there is one split and the workgroup writes the
-//     normalised output itself; otherwise each split writes (max, sum,
-//     unnormalised o[128]) per head and a second kernel merges them (the
-//     standard split-softmax merge);
+//     about 1024 workgroups (4 per CU), or 256 when a workgroup serves 5 or
+//     more query heads (its wavefronts then need more than 256 VGPRs, one
+//     workgroup per CU).  With that many (sequence, kv head) pairs already,
+//     there is one split and the workgroup writes the normalised output
+//     itself; otherwise each split writes (max, sum, unnormalised o[128]) per
+//     head and a second kernel merges them (the standard split-softmax merge);
 //   * a K or V row (128 dims = 256 B) is read by 16 lanes with 16-byte loads,
 //     so a wavefront reads 4 consecutive rows = 1 KB contiguous per load; each
 //     lane keeps 4 K and 4 V loads in flight;
 //   * 16 row groups of 16 lanes each own the slots of one residue mod 16 and
 //     run an online softmax over them (running max and sum in fp32, base-2
 //     exponent with the scale folded into q): per 4 slots, the scores come
-//     from a 16-lane shuffle reduction, the running output (8 dims x heads per
+//     from a 16-lane DPP reduction, the running output (8 dims x heads per
 //     lane) is rescaled once and the 4 weighted V rows are added;
 //   * the 16 row-group states are merged with the same rule (shuffles within a
 //     wave, LDS across the 4 waves).
@@ -34,7 +35,9 @@ namespace {
 
 constexpr int DH = 128;
 constexpr int kMaxRep = 8;  // query heads handled per workgroup
-constexpr int kTargetWGs = 1024;
+// workgroups wanted per call: four per CU (of 256) while a wavefront fits in
+// 256 VGPRs; one per CU once R >= 5 query heads push it past that
+__host__ __device__ constexpr int target_wgs(int R) { return R <= 4 ? 1024 : 256; }
 
 // (m1, l1, a1) <- merge with (m2, l2, a2): both scaled to the larger max
 __device__ __forceinline__ void softmax_merge(float& m1, float& l1, float* a1, float m2, float l2,
@@ -102,14 +105,26 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int e = 0; e < 8; ++e) acc[r][e] = 0.f;
   }
 
-  for (int j = sub; j < n; j += 64) {
-    uint4 ku[4], vu[4];
+  // the 4 K and 4 V rows of this row group's next slots j, j + 16, ...
+  auto fetch = [&](int j, uint4 (&ku)[4], uint4 (&vu)[4]) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bool ok = j + 16 * u < n;
       ku[u] = ok ? *reinterpret_cast<const uint4*>(K + static_cast<size_t>(j + 16 * u) * DH) : make_uint4(0, 0, 0, 0);
       vu[u] = ok ? *reinterpret_cast<const uint4*>(V + static_cast<size_t>(j + 16 * u) * DH) : make_uint4(0, 0, 0, 0);
     }
+  };
+  // with R >= 5 heads a CU holds one workgroup only, so the rows of the next
+  // iteration are fetched before this one's arithmetic (register prefetch)
+  constexpr bool kPrefetch = R >= 5;
+  uint4 ku[4], vu[4];  // this iteration's rows
+  if (kPrefetch) fetch(sub, ku, vu);
+  for (int j = sub; j < n; j += 64) {
+    uint4 kn[4], vn[4];  // the next iteration's rows (prefetch)
+    if (kPrefetch)
+      fetch(j + 64, kn, vn);
+    else
+      fetch(j, ku, vu);
     float sc[R][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -121,10 +136,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) d += qv[r][e] * kf[e];
-        d += __shfl_xor(d, 1, 64);
-        d += __shfl_xor(d, 2, 64);
-        d += __shfl_xor(d, 4, 64);
-        d += __shfl_xor(d, 8, 64);
+        d = sum16_dpp(d);  // the 16 lanes of the row group
         sc[r][u] = j + 16 * u < n ? d : -INFINITY;  // slots past the split are masked
       }
     }
@@ -149,6 +161,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[r][e] += sc[r][u] * vf[e];
+    }
+    if (kPrefetch) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ku[u] = kn[u];
+        vu[u] = vn[u];
+      }
     }
   }
 
@@ -190,34 +209,70 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 }
 
 // Merge the splits: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
-__global__ __launch_bounds__(128) void attn_decode_combine_kernel(const float* __restrict__ part,
-                                                                  bf16_t* __restrict__ o, int o_frag,
-                                                                  int H, int n_split) {
+// One workgroup per (sequence, head); the splits are read in parallel: the
+// 256 threads take the maxima and the weighted sums of the split range in a
+// fixed order (so the result does not depend on timing), then thread pairs
+// (d, half) add the weighted partial outputs of their half of the splits.
+constexpr int kCombineThreads = 256;
+__global__ __launch_bounds__(kCombineThreads) void attn_decode_combine_kernel(const float* __restrict__ part,
+                                                                             bf16_t* __restrict__ o, int o_frag,
+                                                                             int H, int n_split) {
+  __shared__ float red[kCombineThreads];
+  __shared__ float half_sum[DH];
   const int bh = blockIdx.x;  // b * H + h
-  const int d = threadIdx.x;
+  const int t = threadIdx.x;
   const float* pp = part + static_cast<size_t>(bh) * n_split * (DH + 2);
+  // global max over the splits
   float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, pp[s * (DH + 2)]);
-  float num = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float* e = pp + s * (DH + 2);
-      const float w = fast_exp2(e[0] - M);  // exactly 0 for empty splits (m = -inf)
-      den += w * e[1];
-      num += w * e[2 + d];
-    }
+  for (int s = t; s < n_split; s += kCombineThreads) M = fmaxf(M, pp[static_cast<size_t>(s) * (DH + 2)]);
+  red[t] = M;
+  __syncthreads();
+  for (int w = kCombineThreads / 2; w > 0; w >>= 1) {
+    if (t < w) red[t] = fmaxf(red[t], red[t + w]);
+    __syncthreads();
   }
-  const size_t at = o_frag ? frag_index(bh / H, (bh % H) * DH + d, H * DH) : static_cast<size_t>(bh) * DH + d;
-  o[at] = f32_to_bf16(den > 0.f ? num / den : 0.f);
+  M = red[0];
+  __syncthreads();
+  const bool any = M != -INFINITY;
+  // denominator: sum over splits of 2^(m_s - M) l_s (exactly 0 for empty splits)
+  float den = 0.f;
+  if (any)
+    for (int s = t; s < n_split; s += kCombineThreads) {
+      const float* e = pp + static_cast<size_t>(s) * (DH + 2);
+      den += fast_exp2(e[0] - M) * e[1];
+    }
+  red[t] = den;
+  __syncthreads();
+  for (int w = kCombineThreads / 2; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
+  }
+  den = red[0];
+  // numerator for dim d over half hf of the splits
+  const int d = t & (DH - 1), hf = t / DH;
+  float num = 0.f;
+  if (any)
+    for (int s = hf; s < n_split; s += kCombineThreads / DH) {
+      const float* e = pp + static_cast<size_t>(s) * (DH + 2);
+      num += fast_exp2(e[0] - M) * e[2 + d];
+    }
+  if (hf == 1) half_sum[d] = num;
+  __syncthreads();
+  if (hf == 0) {
+    num += half_sum[d];
+    const size_t at = o_frag ? frag_index(bh / H, (bh % H) * DH + d, H * DH) : static_cast<size_t>(bh) * DH + d;
+    o[at] = f32_to_bf16(den > 0.f ? num / den : 0.f);
+  }
 }
 
 // slots per split: one split when the (sequence, kv head, head chunk)
-// workgroups already number kTargetWGs, else enough splits to get there
-int split_len(int max_pos, int B, int Hkv, int chunks) {
+// workgroups already number target_wgs(R), else enough splits to get there
+int split_len(int max_pos, int B, int Hkv, int chunks, int R) {
   const long long wgs = static_cast<long long>(B) * Hkv * chunks;
-  if (wgs >= kTargetWGs) return max_pos;
-  long long L = (static_cast<long long>(max_pos) * wgs + kTargetWGs - 1) / kTargetWGs;
-  L = (L + 63) / 64 * 64;
+  const long long target = target_wgs(R);
+  if (wgs >= target) return max_pos;
+  long long L = (static_cast<long long>(max_pos) * wgs + target - 1) / target;
+  L = (L + 15) / 16 * 16;  // whole row-group steps
   if (L < 64) L = 64;
   if (L > max_pos) L = max_pos;
   return static_cast<int>(L);
@@ -233,7 +288,8 @@ int heads_per_block(int n_rep) {
 
 int decode_attn_splits(int max_pos, int B, int n_heads, int n_kv_heads) {
   const int n_rep = n_heads / n_kv_heads;
-  const int L = split_len(max_pos, B, n_kv_heads, n_rep / heads_per_block(n_rep));
+  const int R = heads_per_block(n_rep);
+  const int L = split_len(max_pos, B, n_kv_heads, n_rep / R, R);
   return (max_pos + L - 1) / L;
 }
 
@@ -243,7 +299,7 @@ hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16
   if (o_frag && B > kSkinnyMaxTokens) return hipErrorInvalidValue;
   const int n_rep = n_heads / n_kv_heads;
   const int R = heads_per_block(n_rep);
-  const int L = split_len(max_pos, B, n_kv_heads, n_rep / R);
+  const int L = split_len(max_pos, B, n_kv_heads, n_rep / R, R);
   if ((max_pos + L - 1) / L != n_split) return hipErrorInvalidValue;
   const dim3 grid(n_split, n_kv_heads * (n_rep / R), B);
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
@@ -260,8 +316,8 @@ hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || n_split == 1) return e;
-  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(B * n_heads), dim3(DH), 0, s, part, o, o_frag, n_heads,
-                     n_split);
+  hipLaunchKernelGGL(attn_decode_combine_kernel, dim3(B * n_heads), dim3(kCombineThreads), 0, s, part, o, o_frag,
+                     n_heads, n_split);
   return hipGetLastError();
 }
 

@@ -75,6 +75,17 @@ __device__ __forceinline__ float warp_sum(float v) {
   return v;
 }
 
+// Sum over each aligned group of 16 lanes, result in every lane of the group,
+// with DPP lane moves (one VALU add each) instead of LDS-routed shuffles:
+// swap neighbours, swap pairs, mirror within 8, mirror within 16.
+__device__ __forceinline__ float sum16_dpp(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));  // row_mirror
+  return v;
+}
+
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
 
 // -------------------------------------------------------------------------
