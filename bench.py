@@ -75,7 +75,12 @@ def traffic_from_profile(kernel_src):
     return prof.get("traffic_bytes_per_launch")
 
 
-def bench_prefill(lib, synth, G, steps, warmup):
+def layer_config(lib, wl, max_tokens):
+    return lib.make_config(wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff, wl.max_pos,
+                           max_tokens, wl.dtype, wl.rms_eps, wl.rope_base)
+
+
+def bench_prefill(lib, synth, steps, warmup):
     import torch
     wl = synth.WORKLOADS["llama7b_prefill"]
     B, T = wl.batch, wl.seq
@@ -84,7 +89,7 @@ def bench_prefill(lib, synth, G, steps, warmup):
     pos = synth.prefill_positions(B, T, device="cuda")
     kc, vc = synth.make_cache(wl, "cuda")
     y = torch.empty_like(x)
-    layer = lib.LlamaLayer(G.layer_config(lib, wl, B * T), w)
+    layer = lib.LlamaLayer(layer_config(lib, wl, B * T), w)
     for _ in range(warmup):
         layer.prefill(x, pos, kc, vc, y=y)
     torch.cuda.synchronize()
@@ -104,7 +109,7 @@ def bench_prefill(lib, synth, G, steps, warmup):
     return wl, (t1 - t0), avg, host
 
 
-def bench_decode(lib, synth, G, steps, warmup):
+def bench_decode(lib, synth, steps, warmup):
     import torch
     wl = synth.WORKLOADS["llama7b_decode"]
     B, p = wl.batch, wl.prior
@@ -113,7 +118,7 @@ def bench_decode(lib, synth, G, steps, warmup):
     pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
     kc, vc = synth.make_cache(wl, "cuda")
     y = torch.empty_like(x)
-    layer = lib.LlamaLayer(G.layer_config(lib, wl, B), w)
+    layer = lib.LlamaLayer(layer_config(lib, wl, B), w)
     # evicts L2 and the Infinity Cache between steps by READING 512 MB: the
     # caches then hold clean lines, as after the other layers of a real decode
     # step (a write-based flush would leave dirty lines whose write-back the
@@ -143,6 +148,67 @@ def bench_decode(lib, synth, G, steps, warmup):
             "hbm_frac": nbytes / med / 1e6 / PEAK_HBM_GBPS, "tokens_per_s": B / med * 1e3,
             "cache_flush_between_steps": "512 MB read",
             "step_ms_by_kernel": {k: v / calls for k, v in step_ms.items()}}
+
+
+def bench_other_configs(lib, synth, steps, warmup):
+    """The other layer shapes, timed the same way (not the headline): 13B-shape
+    prefill (2 x 4096 tokens), 70B-shape GQA prefill (4096 tokens) and the 64
+    single-token decode steps that follow it (positions 4096..4159; caches
+    evicted by a 512 MB read before each step, as for the 7B decode)."""
+    import torch
+    res = {}
+    flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    for name in ("llama13b_prefill", "llama70b_gqa"):
+        wl = synth.WORKLOADS[name]
+        B, T = wl.batch, wl.seq
+        w = synth.make_weights(wl, "cuda")
+        x = synth.make_x(wl, (B, T), device="cuda")
+        pos = synth.prefill_positions(B, T, device="cuda")
+        kc, vc = synth.make_cache(wl, "cuda")
+        y = torch.empty_like(x)
+        layer = lib.LlamaLayer(layer_config(lib, wl, B * T), w)
+        for _ in range(warmup):
+            layer.prefill(x, pos, kc, vc, y=y)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            layer.prefill(x, pos, kc, vc, y=y)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        tfl = prefill_flops(wl, T, B) / (ms * 1e-3) / 1e12
+        res[name.replace("_gqa", "_gqa_prefill")] = {
+            "batch": B, "seq_len": T, "ms_per_step": ms, "tokens_per_s": B * T / ms * 1e3,
+            "tflops": tfl, "mfma_frac": tfl / PEAK_BF16_TFLOPS}
+        log(f"{name}: prefill {ms:.3f} ms/step")
+        layer.close()
+        if wl.decode_steps:
+            # the decode steps continue the cache the prefill just wrote
+            layer = lib.LlamaLayer(layer_config(lib, wl, B), w)
+            xs = [synth.make_x(wl, (B,), tensor_id=100 + s, device="cuda") for s in range(wl.decode_steps)]
+            yd = torch.empty_like(xs[0])
+            times, nbytes = [], 0
+            for s, xd in enumerate(xs):
+                p = T + s
+                pd = torch.full((B,), p, dtype=torch.int32, device="cuda")
+                flush.sum()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                layer.decode(xd, pd, kc, vc, y=yd)
+                e1.record(stream)
+                times.append((e0, e1))
+                nbytes += decode_bytes(wl, B, p)
+            torch.cuda.synchronize()
+            ms_all = [a.elapsed_time(b) for a, b in times]
+            tot = sum(ms_all)
+            med = sorted(ms_all)[len(ms_all) // 2]
+            res[name.replace("_gqa", "_gqa_decode")] = {
+                "batch": B, "positions": [T, T + wl.decode_steps - 1], "steps": wl.decode_steps,
+                "ms_per_step_median": med, "GBps": nbytes / tot / 1e6,
+                "hbm_frac": nbytes / tot / 1e6 / PEAK_HBM_GBPS}
+            log(f"{name}: decode median {med:.3f} ms/step")
+            layer.close()
+    return res
 
 
 def cpu_baseline(wl, host, budget_s):
@@ -193,6 +259,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
+    ap.add_argument("--other-configs", action="store_true",
+                    help="also time the 13B-shape prefill and the 70B-shape GQA prefill + 64 decode steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -215,9 +283,8 @@ def main():
 
     import llama_decoder_block_amd as lib
     import synth
-    from tests import gpu_helpers as G
 
-    wl, elapsed, step_avg, host = bench_prefill(lib, synth, G, args.steps, args.warmup)
+    wl, elapsed, step_avg, host = bench_prefill(lib, synth, args.steps, args.warmup)
     B, T = wl.batch, wl.seq
     ms_per_step = elapsed / args.steps * 1e3
     tokens_per_s = B * T * args.steps / elapsed
@@ -252,7 +319,9 @@ def main():
                   "step_ms_by_kernel": step_avg},
     }
     if not args.no_decode:
-        out["decode"] = bench_decode(lib, synth, G, args.decode_steps, 3)
+        out["decode"] = bench_decode(lib, synth, args.decode_steps, 3)
+    if args.other_configs:
+        out["other_configs"] = bench_other_configs(lib, synth, max(3, args.steps // 4), 2)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_budget_s)
     print(json.dumps(out), flush=True)
