@@ -140,8 +140,11 @@ void llama_layer_destroy(llama_layer* layer);
  *   6 down projection + residual.
  * llama_layer_profile(layer, 1) clears the totals and records a HIP event on
  * the call's stream before each step and after the last one, for every later
- * call; llama_layer_profile(layer, 0) stops recording.  No device memory is
- * allocated (events are created lazily on the first enable).  Errors: NULL, HIP. */
+ * call; llama_layer_profile(layer, 2 + i) clears them and brackets step i
+ * only (two events per call, so the other steps run undisturbed);
+ * llama_layer_profile(layer, 0) stops recording.  No device memory is
+ * allocated (events are created lazily on the first enable).  Errors: NULL,
+ * INVALID (mode outside 0 .. 1 + LLAMA_LAYER_STEPS), HIP. */
 #define LLAMA_LAYER_STEPS 7
 int llama_layer_profile(llama_layer* layer, int enable);
 

@@ -157,8 +157,11 @@ def llama_layer_destroy(handle):
     LIB.llama_layer_destroy(handle)
 
 
-def llama_layer_profile(handle, enable: bool):
-    _check(LIB.llama_layer_profile(handle, 1 if enable else 0))
+def llama_layer_profile(handle, enable: bool, step: int | None = None):
+    """Per-step HIP event timing of later calls: every step, or only `step`
+    (0 .. LLAMA_LAYER_STEPS - 1, two events per call); enable=False stops it."""
+    mode = 0 if not enable else (1 if step is None else 2 + int(step))
+    _check(LIB.llama_layer_profile(handle, mode))
 
 
 def llama_layer_profile_read(handle):

@@ -88,6 +88,7 @@ struct llama_layer {
   // per-step event timing (measurement aid)
   static constexpr int kRing = 256;
   bool prof_on = false;
+  int prof_step = -1;  // -1: every step; else only this step is bracketed
   bool prof_events = false;
   hipEvent_t ev[kRing][LLAMA_LAYER_STEPS + 1];
   long long prof_next = 0, prof_done = 0;  // calls recorded / harvested
@@ -103,9 +104,10 @@ const char* const kStepNames[LLAMA_LAYER_STEPS] = {
 // add the step times of the oldest recorded call to the totals
 hipError_t harvest_one(llama_layer* L) {
   hipEvent_t* e = L->ev[L->prof_done % llama_layer::kRing];
-  hipError_t r = hipEventSynchronize(e[LLAMA_LAYER_STEPS]);
+  const int lo = L->prof_step < 0 ? 0 : L->prof_step, hi = L->prof_step < 0 ? LLAMA_LAYER_STEPS : L->prof_step + 1;
+  hipError_t r = hipEventSynchronize(e[hi]);
   if (r != hipSuccess) return r;
-  for (int i = 0; i < LLAMA_LAYER_STEPS; ++i) {
+  for (int i = lo; i < hi; ++i) {
     float ms = 0.f;
     r = hipEventElapsedTime(&ms, e[i], e[i + 1]);
     if (r != hipSuccess) return r;
@@ -377,7 +379,10 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
     if (L->prof_next - L->prof_done == llama_layer::kRing) HIP_OR_RETURN(harvest_one(L), "profile harvest");
     ev = L->ev[L->prof_next % llama_layer::kRing];
   }
-  auto mark = [&](int i) -> hipError_t { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+  const int ps = L->prof_step;
+  auto mark = [&](int i) -> hipError_t {
+    return ev && (ps < 0 || i == ps || i == ps + 1) ? hipEventRecord(ev[i], s) : hipSuccess;
+  };
 
   HIP_OR_RETURN(mark(0), "event record");
   HIP_OR_RETURN(launch_rmsnorm(xb, 0, L->g1, 0, xn, 0, skinny, M, d, c.rms_eps, s), "rmsnorm 1");
@@ -445,6 +450,8 @@ static int checked_call(llama_layer* L, const void* x, void* y, const int32_t* p
 int llama_layer_profile(llama_layer* L, int enable) {
   g_last_error.clear();
   if (!L) return fail(LLAMA_ERR_NULL, "layer must be non-null");
+  if (enable < 0 || enable >= 2 + LLAMA_LAYER_STEPS)
+    return fail(LLAMA_ERR_INVALID, "profile mode %d: 0 off, 1 every step, 2 + i step i only", enable);
   if (enable) {
     if (!L->prof_events) {
       for (auto& row : L->ev)
@@ -456,6 +463,7 @@ int llama_layer_profile(llama_layer* L, int enable) {
     L->prof_next = L->prof_done = 0;
   }
   L->prof_on = enable != 0;
+  L->prof_step = enable >= 2 ? enable - 2 : -1;
   return LLAMA_OK;
 }
 
