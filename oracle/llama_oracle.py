@@ -17,6 +17,9 @@ Sources, cited by page title and section:
               its memory accounting.
   [MLP]       "深入解析Llama MLP模块：SwiGLU激活函数与参数配置详解" (Llama MLP
               deep dive): §2.2 the gate/up/down computation, §3 parameter counts.
+  [LARQL]     "从纯文本到视觉理解：LARQL多模态支持(SigLIP)架构解析" (LARQL
+              multimodal support): the SigLIP encoder's bidirectional attention,
+              the causal kernel without its future-column mask.
 
 Two modes:
   plain       no intermediate rounding (the gate for fp32 layers);
@@ -169,7 +172,8 @@ def _f64(a):
 
 
 def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_heads,
-                  eps=1e-6, rope_base=10000.0, bf16_points=False, rows=None):
+                  eps=1e-6, rope_base=10000.0, bf16_points=False, rows=None,
+                  bidirectional=False):
     """One pre-norm decoder layer forward over B sequences with a KV cache.
 
         X'  = x  + o_proj(CausalAttn(RoPE(q, k), v))      q,k,v = proj(RMSNorm1(x))
@@ -186,6 +190,10 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
     rows       optional list of flat token indices b*T + t; when given, the
                output is computed for those tokens only (keys and values are
                still computed for every token, as the cache needs them).
+    bidirectional  the encoder-style variant without the causal mask: every
+               new token of sequence b sees every slot up to the largest
+               position among the sequence's new tokens.  [LARQL: the SigLIP
+               encoder's attention is the causal one without the mask.]
 
     Returns (y [B, T, d] (rows not asked for are NaN), k_cache', v_cache').
     """
@@ -228,10 +236,13 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
         xb, xnb, pb = x[b, ts], xn[b, ts], pos[b, ts]               # [n,d]
         q = (xnb @ W["wq"].T).reshape(ts.size, H, dh).transpose(1, 0, 2)   # [H,n,dh]
         q = r(rope(q, pb[None, :], rope_base))
-        S = int(pb.max()) + 1                                        # slots 0 .. max position
+        # the position each query may see up to: its own, or (bidirectional)
+        # the sequence's largest new position
+        lim = np.full(ts.size, pos[b].max()) if bidirectional else pb
+        S = int(lim.max()) + 1                                       # slots 0 .. max position
         kk = repeat_kv(kc[b][:, :S], n_rep)                          # [H,S,dh]
         vv = repeat_kv(vc[b][:, :S], n_rep)
-        heads = [masked_softmax_attention(q[h], kk[h], vv[h], pb, np.arange(S))[0]
+        heads = [masked_softmax_attention(q[h], kk[h], vv[h], lim, np.arange(S))[0]
                  for h in range(H)]
         o = r(np.stack(heads, axis=1).reshape(ts.size, H * dh))      # heads concatenated
         x1 = xb + o @ W["wo"].T                                      # X', never rounded

@@ -230,10 +230,11 @@ def _tiny(seed, B=2, T=6, d=32, H=4, Hkv=2, f=48, S=None, gains=True):
     return x, w, kc, vc
 
 
-def _torch_layer(x, pos, w, kc, vc, H, Hkv, eps=1e-6, base=10000.0):
+def _torch_layer(x, pos, w, kc, vc, H, Hkv, eps=1e-6, base=10000.0, bidirectional=False):
     """Independent fp64 re-derivation from library routines: F.rms_norm,
     F.linear, RoPE as complex multiplication, SDPA with enable_gqa and an
-    explicit boolean position mask, F.silu."""
+    explicit boolean position mask (bidirectional: every new token of a
+    sequence sees the slots up to the sequence's largest new position), F.silu."""
     t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))  # noqa: E731
     x, kc, vc = t(x), t(kc).clone(), t(vc).clone()
     W = {k: t(v) for k, v in w.items()}
@@ -256,7 +257,8 @@ def _torch_layer(x, pos, w, kc, vc, H, Hkv, eps=1e-6, base=10000.0):
         kc[b, :, pos[b]] = k[b]
         vc[b, :, pos[b]] = v[b]
     S = kc.shape[2]
-    allowed = torch.arange(S)[None, None, :] <= pos[:, :, None]      # [B, T, S]
+    lim = pos.max(dim=1, keepdim=True).values.expand(B, T) if bidirectional else pos
+    allowed = torch.arange(S)[None, None, :] <= lim[:, :, None]      # [B, T, S]
     o = F.scaled_dot_product_attention(q, kc, vc, attn_mask=allowed[:, None], enable_gqa=True)
     x1 = x + F.linear(o.transpose(1, 2).reshape(B, T, H * dh), W["wo"])
     xn2 = F.rms_norm(x1, (d,), W["ffn_norm"], eps)
@@ -314,6 +316,40 @@ def test_layer_is_causal():
     y2, _, _ = O.decoder_layer(x2, pos, w, kc, vc, n_heads=4, n_kv_heads=2)
     np.testing.assert_array_equal(y2[0, :5], y[0, :5])
     assert not np.allclose(y2[0, 5:], y[0, 5:])
+
+
+@pytest.mark.parametrize("prior", [0, 5])
+def test_bidirectional_layer_matches_library_rederivation(prior):
+    """The encoder-style variant (LARQL page: the SigLIP encoder's attention is
+    the causal one without the mask), fresh and over a prior cache."""
+    H, Hkv, T = 4, 2, 5
+    x, w, kc, vc = _tiny(40 + prior, B=2, T=T, H=H, Hkv=Hkv, S=prior + T + 3)
+    if prior:
+        rng = _rng(41)
+        kc[:, :, :prior] = rng.standard_normal(kc[:, :, :prior].shape)
+        vc[:, :, :prior] = rng.standard_normal(vc[:, :, :prior].shape)
+    pos = np.tile(np.arange(prior, prior + T), (2, 1))
+    y, k2, _ = O.decoder_layer(x, pos, w, kc, vc, n_heads=H, n_kv_heads=Hkv, bidirectional=True)
+    yr, kr, _ = _torch_layer(x, pos, w, kc, vc, H, Hkv, bidirectional=True)
+    np.testing.assert_allclose(y, yr, rtol=1e-10, atol=1e-10)
+    np.testing.assert_allclose(k2, kr, atol=1e-12)
+
+
+def test_bidirectional_sees_later_tokens_and_agrees_at_the_last():
+    """Without the mask an earlier token's output depends on later tokens; the
+    token at the largest position sees the same slots either way, so its
+    output equals the causal layer's."""
+    x, w, kc, vc = _tiny(42, B=1, T=8)
+    pos = np.arange(8)[None]
+    kw = dict(n_heads=4, n_kv_heads=2)
+    yb, _, _ = O.decoder_layer(x, pos, w, kc, vc, bidirectional=True, **kw)
+    yc, _, _ = O.decoder_layer(x, pos, w, kc, vc, **kw)
+    np.testing.assert_allclose(yb[0, -1], yc[0, -1], rtol=1e-13, atol=1e-13)
+    assert not np.allclose(yb[0, 0], yc[0, 0])
+    x2 = x.copy()
+    x2[0, 5:] = _rng(43).standard_normal(x2[0, 5:].shape)
+    yb2, _, _ = O.decoder_layer(x2, pos, w, kc, vc, bidirectional=True, **kw)
+    assert not np.allclose(yb2[0, :5], yb[0, :5])
 
 
 def test_decode_equals_last_row_of_prefill():
