@@ -40,11 +40,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def prefill_flops(wl, T, B):
-    """2 N P_lin + causal attention 4 dh H sum_t (t + 1) (positions 0..T-1)."""
+def prefill_flops(wl, T, B, bidirectional=False):
+    """2 N P_lin + causal attention 4 dh H sum_t (t + 1) (positions 0..T-1);
+    bidirectional: every token sees all T slots, 4 dh H T^2 per sequence."""
     d, H, Hkv, dh, f = wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff
     p_lin = d * (H + 2 * Hkv) * dh + H * dh * d + 3 * d * f
-    attn = 4 * dh * H * B * (T * (T + 1) // 2)
+    attn = 4 * dh * H * B * (T * T if bidirectional else T * (T + 1) // 2)
     return 2 * B * T * p_lin + attn
 
 
@@ -75,9 +76,9 @@ def traffic_from_profile(kernel_src):
     return prof.get("traffic_bytes_per_launch")
 
 
-def layer_config(lib, wl, max_tokens):
+def layer_config(lib, wl, max_tokens, bidirectional=False):
     return lib.make_config(wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff, wl.max_pos,
-                           max_tokens, wl.dtype, wl.rms_eps, wl.rope_base)
+                           max_tokens, wl.dtype, wl.rms_eps, wl.rope_base, bidirectional=bidirectional)
 
 
 GATE_UP_STEP = 5  # the library's step index of the gate/up projection
@@ -186,7 +187,8 @@ def bench_decode(lib, synth, steps, warmup):
 
 
 def bench_other_configs(lib, synth, steps, warmup):
-    """The other layer shapes, timed the same way (not the headline): 13B-shape
+    """The other layer shapes, timed the same way (not the headline): the 7B
+    shape with bidirectional attention (the encoder-style variant), 13B-shape
     prefill (2 x 4096 tokens), 70B-shape GQA prefill (4096 tokens) and the 64
     single-token decode steps that follow it (positions 4096..4159; caches
     evicted by a 512 MB read before each step, as for the 7B decode)."""
@@ -194,15 +196,16 @@ def bench_other_configs(lib, synth, steps, warmup):
     res = {}
     flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    for name in ("llama13b_prefill", "llama70b_gqa"):
-        wl = synth.WORKLOADS[name]
+    for name in ("llama7b_prefill_bidirectional", "llama13b_prefill", "llama70b_gqa"):
+        bidir = name.endswith("_bidirectional")
+        wl = synth.WORKLOADS[name.replace("_bidirectional", "")]
         B, T = wl.batch, wl.seq
         w = synth.make_weights(wl, "cuda")
         x = synth.make_x(wl, (B, T), device="cuda")
         pos = synth.prefill_positions(B, T, device="cuda")
         kc, vc = synth.make_cache(wl, "cuda")
         y = torch.empty_like(x)
-        layer = lib.LlamaLayer(layer_config(lib, wl, B * T), w)
+        layer = lib.LlamaLayer(layer_config(lib, wl, B * T, bidirectional=bidir), w)
         for _ in range(warmup):
             layer.prefill(x, pos, kc, vc, y=y)
         torch.cuda.synchronize()
@@ -211,7 +214,7 @@ def bench_other_configs(lib, synth, steps, warmup):
             layer.prefill(x, pos, kc, vc, y=y)
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) / steps * 1e3
-        tfl = prefill_flops(wl, T, B) / (ms * 1e-3) / 1e12
+        tfl = prefill_flops(wl, T, B, bidir) / (ms * 1e-3) / 1e12
         res[name.replace("_gqa", "_gqa_prefill")] = {
             "batch": B, "seq_len": T, "ms_per_step": ms, "tokens_per_s": B * T / ms * 1e3,
             "tflops": tfl, "mfma_frac": tfl / PEAK_BF16_TFLOPS}

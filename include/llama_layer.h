@@ -81,6 +81,13 @@ typedef struct {
   int32_t max_pos;     /* cache capacity per sequence; every position < max_pos */
   int32_t max_tokens;  /* largest B*T a call may pass; sizes the scratch */
   int32_t dtype;       /* llama_dtype */
+  int32_t bidirectional; /* 0: causal (the decoder layer).  1: the encoder-style
+                            variant without the causal mask ("LARQL multimodal
+                            support" page: the SigLIP encoder's attention is the
+                            causal kernel without its future-column condition):
+                            every new token of sequence b attends to slots
+                            0 .. P_b, P_b = the largest of b's positions in the
+                            call.  A decode call (T = 1) is the same either way. */
 } llama_layer_config;
 
 /* Device pointers to the caller's weights, each [out, in] row-major in the
@@ -114,7 +121,8 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
  * positions  [B*T] int32: token (b, t) sits at positions[b*T + t]; within a
  *            sequence the positions are distinct and each is < max_pos.  Its
  *            rotated key and its value are written to cache slot positions[.];
- *            its query attends to slots 0 .. positions[.] of sequence b, so
+ *            its query attends to slots 0 .. positions[.] of sequence b
+ *            (bidirectional: 0 .. the largest position of b in the call), so
  *            slots below the sequence's new positions must already hold that
  *            sequence's earlier keys and values (a chunked prefill continues a
  *            cache; positions 0..T-1 start one).

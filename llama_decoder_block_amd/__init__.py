@@ -43,7 +43,8 @@ class LlamaLayerConfig(ctypes.Structure):
                 ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("rms_eps", ctypes.c_float),
                 ("rope_base", ctypes.c_float), ("max_pos", ctypes.c_int32),
-                ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("max_tokens", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("bidirectional", ctypes.c_int32)]
 
 
 WEIGHT_NAMES = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up", "w_down")
@@ -121,10 +122,11 @@ def _ptr(t, name, dtype=None):
 
 
 def make_config(d_model, n_heads, n_kv_heads, head_dim, d_ff, max_pos, max_tokens, dtype,
-                rms_eps=1e-6, rope_base=10000.0) -> LlamaLayerConfig:
+                rms_eps=1e-6, rope_base=10000.0, bidirectional=False) -> LlamaLayerConfig:
     return LlamaLayerConfig(int(d_model), int(n_heads), int(n_kv_heads), int(head_dim), int(d_ff),
                             float(rms_eps), float(rope_base), int(max_pos), int(max_tokens),
-                            LLAMA_BF16 if dtype in ("bf16", LLAMA_BF16) else LLAMA_F32)
+                            LLAMA_BF16 if dtype in ("bf16", LLAMA_BF16) else LLAMA_F32,
+                            1 if bidirectional else 0)
 
 
 def llama_layer_create(config: LlamaLayerConfig, weights: dict, stream=None) -> ctypes.c_void_p:

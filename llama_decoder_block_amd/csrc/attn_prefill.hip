@@ -2,7 +2,11 @@
 //
 // Computes, for every query token m (sequence b, position p_m) and query head
 // h, o = sum_j softmax_j(q.k_j / sqrt(128)) v_j over the cache slots
-// j = 0 .. p_m of sequence b and kv head g = h / (H / Hkv).
+// j = 0 .. p_m of sequence b and kv head g = h / (H / Hkv).  The
+// bidirectional variant (the SigLIP encoder's attention on the "LARQL
+// multimodal support" page: the causal kernel without its mask condition)
+// uses j = 0 .. P_b for every query, P_b = the largest position of sequence b
+// among the call's tokens.
 //
 // Sources: "LMDrive LLM core inference unit" page, §2.3 LlamaAttention
 // (scores q k^T / sqrt(head_dim), additive mask, softmax, weights times v;
@@ -60,7 +64,7 @@ template <int NGRP>
 __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ pos, bf16_t* __restrict__ o,
-    int o_frag, int n_seq, int T, int H, int Hkv, int max_pos, float scale_log2) {
+    int o_frag, int n_seq, int T, int H, int Hkv, int max_pos, int bidir, float scale_log2) {
   __shared__ __attribute__((aligned(16))) bf16_t Ks[NGRP][2][BKV * KSTR];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[NGRP][2][DH * VSTR];
 
@@ -83,6 +87,18 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
   const bool valid = t < T;
   const size_t row = static_cast<size_t>(b) * T + (valid ? t : 0);
   int pq = valid ? pos[row] : -1;
+  if (bidir) {  // uniform: every query of the sequence sees up to its largest position in the call
+    int sm = -1;
+    for (int i = static_cast<int>(threadIdx.x); i < T; i += static_cast<int>(blockDim.x))
+      sm = max(sm, pos[static_cast<size_t>(b) * T + i]);
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) sm = max(sm, __shfl_xor(sm, sft, 64));
+    __shared__ int s_seq[4 * NGRP];
+    if (lane == 0) s_seq[threadIdx.x >> 6] = sm;
+    __syncthreads();
+    for (int w = 0; w < 4 * NGRP; ++w) sm = max(sm, s_seq[w]);
+    if (valid) pq = sm;
+  }
   pq = min(pq, max_pos - 1);
 
   // wave / workgroup position range
@@ -310,7 +326,7 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
 
 hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                                const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
-                               int n_kv_heads, int max_pos, hipStream_t s) {
+                               int n_kv_heads, int max_pos, int bidir, hipStream_t s) {
   if (o_frag && B * T > kSkinnyMaxTokens) return hipErrorInvalidValue;
   const int n_wg = (T + BQ - 1) / BQ * n_heads * B;
   const dim3 grid(static_cast<unsigned>(n_wg));
@@ -320,10 +336,10 @@ hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf1
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
   if (n_wg <= 2 * n_cu)  // one round of two workgroups per CU
     hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(512), 0, s, q, k_cache, v_cache, pos, o, o_frag, B, T,
-                       n_heads, n_kv_heads, max_pos, scale_log2);
+                       n_heads, n_kv_heads, max_pos, bidir, scale_log2);
   else
     hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, o, o_frag, B, T,
-                       n_heads, n_kv_heads, max_pos, scale_log2);
+                       n_heads, n_kv_heads, max_pos, bidir, scale_log2);
   return hipGetLastError();
 }
 

@@ -162,11 +162,12 @@ hipError_t launch_skinny_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int f
                                 bf16_t* out, const SkinnyScratch& sc, hipStream_t s);
 
 // Causal flash attention over the cache for prefill (bf16, dh = 128).
-// q/o [B*T, H*128]; the query of token m sees cache slots 0..pos[m].
+// q/o [B*T, H*128]; the query of token m sees cache slots 0..pos[m], or with
+// bidir = 1 slots 0..max over t of pos[b*T + t] (its sequence's largest).
 // o_frag = 1 writes o in fragment order instead of row-major.
 hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                                const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
-                               int n_kv_heads, int max_pos, hipStream_t s);
+                               int n_kv_heads, int max_pos, int bidir, hipStream_t s);
 
 // Decode attention (bf16, dh = 128) for one query per sequence, split over
 // the cache when the grid would otherwise be small, followed by the merge of
@@ -180,6 +181,7 @@ hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16
 // fp32 path (any shape).
 struct F32Layer {
   int d, H, Hkv, dh, f, max_pos;
+  int bidir;  // attention without the causal mask (each token sees up to its sequence's largest position)
   float eps;
   const float* g1; const float* g2;
   const float* wqkv; const float* wo; const float* wgu; const float* wd;  // wgu: [gate; up]

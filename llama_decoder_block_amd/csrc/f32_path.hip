@@ -57,18 +57,25 @@ __global__ void f32_rope_scatter_kernel(float* __restrict__ qkv, float* __restri
   }
 }
 
-// one wavefront per (token, query head)
+// one wavefront per (token, query head); bidir: the token sees every slot up
+// to its sequence's largest position in the call, not only up to its own
 __global__ __launch_bounds__(64) void f32_attention_kernel(const float* __restrict__ qkv,
                                                            const float* __restrict__ k_cache,
                                                            const float* __restrict__ v_cache,
                                                            const int32_t* __restrict__ pos,
                                                            float* __restrict__ o, int T, int H,
-                                                           int Hkv, int dh, int max_pos) {
+                                                           int Hkv, int dh, int max_pos, int bidir) {
   const int m = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const int g = h / (H / Hkv);
   const int b = m / T;
   const float* q = qkv + static_cast<size_t>(m) * (H + 2 * Hkv) * dh + h * dh;
-  const int p = min(pos[m], max_pos - 1);
+  int lim = pos[m];
+  if (bidir) {
+    for (int t = lane; t < T; t += 64) lim = max(lim, pos[b * T + t]);
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) lim = max(lim, __shfl_xor(lim, sft, 64));
+  }
+  const int p = min(lim, max_pos - 1);
   const float* K = k_cache + static_cast<size_t>(b * Hkv + g) * max_pos * dh;
   const float* V = v_cache + static_cast<size_t>(b * Hkv + g) * max_pos * dh;
   const float scale = 1.f / sqrtf(static_cast<float>(dh));
@@ -131,7 +138,7 @@ hipError_t run_f32_layer(const F32Layer& L, const float* x, float* y, const int3
                      L.rope_cos, L.rope_sin, T, L.H, L.Hkv, L.dh, L.max_pos);
   LLAMA_TRY(hipGetLastError());
   hipLaunchKernelGGL(f32_attention_kernel, dim3(M, L.H), dim3(64), 0, s, L.qkv, k_cache, v_cache, pos,
-                     L.attn, T, L.H, L.Hkv, L.dh, L.max_pos);
+                     L.attn, T, L.H, L.Hkv, L.dh, L.max_pos, L.bidir);
   LLAMA_TRY(hipGetLastError());
   LLAMA_TRY(gemm(L.attn, L.wo, x, L.x1, M, L.d, L.H * L.dh, s));
   LLAMA_TRY(launch_rmsnorm(L.x1, 1, L.g2, 1, L.xn, 1, 0, M, L.d, L.eps, s));

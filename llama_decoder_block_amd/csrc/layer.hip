@@ -148,6 +148,7 @@ int check_config(const llama_layer_config* c) {
   if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps) || !(c->rope_base > 0.f) || !isfinite(c->rope_base))
     return fail(LLAMA_ERR_INVALID, "rms_eps must be finite and >= 0, rope_base finite and > 0");
   if (c->dtype != LLAMA_F32 && c->dtype != LLAMA_BF16) return fail(LLAMA_ERR_INVALID, "unknown dtype");
+  if (c->bidirectional != 0 && c->bidirectional != 1) return fail(LLAMA_ERR_INVALID, "bidirectional must be 0 or 1");
   if (c->dtype == LLAMA_BF16) {
     if (c->head_dim != 128) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 kernels need head_dim 128");
     if (c->d_model % 128 || c->d_ff % 128)
@@ -337,6 +338,7 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
   if (c.dtype == LLAMA_F32) {
     F32Layer F{};
     F.d = d; F.H = H; F.Hkv = Hkv; F.dh = c.head_dim; F.f = f; F.max_pos = c.max_pos; F.eps = c.rms_eps;
+    F.bidir = c.bidirectional;
     F.g1 = static_cast<const float*>(L->g1); F.g2 = static_cast<const float*>(L->g2);
     F.wqkv = static_cast<const float*>(L->wqkv); F.wo = static_cast<const float*>(L->wo);
     F.wgu = static_cast<const float*>(L->wgu); F.wd = static_cast<const float*>(L->wd);
@@ -405,7 +407,7 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
     }
   } else {
     HIP_OR_RETURN(launch_attn_prefill(q, static_cast<const bf16_t*>(kc), static_cast<const bf16_t*>(vc), pos,
-                                      o, skinny, B, T, H, Hkv, c.max_pos, s),
+                                      o, skinny, B, T, H, Hkv, c.max_pos, c.bidirectional, s),
                   "prefill attention");
   }
   HIP_OR_RETURN(mark(3), "event record");

@@ -19,21 +19,24 @@ def f64(t) -> np.ndarray:
     return t.detach().to("cpu").to(torch.float64).numpy()
 
 
-def layer_config(lib, wl: synth.Workload, max_tokens: int, max_pos: int | None = None):
+def layer_config(lib, wl: synth.Workload, max_tokens: int, max_pos: int | None = None,
+                 bidirectional: bool = False):
     return lib.make_config(wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff,
-                           max_pos or wl.max_pos, max_tokens, wl.dtype, wl.rms_eps, wl.rope_base)
+                           max_pos or wl.max_pos, max_tokens, wl.dtype, wl.rms_eps, wl.rope_base,
+                           bidirectional=bidirectional)
 
 
 def oracle_weights(w: dict) -> dict:
     return {k: f64(v) for k, v in w.items()}
 
 
-def oracle_prefill(wl, w64, x, pos, kc, vc, rows=None, bf16_points=None):
+def oracle_prefill(wl, w64, x, pos, kc, vc, rows=None, bf16_points=None, bidirectional=False):
     if bf16_points is None:
         bf16_points = wl.dtype == "bf16"
     return O.decoder_layer(f64(x), f64(pos).astype(np.int64), w64, f64(kc), f64(vc),
                            n_heads=wl.n_heads, n_kv_heads=wl.n_kv_heads, eps=wl.rms_eps,
-                           rope_base=wl.rope_base, bf16_points=bf16_points, rows=rows)
+                           rope_base=wl.rope_base, bf16_points=bf16_points, rows=rows,
+                           bidirectional=bidirectional)
 
 
 def rms(a) -> float:

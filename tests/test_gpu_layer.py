@@ -21,19 +21,20 @@ def _wl(name="small", dtype="bf16", d=512, H=4, Hkv=2, f=1408, B=2, T=300, prior
                           prior=prior, decode_steps=steps, seed=seed)
 
 
-def _setup(wl, random_gains=False, max_tokens=None):
+def _setup(wl, random_gains=False, max_tokens=None, bidirectional=False):
     w = synth.make_weights(wl, DEV, random_gains=random_gains)
     x = synth.make_x(wl, (wl.batch, wl.seq), device=DEV)
     kc, vc = synth.make_cache(wl, DEV)
     pos = synth.prefill_positions(wl.batch, wl.seq, start=wl.prior, device=DEV)
-    layer = lib.LlamaLayer(G.layer_config(lib, wl, max_tokens or wl.batch * wl.seq), w)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, max_tokens or wl.batch * wl.seq,
+                                          bidirectional=bidirectional), w)
     return w, x, kc, vc, pos, layer
 
 
-def _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc):
+def _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc, bidirectional=False):
     torch.cuda.synchronize()
     w64 = G.oracle_weights(w)
-    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)
+    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0, bidirectional=bidirectional)
     written = slice(wl.prior, wl.prior + wl.seq)
     kg, vg = G.f64(kc), G.f64(vc)
     if wl.dtype == "bf16":
@@ -41,7 +42,7 @@ def _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc):
         fk, fv = G.kv_floors(x, w)
         G.assert_bf16_storage(kg[:, :, written], ko[:, :, written], "K written", fk)
         G.assert_bf16_storage(vg[:, :, written], vo[:, :, written], "V written", fv)
-        yp, _, _ = G.oracle_prefill(wl, w64, x, pos, kc0, vc0, bf16_points=False)
+        yp, _, _ = G.oracle_prefill(wl, w64, x, pos, kc0, vc0, bf16_points=False, bidirectional=bidirectional)
         print(f"  (vs plain oracle: y max|err|/rms = {G.rel_err(G.f64(y), yp):.5f})")
     else:
         G.assert_f32(G.f64(y), yo, "y")
@@ -92,6 +93,39 @@ def test_chunked_prefill_over_prior_cache(dtype):
     kc0, vc0 = kc.clone(), vc.clone()
     y = layer.prefill(x, pos, kc, vc)
     _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(dtype="bf16", d=512, H=4, Hkv=2, f=1408, B=2, T=300),             # tiled GEMMs, ragged query tile
+    dict(dtype="bf16", d=256, H=2, Hkv=2, f=384, B=3, T=5),                # weight-streaming GEMMs
+    dict(dtype="bf16", d=512, H=4, Hkv=2, f=1408, B=2, T=100, prior=150),  # over a prior cache
+    dict(dtype="f32", d=64, H=4, Hkv=2, f=96, B=2, T=7, prior=9),
+])
+def test_bidirectional_prefill(shape):
+    """The encoder-style variant: every new token sees its sequence's slots up
+    to the largest position in the call."""
+    wl = _wl(**shape)
+    print(f"case {shape}", flush=True)
+    w, x, kc, vc, pos, layer = _setup(wl, random_gains=True, bidirectional=True)
+    kc0, vc0 = kc.clone(), vc.clone()
+    y = layer.prefill(x, pos, kc, vc)
+    _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc, bidirectional=True)
+
+
+@pytest.mark.parametrize("bidirectional", [False, True])
+def test_attention_with_several_workgroup_rounds(bidirectional):
+    """576 query-tile workgroups (more than two per CU): the attention kernel
+    with one wave group per tile, checked on sampled rows of every sequence."""
+    wl = _wl(d=1024, H=8, Hkv=2, f=1408, B=8, T=1100, seed=9)
+    print(f"case {wl} bidirectional={bidirectional}", flush=True)
+    w, x, kc, vc, pos, layer = _setup(wl, bidirectional=bidirectional)
+    kc0, vc0 = kc.clone(), vc.clone()
+    y = layer.prefill(x, pos, kc, vc)
+    torch.cuda.synchronize()
+    rows = G.sample_rows(wl.batch, wl.seq, seed=3)
+    yo, _, _ = G.oracle_prefill(wl, G.oracle_weights(w), x, pos, kc0, vc0, rows=rows,
+                                bidirectional=bidirectional)
+    G.assert_bf16_output(G.f64(y).reshape(-1, wl.d_model)[rows], yo.reshape(-1, wl.d_model)[rows], "y rows")
 
 
 @pytest.mark.parametrize("B,Hkv", [(5, 2), (1, 1), (40, 4)])
