@@ -35,6 +35,8 @@ LLAMA_BF16 = 1
 EXPORTED = ("llama_layer_create", "llama_layer_prefill", "llama_layer_decode",
             "llama_layer_destroy", "llama_layer_strerror", "llama_layer_last_error",
             "llama_layer_profile", "llama_layer_profile_read", "llama_layer_step_name")
+EXPORTED_MODEL = ("llama_model_create", "llama_model_destroy", "llama_model_prefill",
+                  "llama_model_decode", "llama_model_generate", "llama_sample")
 LLAMA_LAYER_STEPS = 7
 
 
@@ -52,6 +54,20 @@ WEIGHT_NAMES = ("attn_norm", "wq", "wk", "wv", "wo", "ffn_norm", "w_gate", "w_up
 
 class LlamaLayerWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_NAMES]
+
+
+class LlamaModelConfig(ctypes.Structure):
+    _fields_ = [("layer", LlamaLayerConfig), ("n_layers", ctypes.c_int32), ("vocab", ctypes.c_int32)]
+
+
+class LlamaModelWeights(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
+                ("layers", ctypes.POINTER(LlamaLayerWeights))]
+
+
+class LlamaSampling(ctypes.Structure):
+    _fields_ = [("temperature", ctypes.c_float), ("top_p", ctypes.c_float),
+                ("repetition_penalty", ctypes.c_float), ("eos_id", ctypes.c_int32)]
 
 
 class LlamaLayerError(RuntimeError):
@@ -89,6 +105,22 @@ def _load():
     lib.llama_layer_profile_read.restype = ctypes.c_int
     lib.llama_layer_step_name.argtypes = [ctypes.c_int]
     lib.llama_layer_step_name.restype = ctypes.c_char_p
+    pp = ctypes.POINTER(vp)
+    lib.llama_model_create.argtypes = [ctypes.POINTER(LlamaModelConfig), ctypes.POINTER(LlamaModelWeights),
+                                       vp, ctypes.POINTER(vp)]
+    lib.llama_model_create.restype = ctypes.c_int
+    lib.llama_model_destroy.argtypes = [vp]
+    lib.llama_model_destroy.restype = None
+    lib.llama_model_prefill.argtypes = [vp, vp, i32, i32, pp, pp, vp, vp]
+    lib.llama_model_prefill.restype = ctypes.c_int
+    lib.llama_model_decode.argtypes = [vp, vp, vp, i32, pp, pp, vp, vp]
+    lib.llama_model_decode.restype = ctypes.c_int
+    lib.llama_sample.argtypes = [vp, i32, i32, i32, ctypes.POINTER(LlamaSampling), vp, vp, i32, vp, vp, vp]
+    lib.llama_sample.restype = ctypes.c_int
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.llama_model_generate.argtypes = [vp, ip, i32, i32, i32, ctypes.POINTER(LlamaSampling),
+                                         ctypes.POINTER(ctypes.c_float), pp, pp, ip, ip, vp]
+    lib.llama_model_generate.restype = ctypes.c_int
     return lib
 
 
@@ -202,6 +234,109 @@ class LlamaLayer:
         h = getattr(self, "handle", None)
         if h is not None and h.value:
             llama_layer_destroy(h)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+# ---------------------------------------------------------------- generation stack
+
+def make_sampling(temperature=0.0, top_p=1.0, repetition_penalty=1.0, eos_id=-1) -> LlamaSampling:
+    return LlamaSampling(float(temperature), float(top_p), float(repetition_penalty), int(eos_id))
+
+
+def _ptr_array(tensors, name):
+    arr = (ctypes.c_void_p * len(tensors))()
+    for i, t in enumerate(tensors):
+        arr[i] = _ptr(t, f"{name}[{i}]").value
+    return arr
+
+
+def llama_sample(logits, params: LlamaSampling, history=None, history_len=None, uniforms=None, out=None,
+                 stream=None):
+    """One token per row of logits [B, V] (fp32); history [B, H] int32 with
+    history_len [B] (for the repetition penalty), uniforms [B] fp32 (for
+    temperature > 0).  Returns the int32 ids [B]."""
+    import torch
+    B, V = int(logits.shape[0]), int(logits.shape[1])
+    out = torch.empty(B, dtype=torch.int32, device=logits.device) if out is None else out
+    opt = lambda t, n, dt: None if t is None else _ptr(t, n, dt)  # noqa: E731
+    _check(LIB.llama_sample(_ptr(logits, "logits", torch.float32), B, V, V, ctypes.byref(params),
+                            opt(history, "history", torch.int32), opt(history_len, "history_len", torch.int32),
+                            0 if history is None else int(history.shape[1]),
+                            opt(uniforms, "uniforms", torch.float32), _ptr(out, "out", torch.int32),
+                            _stream_ptr(stream)))
+    return out
+
+
+class LlamaModel:
+    """Embedding, n_layers decoder layers, final RMSNorm and LM head (weights
+    copied at construction), with prefill / decode logits and a native
+    generation loop."""
+
+    def __init__(self, layer_config: LlamaLayerConfig, n_layers: int, vocab: int, embed, final_norm,
+                 lm_head, layer_weights: list, stream=None):
+        import torch
+        dt = torch.bfloat16 if layer_config.dtype == LLAMA_BF16 else torch.float32
+        self.config = LlamaModelConfig(layer_config, int(n_layers), int(vocab))
+        lw = (LlamaLayerWeights * len(layer_weights))(
+            *[LlamaLayerWeights(*[_ptr(w[n], n, dt) for n in WEIGHT_NAMES]) for w in layer_weights])
+        mw = LlamaModelWeights(_ptr(embed, "embed", dt), _ptr(final_norm, "final_norm", dt),
+                               _ptr(lm_head, "lm_head", dt), lw)
+        self.handle = ctypes.c_void_p()
+        _check(LIB.llama_model_create(ctypes.byref(self.config), ctypes.byref(mw), _stream_ptr(stream),
+                                      ctypes.byref(self.handle)))
+        self.vocab = int(vocab)
+
+    def prefill(self, ids, k_caches, v_caches, logits=None, stream=None):
+        """ids [B, T] int32 (positions 0..T-1) -> the last position's logits [B, V] fp32."""
+        import torch
+        B, T = int(ids.shape[0]), int(ids.shape[1])
+        logits = torch.empty(B, self.vocab, dtype=torch.float32, device=ids.device) if logits is None else logits
+        _check(LIB.llama_model_prefill(self.handle, _ptr(ids, "ids", torch.int32), B, T,
+                                       _ptr_array(k_caches, "k_caches"), _ptr_array(v_caches, "v_caches"),
+                                       _ptr(logits, "logits", torch.float32), _stream_ptr(stream)))
+        return logits
+
+    def decode(self, ids, positions, k_caches, v_caches, logits=None, stream=None):
+        """ids [B] int32 at positions [B] -> logits [B, V] fp32."""
+        import torch
+        B = int(ids.shape[0])
+        logits = torch.empty(B, self.vocab, dtype=torch.float32, device=ids.device) if logits is None else logits
+        _check(LIB.llama_model_decode(self.handle, _ptr(ids, "ids", torch.int32),
+                                      _ptr(positions, "positions", torch.int32), B,
+                                      _ptr_array(k_caches, "k_caches"), _ptr_array(v_caches, "v_caches"),
+                                      _ptr(logits, "logits", torch.float32), _stream_ptr(stream)))
+        return logits
+
+    def generate(self, prompt, max_new: int, params: LlamaSampling, k_caches, v_caches, uniforms=None,
+                 stream=None):
+        """prompt: host int sequence [B][T]; uniforms: host [max_new][B] floats or
+        None (greedy).  Returns the generated id lists (EOS not included)."""
+        import numpy as np
+        p = np.ascontiguousarray(np.asarray(prompt, dtype=np.int32))
+        B, T = p.shape
+        out = np.zeros((B, max_new), dtype=np.int32)
+        n = np.zeros(B, dtype=np.int32)
+        ip = ctypes.POINTER(ctypes.c_int32)
+        u = None
+        if uniforms is not None:
+            u = np.ascontiguousarray(np.asarray(uniforms, dtype=np.float32).reshape(max_new, B))
+        _check(LIB.llama_model_generate(
+            self.handle, p.ctypes.data_as(ip), B, T, int(max_new), ctypes.byref(params),
+            None if u is None else u.ctypes.data_as(ctypes.POINTER(ctypes.c_float)),
+            _ptr_array(k_caches, "k_caches"), _ptr_array(v_caches, "v_caches"),
+            out.ctypes.data_as(ip), n.ctypes.data_as(ip), _stream_ptr(stream)))
+        return [out[b, :n[b]].tolist() for b in range(B)]
+
+    def close(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            LIB.llama_model_destroy(h)
         self.handle = None
 
     def __del__(self):

@@ -160,6 +160,10 @@ hipError_t launch_skinny_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, 
                                        hipStream_t s);
 hipError_t launch_skinny_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int f, int K,
                                 bf16_t* out, const SkinnyScratch& sc, hipStream_t s);
+// out[m, n] = (A W^T)[m, n] in fp32 for n < n_valid, row stride ld (N, the
+// weight's padded row count, a multiple of 128); the LM head
+hipError_t launch_skinny_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K, float* out,
+                                int n_valid, int ld, const SkinnyScratch& sc, hipStream_t s);
 
 // Causal flash attention over the cache for prefill (bf16, dh = 128).
 // q/o [B*T, H*128]; the query of token m sees cache slots 0..pos[m], or with
@@ -191,5 +195,10 @@ struct F32Layer {
 };
 hipError_t run_f32_layer(const F32Layer& L, const float* x, float* y, const int32_t* pos, int B,
                          int T, float* k_cache, float* v_cache, hipStream_t s);
+// out[m, n] = sum_k A[m, k] W[n, k] (+ resid[m, n]), fp32, all row-major
+hipError_t launch_f32_gemm(const float* A, const float* W, const float* resid, float* out, int M, int N, int K,
+                           hipStream_t s);
+// the calling thread's last-error text (shared by every C entry point)
+int set_error(int status, const char* fmt, ...);
 
 }  // namespace llama

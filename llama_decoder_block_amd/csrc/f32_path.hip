@@ -125,6 +125,11 @@ hipError_t gemm(const float* A, const float* W, const float* resid, float* out, 
 
 }  // namespace
 
+hipError_t launch_f32_gemm(const float* A, const float* W, const float* resid, float* out, int M, int N, int K,
+                           hipStream_t s) {
+  return gemm(A, W, resid, out, M, N, K, s);
+}
+
 hipError_t run_f32_layer(const F32Layer& L, const float* x, float* y, const int32_t* pos, int B,
                          int T, float* k_cache, float* v_cache, hipStream_t s) {
   const int M = B * T;

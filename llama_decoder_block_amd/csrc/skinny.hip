@@ -37,7 +37,7 @@
 namespace llama {
 namespace {
 
-enum { SK_QKV = 0, SK_RESID32 = 1, SK_RESID16 = 2, SK_SWIGLU = 3 };
+enum { SK_QKV = 0, SK_RESID32 = 1, SK_RESID16 = 2, SK_SWIGLU = 3, SK_F32OUT = 4 };
 
 struct SkinnyArgs {
   QkvEpilogue qkv;
@@ -46,6 +46,7 @@ struct SkinnyArgs {
   float* part;     // 2 G partial slots of NB * TB * 1024 floats
   unsigned* cnt;   // per column group, zero between launches
   int cnt_len;
+  int n_valid, ld; // SK_F32OUT: columns written (< N) and the output's row stride
 };
 
 template <int NB, int TB, int NW, int DEPTH, int EPI>
@@ -126,6 +127,12 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
         bf16_t* out = static_cast<bf16_t*>(ep.out);
         *reinterpret_cast<uint2*>(out + frag_index(tok, c, f)) =
             make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+      } else if constexpr (EPI == SK_F32OUT) {
+        // plain fp32 rows (LM head logits): columns past n_valid are padding
+        float* out = static_cast<float*>(ep.out) + static_cast<size_t>(tok) * ep.ld;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (nb0 * 32 + fib + e < ep.n_valid) out[nb0 * 32 + fib + e] = v[0][4 * r4 + e];
       } else {
 #pragma unroll
         for (int j = 0; j < NB; ++j) {
@@ -341,6 +348,18 @@ hipError_t launch_skinny_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, 
   ep.cnt = sc.cnt;
   ep.cnt_len = sc.cnt_len;
   return launch<SK_RESID16>(A, W, M, N, K, ep, s);
+}
+hipError_t launch_skinny_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K, float* out, int n_valid,
+                                int ld, const SkinnyScratch& sc, hipStream_t s) {
+  if (n_valid > N || ld < n_valid) return hipErrorInvalidValue;
+  SkinnyArgs ep{};
+  ep.out = out;
+  ep.part = sc.part;
+  ep.cnt = sc.cnt;
+  ep.cnt_len = sc.cnt_len;
+  ep.n_valid = n_valid;
+  ep.ld = ld;
+  return launch<SK_F32OUT>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_skinny_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int f, int K, bf16_t* out,
                                 const SkinnyScratch& sc, hipStream_t s) {

@@ -41,6 +41,8 @@ TID_WQ, TID_WK, TID_WV, TID_WO, TID_WGATE, TID_WUP, TID_WDOWN = 2, 3, 4, 5, 6, 7
 TID_KCACHE, TID_VCACHE = 9, 10
 TID_GAIN1, TID_GAIN2 = 11, 12
 TID_DECODE_BASE = 100  # decode step s draws its input with tensor id 100 + s
+TID_EMBED, TID_FINAL_NORM, TID_LMHEAD, TID_UNIFORM = 13, 14, 15, 16
+TID_LAYER_SEED_STRIDE = 1000  # layer l of a stack uses seed + 1000 l
 
 
 def splitmix64_int(z: int) -> int:
@@ -244,3 +246,28 @@ def prefill_positions(batch: int, seq: int, start: int = 0, device="cpu"):
 def scaled(wl: Workload, **changes) -> Workload:
     """A copy of a workload with some fields changed (e.g. a shorter sequence)."""
     return dataclasses.replace(wl, **changes)
+
+
+def uniform_np(seed: int, tensor_id: int, count: int) -> np.ndarray:
+    """U[0, 1) draws (53-bit) from the same counter-based generator, fp64."""
+    base = np.uint64(_base(seed, tensor_id))
+    idx = np.arange(count, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        a = _splitmix64_np(base + idx)
+    return (a >> np.uint64(11)).astype(np.float64) * 2.0**-53
+
+
+def make_model_weights(wl: Workload, n_layers: int, vocab: int, device="cpu", random_gains: bool = False,
+                       lm_std: float = 0.05):
+    """Embedding [V, d] ~ N(0, 1), final gain, LM head [V, d] ~ N(0, lm_std^2),
+    and n_layers layer weight dicts (layer l drawn with seed + 1000 l)."""
+    import torch
+
+    dt = torch_dtype(wl)
+    d, s = wl.d_model, wl.seed
+    layers = [make_weights(dataclasses.replace(wl, seed=s + TID_LAYER_SEED_STRIDE * (l + 1)), device, random_gains)
+              for l in range(n_layers)]
+    final = ((1.0 + normal_tensor(s, TID_FINAL_NORM, (d,), 0.1, torch.float32, device)).to(dt)
+             if random_gains else torch.ones(d, dtype=dt, device=device))
+    return {"embed": normal_tensor(s, TID_EMBED, (vocab, d), 1.0, dt, device), "final_norm": final,
+            "lm_head": normal_tensor(s, TID_LMHEAD, (vocab, d), lm_std, dt, device), "layers": layers}

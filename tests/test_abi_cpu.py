@@ -13,25 +13,61 @@ import llama_decoder_block_amd as lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "llama_layer.h")
+MODEL_HEADER = os.path.join(ROOT, "include", "llama_model.h")
 
 
-def _declared_functions():
-    text = open(HEADER).read()
+def _declared_functions(header=HEADER, pattern=r"llama_layer_[a-z_]+"):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(llama_layer_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(" + pattern + r")\s*\(", text)))
+
+
+def _model_functions():
+    return _declared_functions(MODEL_HEADER, r"llama_model_[a-z_]+|llama_sample")
 
 
 def test_header_declares_the_abi():
     assert _declared_functions() == sorted(lib.EXPORTED)
+    assert _model_functions() == sorted(lib.EXPORTED_MODEL)
 
 
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (llama_layer_[a-z_]+)\b", out))
-    for name in _declared_functions():
+    exported = set(re.findall(r"\bT (llama_[a-z_]+)\b", out))
+    for name in _declared_functions() + _model_functions():
         assert name in exported, name
         assert hasattr(lib.LIB, name)
+
+
+def test_model_and_sampling_reject_bad_arguments():
+    """Argument validation of the generation ABI returns before any HIP call."""
+    h = ctypes.c_void_p()
+    lw = (lib.LlamaLayerWeights * 1)(_weights())
+    mw = lib.LlamaModelWeights(ctypes.c_void_p(4096), ctypes.c_void_p(4096), ctypes.c_void_p(4096), lw)
+    cfg = lib.LlamaModelConfig(_cfg(), 0, 100)
+    assert lib.LIB.llama_model_create(ctypes.byref(cfg), ctypes.byref(mw), None, ctypes.byref(h)) == \
+        lib.LLAMA_ERR_INVALID  # no layers
+    cfg = lib.LlamaModelConfig(_cfg(), 2, 1)
+    assert lib.LIB.llama_model_create(ctypes.byref(cfg), ctypes.byref(mw), None, ctypes.byref(h)) == \
+        lib.LLAMA_ERR_INVALID  # vocab < 2
+    assert lib.LIB.llama_model_create(None, ctypes.byref(mw), None, ctypes.byref(h)) == lib.LLAMA_ERR_NULL
+    fake = ctypes.c_void_p(4096)
+    bad = [lib.make_sampling(temperature=-1.0), lib.make_sampling(top_p=0.0), lib.make_sampling(top_p=1.5),
+           lib.make_sampling(repetition_penalty=0.5), lib.make_sampling(temperature=float("nan"))]
+    for p in bad:
+        assert lib.LIB.llama_sample(fake, 2, 100, 100, ctypes.byref(p), None, None, 0, fake, fake, None) == \
+            lib.LLAMA_ERR_INVALID
+    ok = lib.make_sampling(temperature=1.0)
+    assert lib.LIB.llama_sample(fake, 2, 100, 100, ctypes.byref(ok), None, None, 0, None, fake, None) == \
+        lib.LLAMA_ERR_NULL  # sampling needs uniforms
+    pen = lib.make_sampling(repetition_penalty=1.3)
+    assert lib.LIB.llama_sample(fake, 2, 100, 100, ctypes.byref(pen), None, None, 0, None, fake, None) == \
+        lib.LLAMA_ERR_NULL  # the penalty needs a history
+    assert lib.LIB.llama_sample(fake, 2, 100, 50, ctypes.byref(lib.make_sampling()), None, None, 0, None, fake,
+                                None) == lib.LLAMA_ERR_INVALID  # ld < vocab
+    assert lib.LIB.llama_sample(fake, 2, 1, 1, ctypes.byref(lib.make_sampling()), None, None, 0, None, fake,
+                                None) == lib.LLAMA_ERR_INVALID  # vocab < 2
 
 
 def test_strerror_covers_every_status():
