@@ -249,6 +249,54 @@ def bench_other_configs(lib, synth, steps, warmup):
     return res
 
 
+def bench_generate(lib, synth, n_layers=32, vocab=32000, B=32, T=128, max_new=64):
+    """Greedy generation with a 7B-shape stack (32 layers, LLaMA's 32000-token
+    vocabulary, random weights): B prompts of T tokens, then max_new tokens
+    each through the library's native loop (sampling, EOS bookkeeping and a
+    host sync per step included).  Decode rate = tokens generated / (loop
+    time - prefill time); bytes per decode step = every layer's weights and
+    gains + the LM head + the K/V read at the mean position."""
+    import dataclasses
+
+    import numpy as np
+    import torch
+    wl = dataclasses.replace(synth.WORKLOADS["llama7b_prefill"], batch=B, seq=T, decode_steps=max_new)
+    mw = synth.make_model_weights(wl, n_layers, vocab, "cuda")
+    cfg = layer_config(lib, wl, B * T)
+    model = lib.LlamaModel(cfg, n_layers, vocab, mw["embed"], mw["final_norm"], mw["lm_head"], mw["layers"])
+    del mw
+    kc = [torch.zeros(B, wl.n_kv_heads, wl.max_pos, wl.head_dim, dtype=torch.bfloat16, device="cuda")
+          for _ in range(n_layers)]
+    vc = [torch.zeros_like(k) for k in kc]
+    rng = np.random.default_rng(5)
+    prompt = rng.integers(0, vocab, size=(B, T)).astype(np.int32)
+    ids = torch.tensor(prompt, device="cuda")
+    sp = lib.make_sampling()
+    model.generate(prompt, 4, sp, kc, vc)  # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        model.prefill(ids, kc, vc)
+    torch.cuda.synchronize()
+    pre_ms = (time.perf_counter() - t0) / 3 * 1e3
+    t0 = time.perf_counter()
+    out = model.generate(prompt, max_new, sp, kc, vc)
+    gen_ms = (time.perf_counter() - t0) * 1e3
+    n_tok = sum(len(o) for o in out)
+    step_ms = (gen_ms - pre_ms) / max_new
+    d = wl.d_model
+    p_layer = d * (wl.n_heads + 2 * wl.n_kv_heads) * wl.head_dim + wl.n_heads * wl.head_dim * d + 3 * d * wl.d_ff
+    kv = 2 * 2 * B * wl.n_kv_heads * wl.head_dim * (T + max_new / 2) * n_layers
+    step_bytes = 2 * (n_layers * (p_layer + 2 * d) + vocab * d + d) + kv
+    model.close()
+    log(f"generate: prefill {pre_ms:.2f} ms, {max_new} steps {gen_ms - pre_ms:.1f} ms")
+    return {"layers": n_layers, "vocab": vocab, "batch": B, "prompt": T, "new_tokens": max_new,
+            "sampling": "greedy", "prefill_ms": pre_ms, "decode_step_ms": step_ms,
+            "decode_tokens_per_s": n_tok / ((gen_ms - pre_ms) * 1e-3),
+            "decode_GBps": step_bytes / (step_ms * 1e-3) / 1e9,
+            "decode_hbm_frac": step_bytes / (step_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+
+
 def cpu_baseline(wl, host, budget_s):
     """The oracle as it stands (plain fp64 numpy) on a prefix of the same layer
     call: tokens 0..T'-1 of the sequence, T' doubled from 64 until one run takes
@@ -360,6 +408,7 @@ def main():
         out["decode"] = bench_decode(lib, synth, args.decode_steps, 3)
     if args.other_configs:
         out["other_configs"] = bench_other_configs(lib, synth, max(3, args.steps // 4), 2)
+        out["other_configs"]["llama7b_generate"] = bench_generate(lib, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_budget_s)
     print(json.dumps(out), flush=True)
