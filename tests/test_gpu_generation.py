@@ -230,3 +230,37 @@ def test_generation_stops_at_eos_as_in_the_notes():
     got = model.generate([[2, 2], [1, 3]], 5, lib.make_sampling(), kc, vc)  # no penalty, no EOS
     assert got == [[0] * 5, [0] * 5]
     model.close()
+
+
+def test_bf16_gqa_batch_generation_with_eos_and_edges():
+    """A bf16 GQA stack (4 query heads over 1 kv head), three prompts of one
+    token, greedy with an EOS taken from the oracle's own output so that one
+    row stops early; max_new = 1 as the smallest loop.  Tokens compared with
+    the oracle up to the first fp32-marginal step."""
+    wl = synth.Workload("gqa_model", "bf16", 512, 4, 1, 128, 1408, 3, 1, decode_steps=6, seed=35)
+    L, V, B, T, N = 2, 512, 3, 1, 6
+    mw = _model(wl, L, V, lm_std=0.5)
+    om = _oracle_model(wl, mw)
+    model = _gpu_model(wl, mw, L, V, B * T)
+    prompt = np.array([[5], [77], [300]], dtype=np.int32)
+    ref, seen = GO.generate(prompt, om, _oracle_caches(wl, B, L), max_new=N, temperature=0.0, bf16_points=True)
+    kc, vc = _caches(wl, B, L)
+    got = model.generate(prompt, N, lib.make_sampling(), kc, vc)
+    same = 0
+    for b in range(B):
+        for s_, t in enumerate(ref[b]):
+            if not _check_pick(got[b][s_], seen[s_, b], 0.0, 1.0, 1.0, [], 0.0, tol=2e-2):
+                break
+            assert got[b][s_] == t
+            same += 1
+    print(f"  {same} greedy tokens identical to the oracle's")
+    eos = ref[0][2]
+    kc, vc = _caches(wl, B, L)
+    got2 = model.generate(prompt, N, lib.make_sampling(eos_id=eos), kc, vc)
+    for b in range(B):  # every row is the greedy sequence cut at its first EOS
+        k = got[b].index(eos) if eos in got[b] else len(got[b])
+        assert got2[b] == got[b][:k]
+    kc, vc = _caches(wl, B, L)
+    got1 = model.generate(prompt, 1, lib.make_sampling(), kc, vc)
+    assert got1 == [g[:1] for g in got]
+    model.close()
