@@ -127,6 +127,9 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
  *            sequence's earlier keys and values (a chunked prefill continues a
  *            cache; positions 0..T-1 start one).
  * k_cache, v_cache  [B, Hkv, max_pos, dh] (layer dtype), updated in place.
+ * bf16 precision: the attention multiplies its softmax weights (fp16, 11
+ * significant bits) with the values converted to fp16, exact for value
+ * entries within +-65504 (larger magnitudes saturate there).
  * Errors: NULL, INVALID (B or T < 1), CAPACITY (B*T > max_tokens or
  * T > max_pos), HIP (launch failure). */
 int llama_layer_prefill(llama_layer* layer, const void* x, void* y, const int32_t* positions,

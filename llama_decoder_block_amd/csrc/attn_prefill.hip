@@ -30,8 +30,9 @@
 // a lane's 16 score registers are two runs of 8 consecutive keys — exactly the
 // B operand of the next MFMA, O^T += V^T P^T, with no register shuffling.  V
 // is transposed to [dd][slot] while it is written to LDS.  P stays in fp32 in
-// the online softmax and is fed to the PV product as bf16 hi + bf16 lo (two
-// MFMAs), so the product sees P to about 16 bits instead of bf16's 8.
+// the online softmax and is fed to the PV product in fp16 (11 significant bits
+// against bf16's 8), with V converted to fp16 as it is staged; the weights
+// carry a factor 2^15 so that small ones stay fp16 normals.
 // Query tiles are launched heaviest first across all heads and sequences (the
 // causal workload grows with the tile index).  Tiles that lie wholly above a wave's diagonal are skipped, and
 // the -inf mask is applied only on tiles that cross it.
@@ -55,6 +56,24 @@ __device__ __forceinline__ int kappa(int m) {  // swap bits 2 and 3
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// two bf16 (one 32-bit word) -> two fp16: exact for |v| in [2^-14, 65504]
+// (fp16 carries bf16's 8 significant bits with 3 to spare); below that fp16's
+// subnormals keep the value to within 2^-25
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  typedef __fp16 h16x2 __attribute__((ext_vector_type(2)));
+  const h16x2 h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// two fp32 -> two fp16, round to nearest even
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+  const f16x2 h = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+  return __builtin_bit_cast(uint32_t, h);
+}
 
 // NGRP wave groups of 4 share the query tile and take every NGRP-th K/V tile
 // (NGRP = 2 halves the longest serial chain when the grid is a single round
@@ -154,7 +173,14 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
   };
   auto lstore = [&](int st) {
     if (stage_v) {
-      const uint32_t* w = reinterpret_cast<const uint32_t*>(sreg);  // w[4 * slot + dim/2]
+      // V goes to LDS as fp16 (the P.V product runs in fp16 so that P keeps
+      // 11 significant bits in one operand)
+      uint32_t w[32];  // w[4 * slot + dim/2]
+      {
+        const uint32_t* wb = reinterpret_cast<const uint32_t*>(sreg);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) w[i] = bf16x2_to_f16x2(wb[i]);
+      }
 #pragma unroll
       for (int d = 0; d < 8; ++d) {
         const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
@@ -229,17 +255,18 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
       const float alpha = fast_exp2(m_run - m_use);
       m_run = m_new;
       float lsum = 0.f;
-      uint32_t phi[2][2][4], plo[2][2][4];  // [kb][half][packed pair]
+      // the weights carry a factor 2^15 (so does their sum, which cancels it):
+      // they stay fp16 normals down to 2^-29 of the row maximum, which is 1
+      const float m_sh = m_use - 15.f;
+      uint32_t ph[2][2][4];  // [kb][half][packed fp16 pair]
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_use));
-          const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], scale_log2, -m_use));
+          const float p0 = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_sh));
+          const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], scale_log2, -m_sh));
           lsum += p0 + p1;
-          const uint32_t hp = pack_bf16x2(p0, p1);
-          phi[kb][r >> 3][(r & 7) >> 1] = hp;
-          plo[kb][r >> 3][(r & 7) >> 1] = pack_bf16x2(p0 - lo_bf16(hp), p1 - hi_bf16(hp));
+          ph[kb][r >> 3][(r & 7) >> 1] = pack_f16x2(p0, p1);
         }
       l_run = l_run * alpha + lsum;
       // once the running max settles alpha is 1 for the whole wave
@@ -254,14 +281,12 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const bf16x8 bh = as_bf16x8(make_uint4(phi[kb][half][0], phi[kb][half][1], phi[kb][half][2], phi[kb][half][3]));
-          const bf16x8 bl = as_bf16x8(make_uint4(plo[kb][half][0], plo[kb][half][1], plo[kb][half][2], plo[kb][half][3]));
+          const f16x8 bp = __builtin_bit_cast(f16x8, make_uint4(ph[kb][half][0], ph[kb][half][1], ph[kb][half][2], ph[kb][half][3]));
           const int kcol = (kb * 2 + half) * 16;
 #pragma unroll
           for (int fd = 0; fd < 4; ++fd) {
-            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[grp][st][v_row0 + fd * 32 * VSTR + kcol]);
-            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, oacc[fd], 0, 0, 0);
-            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, oacc[fd], 0, 0, 0);
+            const f16x8 a = *reinterpret_cast<const f16x8*>(&Vt[grp][st][v_row0 + fd * 32 * VSTR + kcol]);
+            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bp, oacc[fd], 0, 0, 0);
           }
         }
     };
