@@ -16,14 +16,20 @@
 // the rotate-half pairing of dimension i with i + dh/2; "Llama MLP deep dive"
 // page §2.2 (gate branch activated, up branch linear).
 //
-// gfx950 design.  256 threads = 4 wavefronts in a 2x2 grid over a 256 x BN
-// tile; each wave owns a 128 x (BN/2) block of 32x32 accumulator tiles of
-// v_mfma_f32_32x32x16_bf16.  K advances in 64-wide slabs.
+// gfx950 design.  256 threads = 4 wavefronts over a BM x BN tile, each wave
+// owning a block of 32x32 accumulator tiles of v_mfma_f32_32x32x16_bf16:
+//   * BM = 256: a 2x2 wave grid, wave tile 128 x (BN/2) (QKV: 256 x 192);
+//   * BM = 128: a 1x4 wave grid, wave tile 128 x (BN/4) (o_proj and down:
+//     128 x 256 or 128 x 512; gate/up: 128 x 512).  No two waves load the
+//     same weight fragment, so the L1 carries (BM + BN) x 32 bytes per k step
+//     instead of (BM + 2 BN) x 32; the wide tiles also halve the weight and
+//     activation bytes per flop at large K.
+// K advances in 64-wide slabs.
 //   * W is stored in fragment order, so a wave fetches each 32 x 16 weight
 //     fragment it needs with one contiguous 1 KB buffer load straight into
 //     registers (a two-deep ring per k step); W never touches LDS.
 //   * A (activations, row-major) is staged through registers into two LDS
-//     stages of 256 rows x 128 bytes; the 16-byte column chunk c of row r is
+//     stages of BM rows x 128 bytes; the 16-byte column chunk c of row r is
 //     stored at c ^ ((r >> 1) & 7) so the fragment reads of 32 consecutive
 //     rows hit distinct banks.  Rows past M read as zeros (buffer range
 //     check).  (Direct buffer->LDS loads would save the register hop, but a
@@ -37,7 +43,8 @@
 //     XCDs) gets a contiguous, M-grouped range, which keeps the A and W panels
 //     it shares inside its own L2.
 // Requires K % 128 == 0 (an even number of slabs) and N % BN == 0 except for
-// the resid epilogues, which bounds-check columns.
+// the QKV and resid epilogues, which bounds-check columns (weight fragments
+// past N read as zeros).
 #include "common.h"
 
 namespace llama {
@@ -53,7 +60,6 @@ struct EpiArgs {
 
 constexpr int BK = 64;
 constexpr int kGroupM = 8;
-constexpr int kResidBN = 128;  // N = d_model is narrow: smaller tiles, more of them
 // QKV: N = 128 (H + 2 Hkv); 192-wide tiles make 64 column tiles at 32 heads
 // (512 tiles at 2048 tokens: two full rounds of 256 CUs, where 256-wide
 // tiles leave the second round half empty)
@@ -75,13 +81,14 @@ __device__ __forceinline__ void tile_coords(int M, int N, int BM, int BN, int& m
 
 __device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
 
-template <int BN, int EPI>
+template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Wp,
                                                     int M, int N, int K, EpiArgs ep) {
-  constexpr int BM = 256;
-  constexpr int FM = 4, FN = BN / 64;          // wave tile 128 x (BN/2)
-  constexpr int STAGE = BM * 128;               // bytes per LDS stage (256 rows x 64 k)
-  constexpr int TN = BN / 2;                    // wave tile width
+  constexpr int WM = BM == 256 ? 2 : 1, WN = 4 / WM;  // wave grid
+  constexpr int TM = BM / WM, TN = BN / WN;           // wave tile
+  constexpr int FM = TM / 32, FN = TN / 32;
+  constexpr int NA = BM / 32;                         // A chunks per thread per slab
+  constexpr int STAGE = BM * 128;               // bytes per LDS stage (BM rows x 64 k)
   // epilogue: a wave's 32-row block in fp32, rows TN + 8 floats apart, so
   // rows r and r + 4 (the two halves of a wavefront store) start 32 banks apart
   constexpr int TNP = TN + 8;
@@ -93,7 +100,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   int m0, n0;
   tile_coords(M, N, BM, BN, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = WM == 2 ? wave >> 1 : 0, wn = WM == 2 ? wave & 1 : wave;
   const int KB = K >> 4;
   const __amdgpu_buffer_rsrc_t a_rs = make_rsrc(A, static_cast<uint32_t>(M) * K * 2u);
   const __amdgpu_buffer_rsrc_t b_rs = make_rsrc(Wp, static_cast<uint32_t>(N) * K * 2u);
@@ -102,12 +109,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   // 32 i + tid / 8, column chunk tid % 8 (eight threads read one 128-byte row
   // segment); it is stored at column chunk (tid % 8) ^ swz(row), and swz(row)
   // = (row >> 1) & 7 = (tid >> 4) & 7 for every i.
-  uint32_t a_goff[8];
+  uint32_t a_goff[NA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < NA; ++i)
     a_goff[i] = (static_cast<uint32_t>(m0 + 32 * i + (tid >> 3)) * K + (tid & 7) * 8) * 2u;
   const int a_woff = (tid >> 3) * 128 + (((tid & 7) ^ ((tid >> 4) & 7)) << 4);
-  uint4 sa[8];
+  uint4 sa[NA];
   auto a_gload = [&](int i, int kt) { sa[i] = buf_load16(a_rs, a_goff[i], static_cast<uint32_t>(kt) * (BK * 2u)); };
   auto a_lstore = [&](int i, int st) { *reinterpret_cast<uint4*>(stage_base(st) + a_woff + i * 32 * 128) = sa[i]; };
   // B fragments: this wave's FN n-blocks, straight from the fragment-ordered weights
@@ -121,7 +128,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   // A fragment reads
   int a_rd[FM];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) a_rd[i] = (wm * 128 + i * 32 + (lane & 31)) * 128;
+  for (int i = 0; i < FM; ++i) a_rd[i] = (wm * TM + i * 32 + (lane & 31)) * 128;
   const int a_sw = a_swz(lane & 31);  // (row >> 1) & 7 depends only on lane & 31 here (row base is a multiple of 32)
   auto frag_a = [&](int stage, int kk, int i) {
     const int c = (2 * kk + (lane >> 5)) ^ a_sw;
@@ -140,11 +147,11 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   const int nk = K / BK;  // even
   // prologue: A slab 0 -> stage 0, A slab 1 -> registers; B k-steps 0, 1 -> ring
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a_gload(i, 0);
+  for (int i = 0; i < NA; ++i) a_gload(i, 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a_lstore(i, 0);
+  for (int i = 0; i < NA; ++i) a_lstore(i, 0);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) a_gload(i, 1);
+  for (int i = 0; i < NA; ++i) a_gload(i, 1);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
@@ -178,8 +185,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
         // refilled with the same chunk of slab kt+2 two slots later, so every
         // A load has a whole slab to arrive
         if (kk < 2) {
-          constexpr int s2 = FM * FN / 4;  // slots per chunk
-          const int i = kk * 4 + m / s2;
+          constexpr int s2 = FM * FN / (NA / 2);  // slots per chunk
+          const int i = kk * (NA / 2) + m / s2;
           if (m % s2 == s2 / 2 - 1) a_lstore(i, st ^ 1);
           if (m % s2 == s2 - 1) a_gload(i, kt + 2);
         }
@@ -219,7 +226,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
 #pragma unroll
       for (int r = 0; r < 16; ++r) ebuf[(8 * (r >> 2) + hr + (r & 3)) * TNP + 32 * j + lc] = acc[i][j][r];
     // the same wave reads the block back: its LDS accesses complete in order
-    const int row0 = m0 + wm * 128 + i * 32;
+    const int row0 = m0 + wm * TM + i * 32;
     if constexpr (EPI == EPI_QKV) {
       // rotary-pair order: column 2x of a head is dim x, column 2x + 1 dim
       // x + 64.  Task: row R, 8 columns = dims x0 .. x0 + 3 and their partners.
@@ -296,24 +303,43 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   }
 }
 
-template <int BN, int EPI>
+template <int BM, int BN, int EPI>
 hipError_t launch_tiled(const bf16_t* A, const bf16_t* Wp, int M, int N, int K, const EpiArgs& ep, hipStream_t s) {
-  const int tiles = ((M + 255) / 256) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<BN, EPI>), dim3(tiles), dim3(256), 0, s, A, Wp, M, N, K, ep);
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI>), dim3(tiles), dim3(256), 0, s, A, Wp, M, N, K, ep);
   return hipGetLastError();
+}
+
+// 128 x 512 tiles do a 128 x 256 tile's work in ~1.6x its time (measured on
+// the 13B / 70B o_proj and down shapes); take them when that wins after
+// rounding each choice up to whole rounds of one tile per CU.
+bool wide_resid_tiles(int M, int N) {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    n_cu = 256;
+  const long mt = (M + 127) / 128;
+  const long r256 = (mt * ((N + 255) / 256) + n_cu - 1) / n_cu;
+  const long r512 = (mt * ((N + 511) / 512) + n_cu - 1) / n_cu;
+  return 8 * r512 < 5 * r256;
 }
 }  // namespace
 
 hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, const QkvEpilogue& q, hipStream_t s) {
-  EpiArgs ep{}; ep.qkv = q; return launch_tiled<kQkvBN, EPI_QKV>(A, W, M, N, K, ep, s);
+  EpiArgs ep{}; ep.qkv = q; return launch_tiled<256, kQkvBN, EPI_QKV>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_gemm_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K, const bf16_t* resid, float* out, hipStream_t s) {
-  EpiArgs ep{}; ep.resid = resid; ep.out = out; return launch_tiled<kResidBN, EPI_RESID32>(A, W, M, N, K, ep, s);
+  EpiArgs ep{}; ep.resid = resid; ep.out = out;
+  return wide_resid_tiles(M, N) ? launch_tiled<128, 512, EPI_RESID32>(A, W, M, N, K, ep, s)
+                                : launch_tiled<128, 256, EPI_RESID32>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_gemm_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K, const float* resid, bf16_t* out, hipStream_t s) {
-  EpiArgs ep{}; ep.resid = resid; ep.out = out; return launch_tiled<kResidBN, EPI_RESID16>(A, W, M, N, K, ep, s);
+  EpiArgs ep{}; ep.resid = resid; ep.out = out;
+  return wide_resid_tiles(M, N) ? launch_tiled<128, 512, EPI_RESID16>(A, W, M, N, K, ep, s)
+                                : launch_tiled<128, 256, EPI_RESID16>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, int K, bf16_t* out, hipStream_t s) {
-  EpiArgs ep{}; ep.out = out; return launch_tiled<256, EPI_SWIGLU>(A, Wgu, M, N, K, ep, s);
+  EpiArgs ep{}; ep.out = out;
+  return N % 512 == 0 ? launch_tiled<128, 512, EPI_SWIGLU>(A, Wgu, M, N, K, ep, s)
+                      : launch_tiled<256, 256, EPI_SWIGLU>(A, Wgu, M, N, K, ep, s);
 }
 }  // namespace llama

@@ -66,6 +66,7 @@ def test_tiny_fp32_layer():
 
 @pytest.mark.parametrize("shape", [
     dict(d=512, H=4, Hkv=2, f=1408, B=2, T=300),      # tiled GEMMs, ragged M and query tile
+    dict(d=512, H=4, Hkv=2, f=1536, B=2, T=300),      # 2f a multiple of 512: 128 x 512 gate/up tiles
     dict(d=384, H=3, Hkv=1, f=640, B=1, T=129),       # odd heads, MQA, N not a multiple of 256
     dict(d=256, H=2, Hkv=2, f=384, B=3, T=5),         # 15 tokens: weight-streaming GEMMs
     dict(d=1024, H=8, Hkv=2, f=2816, B=1, T=1),       # single token prefill
