@@ -394,7 +394,7 @@ def main():
         "config": {"workload": "llama7b_prefill", "global_batch": B, "seq_len": T,
                    "d_model": wl.d_model, "n_heads": wl.n_heads, "n_kv_heads": wl.n_kv_heads,
                    "head_dim": wl.head_dim, "d_ff": wl.d_ff, "parallelism": "single GPU"},
-        "roofline": {"bound": "mfma", "kernel": "gate_up_swiglu (gemm_kernel<256, EPI_SWIGLU>)",
+        "roofline": {"bound": "mfma", "kernel": "gate_up_swiglu (gemm_kernel<128, 512, EPI_SWIGLU>)",
                      "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gu_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_from_profile(kernel_src),
