@@ -20,7 +20,7 @@
 // owning a block of 32x32 accumulator tiles of v_mfma_f32_32x32x16_bf16:
 //   * BM = 256: a 2x2 wave grid, wave tile 128 x (BN/2) (QKV: 256 x 192);
 //   * BM = 128: a 1x4 wave grid, wave tile 128 x (BN/4) (o_proj and down:
-//     128 x 256 or 128 x 512; gate/up: 128 x 512).  No two waves load the
+//     128 x 256 or 128 x 512; gate/up: 128 x 512; QKV at large M: 128 x 512).  No two waves load the
 //     same weight fragment, so the L1 carries (BM + BN) x 32 bytes per k step
 //     instead of (BM + 2 BN) x 32; the wide tiles also halve the weight and
 //     activation bytes per flop at large K.
@@ -310,22 +310,39 @@ hipError_t launch_tiled(const bf16_t* A, const bf16_t* Wp, int M, int N, int K, 
   return hipGetLastError();
 }
 
+int cu_count() {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    n_cu = 256;
+  return n_cu;
+}
+
+// rounds of one tile per CU for BM x BN tiles
+long rounds(int M, int N, int BM, int BN, int n_cu) {
+  return ((static_cast<long>(M + BM - 1) / BM) * ((N + BN - 1) / BN) + n_cu - 1) / n_cu;
+}
+
 // 128 x 512 tiles do a 128 x 256 tile's work in ~1.6x its time (measured on
 // the 13B / 70B o_proj and down shapes); take them when that wins after
 // rounding each choice up to whole rounds of one tile per CU.
 bool wide_resid_tiles(int M, int N) {
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
-    n_cu = 256;
-  const long mt = (M + 127) / 128;
-  const long r256 = (mt * ((N + 255) / 256) + n_cu - 1) / n_cu;
-  const long r512 = (mt * ((N + 511) / 512) + n_cu - 1) / n_cu;
-  return 8 * r512 < 5 * r256;
+  const int n_cu = cu_count();
+  return 8 * rounds(M, N, 128, 512, n_cu) < 5 * rounds(M, N, 128, 256, n_cu);
+}
+
+// QKV: a 128 x 512 tile (one head per wave) does 4/3 of a 256 x 192 tile's
+// work in ~1.2x its time (measured at the 13B and 70B shapes); the same
+// rounding rule decides.
+bool wide_qkv_tiles(int M, int N) {
+  const int n_cu = cu_count();
+  return 40 * rounds(M, N, 128, 512, n_cu) < 33 * rounds(M, N, 256, 192, n_cu);
 }
 }  // namespace
 
 hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, const QkvEpilogue& q, hipStream_t s) {
-  EpiArgs ep{}; ep.qkv = q; return launch_tiled<256, kQkvBN, EPI_QKV>(A, W, M, N, K, ep, s);
+  EpiArgs ep{}; ep.qkv = q;
+  return wide_qkv_tiles(M, N) ? launch_tiled<128, 512, EPI_QKV>(A, W, M, N, K, ep, s)
+                              : launch_tiled<256, kQkvBN, EPI_QKV>(A, W, M, N, K, ep, s);
 }
 hipError_t launch_gemm_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K, const bf16_t* resid, float* out, hipStream_t s) {
   EpiArgs ep{}; ep.resid = resid; ep.out = out;
