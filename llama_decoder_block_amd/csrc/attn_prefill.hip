@@ -147,54 +147,43 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
   }
 
   // ---- K / V tile staging (buffer loads over this (b, g) cache slice), each
-  // group for its own tiles.  Waves 0-1 of a group stage V, waves 2-3 stage K,
-  // 8 loads of 16 bytes per thread each.
-  // V: thread (kg, dg) loads slots 8 kg .. 8 kg + 7 at dims 8 dg .. 8 dg + 7 and
-  // writes them transposed as 8 rows (dims) of 8 slots, 16 bytes per row; with
-  // the 144-byte row stride a 16-lane group (8 slot groups x 2 dim groups) hits
-  // 64 distinct banks.
+  // group for its own tiles: every thread loads 4 K and 4 V chunks of 16 bytes.
   const size_t slice = (static_cast<size_t>(b) * Hkv + g) * max_pos * DH;
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k_cache + slice, static_cast<uint32_t>(max_pos) * DH * 2u);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v_cache + slice, static_cast<uint32_t>(max_pos) * DH * 2u);
-  const bool stage_v = tid < 128;
-  const int st_t = tid & 127;
-  const int vkg = st_t & 7, vdg = st_t >> 3;      // V: slot group, dim group (16 of 8 dims)
-  const int kr = st_t >> 4, kc = st_t & 15;        // K: row (of 8 per pass), 16-byte chunk
-  uint4 sreg[8];
+  // V: thread (vkg, vdg) loads slots 4 vkg .. 4 vkg + 3 at dims 8 vdg .. 8 vdg + 7
+  // and writes them transposed as 8 rows (dims) of 4 slots, 8 bytes per row.
+  // K: thread (kr, kc) loads 16-byte chunk kc of rows kr + 16 i, i < 4.
+  // Every wave stages both, so the fp16 conversion work is spread evenly.
+  const int vkg = tid & 15, vdg = tid >> 4;
+  const int kr = tid >> 4, kc = tid & 15;
+  uint4 kreg[4], vreg[4];
   auto gload = [&](int j0) {
     const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j0) * DH * 2u);  // tile offset, uniform
-    if (stage_v) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sreg[i] = buf_load16(v_rs, ((8 * vkg + i) * DH + vdg * 8) * 2u, so);
-    } else {
+    for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(v_rs, ((4 * vkg + i) * DH + vdg * 8) * 2u, so);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sreg[i] = buf_load16(k_rs, ((kr + 8 * i) * DH + kc * 8) * 2u, so);
-    }
+    for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(k_rs, ((kr + 16 * i) * DH + kc * 8) * 2u, so);
   };
   auto lstore = [&](int st) {
-    if (stage_v) {
-      // V goes to LDS as fp16 (the P.V product runs in fp16 so that P keeps
-      // 11 significant bits in one operand)
-      uint32_t w[32];  // w[4 * slot + dim/2]
-      {
-        const uint32_t* wb = reinterpret_cast<const uint32_t*>(sreg);
+    // V goes to LDS as fp16 (the P.V product runs in fp16 so that P keeps
+    // 11 significant bits in one operand)
+    uint32_t w[16];  // w[4 * slot + dim/2]
+    {
+      const uint32_t* wb = reinterpret_cast<const uint32_t*>(vreg);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) w[i] = bf16x2_to_f16x2(wb[i]);
-      }
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-        uint4 o;
-        o.x = __builtin_amdgcn_perm(w[4 * 1 + (d >> 1)], w[4 * 0 + (d >> 1)], sel);
-        o.y = __builtin_amdgcn_perm(w[4 * 3 + (d >> 1)], w[4 * 2 + (d >> 1)], sel);
-        o.z = __builtin_amdgcn_perm(w[4 * 5 + (d >> 1)], w[4 * 4 + (d >> 1)], sel);
-        o.w = __builtin_amdgcn_perm(w[4 * 7 + (d >> 1)], w[4 * 6 + (d >> 1)], sel);
-        *reinterpret_cast<uint4*>(&Vt[grp][st][(vdg * 8 + d) * VSTR + 8 * vkg]) = o;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *reinterpret_cast<uint4*>(&Ks[grp][st][(kr + 8 * i) * KSTR + kc * 8]) = sreg[i];
+      for (int i = 0; i < 16; ++i) w[i] = bf16x2_to_f16x2(wb[i]);
     }
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
+      uint2 o;
+      o.x = __builtin_amdgcn_perm(w[4 * 1 + (d >> 1)], w[4 * 0 + (d >> 1)], sel);
+      o.y = __builtin_amdgcn_perm(w[4 * 3 + (d >> 1)], w[4 * 2 + (d >> 1)], sel);
+      *reinterpret_cast<uint2*>(&Vt[grp][st][(vdg * 8 + d) * VSTR + 4 * vkg]) = o;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&Ks[grp][st][(kr + 16 * i) * KSTR + kc * 8]) = kreg[i];
   };
 
   f32x16 oacc[4];
