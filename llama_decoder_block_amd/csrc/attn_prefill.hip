@@ -31,8 +31,11 @@
 // B operand of the next MFMA, O^T += V^T P^T, with no register shuffling.  V
 // is transposed to [dd][slot] while it is written to LDS.  P stays in fp32 in
 // the online softmax and is fed to the PV product in fp16 (11 significant bits
-// against bf16's 8), with V converted to fp16 as it is staged; the weights
-// carry a factor 2^15 so that small ones stay fp16 normals.
+// against bf16's 8), with V converted to fp16 as it is staged.  The weights
+// are taken against a reference max that moves only when a tile's max
+// exceeds it by more than 8 (log2 units), so the output is rarely rescaled,
+// and the row sum adds the same fp16 weights the product multiplies.  The
+// row-max exchange between the two lanes of a query is a permlane32 swap.
 // Query tiles are launched heaviest first across all heads and sequences (the
 // causal workload grows with the tile index).  Tiles that lie wholly above a wave's diagonal are skipped, and
 // the -inf mask is applied only on tiles that cross it.
@@ -237,16 +240,31 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
           }
           mt = fmaxf(mt, sacc[kb][r]);
         }
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-      // running max in log2 units; the scale is positive, so max and scaling commute
-      const float m_new = fmaxf(m_run, mt * scale_log2);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-      float lsum = 0.f;
-      // the weights carry a factor 2^15 (so does their sum, which cancels it):
-      // they stay fp16 normals down to 2^-29 of the row maximum, which is 1
-      const float m_sh = m_use - 15.f;
+      {  // lanes l and l ^ 32 hold the two halves of a query's slots
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      // Reference max m_run (log2 units; the scale is positive, so max and
+      // scaling commute).  It moves only when a tile's max exceeds it by more
+      // than 8, so the running output is rarely rescaled; the weights
+      // 2^(s - m_run + 7) then stay within 2^15 (fp16 range) and are fp16
+      // normals down to 2^-21 of the reference.  Output and sum carry the
+      // same factor, which the final division cancels.
+      const float m_tile = mt * scale_log2;
+      if (__any(m_tile > m_run + 8.f)) {  // wave-uniform
+        const float m_new = m_tile > m_run + 8.f ? m_tile : m_run;
+        const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);  // 0 from -inf
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
+        m_run = m_new;
+      }
+      const float m_sh = (m_run == -INFINITY ? 0.f : m_run) - 7.f;
+      // the row sum adds the fp16 weights the P.V product multiplies
+      const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
+      float lsum[2] = {0.f, 0.f};
       uint32_t ph[2][2][4];  // [kb][half][packed fp16 pair]
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -254,17 +272,11 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
         for (int r = 0; r < 16; r += 2) {
           const float p0 = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_sh));
           const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], scale_log2, -m_sh));
-          lsum += p0 + p1;
-          ph[kb][r >> 3][(r & 7) >> 1] = pack_f16x2(p0, p1);
+          const uint32_t pp = pack_f16x2(p0, p1);
+          ph[kb][r >> 3][(r & 7) >> 1] = pp;
+          lsum[kb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pp), ones, lsum[kb], false);
         }
-      l_run = l_run * alpha + lsum;
-      // once the running max settles alpha is 1 for the whole wave
-      if (!__all(alpha == 1.f)) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
-      }
+      l_run += lsum[0] + lsum[1];
       // O^T += V^T P^T over 4 blocks of 16 slots
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
