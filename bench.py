@@ -186,6 +186,37 @@ def bench_decode(lib, synth, steps, warmup):
             "step_ms_by_kernel_note": "separate untimed pass with HIP events around every step"}
 
 
+def measure_ceilings(lib, runs=5):
+    """What this GPU sustains, measured by the library's ceiling kernels: a
+    register-only MFMA loop (dense bf16) and a one-pass 2 GiB streaming read,
+    each the median of `runs` event-timed launches after a warm-up."""
+    import torch
+    stream = torch.cuda.current_stream()
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def timed(launch):
+        launch()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(runs):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            out = launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        return sorted(ms)[len(ms) // 2], out
+
+    mfma_ms, flops = timed(lambda: lib.llama_layer_ceiling_mfma(40000, sink))
+    buf = torch.arange(1 << 28, dtype=torch.int64, device="cuda")  # 2 GiB of distinct values
+    read_ms, _ = timed(lambda: lib.llama_layer_ceiling_read(buf, sink))
+    nbytes = buf.numel() * buf.element_size()
+    del buf
+    return {"mfma_loop_tflops": flops / (mfma_ms * 1e-3) / 1e12, "mfma_loop_ms": mfma_ms,
+            "stream_read_GBps": nbytes / (read_ms * 1e-3) / 1e9, "stream_read_bytes": nbytes,
+            "stream_read_ms": read_ms}
+
+
 def bench_other_configs(lib, synth, steps, warmup):
     """The other layer shapes, timed the same way (not the headline): the 7B
     shape with bidirectional attention (the encoder-style variant), 13B-shape
@@ -406,6 +437,13 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(lib, synth, args.decode_steps, 3)
+    # fractions of what this GPU sustains (the roofline above uses the published peaks)
+    ceil = measure_ceilings(lib)
+    ceil["prefill_layer_frac_of_mfma_loop"] = out["layer"]["tflops"] / ceil["mfma_loop_tflops"]
+    ceil["gate_up_frac_of_mfma_loop"] = gu_tflops / ceil["mfma_loop_tflops"]
+    if "decode" in out:
+        ceil["decode_frac_of_stream_read"] = out["decode"]["GBps"] / ceil["stream_read_GBps"]
+    out["ceilings"] = ceil
     if args.other_configs:
         out["other_configs"] = bench_other_configs(lib, synth, max(3, args.steps // 4), 2)
         out["other_configs"]["llama7b_generate"] = bench_generate(lib, synth)

@@ -167,6 +167,24 @@ int llama_layer_profile_read(llama_layer* layer, double* step_ms, int n_steps, l
 /* Name of step i (0 <= i < LLAMA_LAYER_STEPS), or "" for any other i. */
 const char* llama_layer_step_name(int step);
 
+/* ---- measurement aid: ceilings of this GPU ----
+ * Both launch one kernel on `stream` and return at once; the caller times
+ * them there (e.g. with events) and keeps the sink (4 bytes of device memory
+ * the kernels may write) alive until they finish.
+ * llama_layer_ceiling_mfma: every wavefront (8 per compute unit) issues
+ * n_iter rounds of 8 independent v_mfma_f32_32x32x16_bf16 on pseudo-random
+ * register operands (different for consecutive MFMAs), with no memory traffic;
+ * *flops (host) receives the flops issued,
+ * so flops / time is the dense bf16 matrix rate the GPU sustains.
+ * Errors: NULL, INVALID (n_iter < 1), HIP.
+ * llama_layer_ceiling_read: reads `bytes` of device memory at `buf` (16-byte
+ * aligned, bytes a positive multiple of 1024) once, the whole grid sweeping one
+ * contiguous front, so bytes / time is the HBM read rate it sustains (use a
+ * buffer well above the 256 MB of on-chip caches).
+ * Errors: NULL, INVALID, HIP. */
+int llama_layer_ceiling_mfma(int32_t n_iter, void* sink, double* flops, void* stream);
+int llama_layer_ceiling_read(const void* buf, uint64_t bytes, void* sink, void* stream);
+
 /* Static description of a status code. */
 const char* llama_layer_strerror(int status);
 

@@ -34,7 +34,8 @@ LLAMA_BF16 = 1
 
 EXPORTED = ("llama_layer_create", "llama_layer_prefill", "llama_layer_decode",
             "llama_layer_destroy", "llama_layer_strerror", "llama_layer_last_error",
-            "llama_layer_profile", "llama_layer_profile_read", "llama_layer_step_name")
+            "llama_layer_profile", "llama_layer_profile_read", "llama_layer_step_name",
+            "llama_layer_ceiling_mfma", "llama_layer_ceiling_read")
 EXPORTED_MODEL = ("llama_model_create", "llama_model_destroy", "llama_model_prefill",
                   "llama_model_decode", "llama_model_generate", "llama_sample")
 LLAMA_LAYER_STEPS = 7
@@ -105,6 +106,10 @@ def _load():
     lib.llama_layer_profile_read.restype = ctypes.c_int
     lib.llama_layer_step_name.argtypes = [ctypes.c_int]
     lib.llama_layer_step_name.restype = ctypes.c_char_p
+    lib.llama_layer_ceiling_mfma.argtypes = [i32, vp, ctypes.POINTER(ctypes.c_double), vp]
+    lib.llama_layer_ceiling_mfma.restype = ctypes.c_int
+    lib.llama_layer_ceiling_read.argtypes = [vp, ctypes.c_uint64, vp, vp]
+    lib.llama_layer_ceiling_read.restype = ctypes.c_int
     pp = ctypes.POINTER(vp)
     lib.llama_model_create.argtypes = [ctypes.POINTER(LlamaModelConfig), ctypes.POINTER(LlamaModelWeights),
                                        vp, ctypes.POINTER(vp)]
@@ -206,6 +211,22 @@ def llama_layer_profile_read(handle):
     _check(LIB.llama_layer_profile_read(handle, arr, LLAMA_LAYER_STEPS, ctypes.byref(calls)))
     names = [LIB.llama_layer_step_name(i).decode() for i in range(LLAMA_LAYER_STEPS)]
     return dict(zip(names, list(arr))), int(calls.value)
+
+
+def llama_layer_ceiling_mfma(n_iter: int, sink, stream=None) -> float:
+    """Launch the MFMA-loop ceiling kernel on `stream` (default: torch's
+    current stream); returns the flops it issues.  sink: a device tensor of at
+    least 4 bytes, kept alive until the kernel has run."""
+    flops = ctypes.c_double()
+    _check(LIB.llama_layer_ceiling_mfma(int(n_iter), sink.data_ptr(), ctypes.byref(flops), _stream_ptr(stream)))
+    return flops.value
+
+
+def llama_layer_ceiling_read(buf, sink, stream=None):
+    """Launch the streaming-read ceiling kernel over the device tensor `buf`
+    (all of its bytes) on `stream`."""
+    _check(LIB.llama_layer_ceiling_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                        _stream_ptr(stream)))
 
 
 class LlamaLayer:

@@ -145,3 +145,17 @@ def test_one_hip_runtime_in_the_process():
     maps = open("/proc/self/maps").read()
     runtimes = sorted(set(re.findall(r"/\S*libamdhip64\.so\S*", maps)))
     assert len(runtimes) == 1, runtimes
+
+
+def test_ceiling_probes_reject_bad_arguments():
+    """The ceiling entry points validate their arguments before any HIP call."""
+    fake = ctypes.c_void_p(4096)
+    flops = ctypes.c_double()
+    assert lib.LIB.llama_layer_ceiling_mfma(10, None, ctypes.byref(flops), None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_ceiling_mfma(10, fake, None, None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_ceiling_mfma(0, fake, ctypes.byref(flops), None) == lib.LLAMA_ERR_INVALID
+    assert lib.LIB.llama_layer_ceiling_read(None, 1024, fake, None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_ceiling_read(fake, 0, fake, None) == lib.LLAMA_ERR_INVALID
+    assert lib.LIB.llama_layer_ceiling_read(fake, 1000, fake, None) == lib.LLAMA_ERR_INVALID
+    assert lib.LIB.llama_layer_ceiling_read(fake, 1040, fake, None) == lib.LLAMA_ERR_INVALID
+    assert lib.LIB.llama_layer_ceiling_read(ctypes.c_void_p(4100), 1024, fake, None) == lib.LLAMA_ERR_INVALID
