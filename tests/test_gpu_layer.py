@@ -176,6 +176,79 @@ def test_decode_matches_prefill_of_one_more_token():
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_extreme_inputs(dtype):
+    """Rows of zeros, rows scaled by 1e-3 and by 1e3, and a sharp softmax (the
+    query and key weights scaled so the scores have a standard deviation near
+    10, which moves the attention's reference max often): a prefill over
+    several key tiles, then one decode step with extreme rows.  Each row
+    group is checked on its own scale (RMSNorm makes the layer's work scale
+    free, so a row scaled by s is held to s times the unit-scale gate)."""
+    from oracle import llama_oracle as O
+    if dtype == "bf16":
+        wl, sharpen = _wl(d=512, H=4, Hkv=2, f=1408, B=2, T=130, steps=1, seed=21), 7.0
+    else:
+        wl, sharpen = _wl(dtype="f32", d=64, H=4, Hkv=2, f=96, B=2, T=20, steps=1, seed=21), 20.0
+    print(f"case {dtype}", flush=True)
+    w = synth.make_weights(wl, DEV, random_gains=True)
+    for name in ("wq", "wk"):
+        w[name] = (w[name].float() * sharpen).to(w[name].dtype)
+    x = synth.make_x(wl, (wl.batch, wl.seq), device=DEV).float()
+    groups = {"zero": [(0, 5), (1, 0)], "x1e-3": [(0, 6), (0, 7), (0, 8)], "x1e3": [(1, 10), (1, 11), (1, 12)]}
+    for b, t in groups["zero"]:
+        x[b, t] = 0.0
+    for b, t in groups["x1e-3"]:
+        x[b, t] *= 1e-3
+    for b, t in groups["x1e3"]:
+        x[b, t] *= 1e3
+    x = x.to(synth.torch_dtype(wl))
+    special = {bt for v in groups.values() for bt in v}
+    groups["unscaled"] = [(b, t) for b in range(wl.batch) for t in range(wl.seq) if (b, t) not in special]
+    scale = {"zero": 1.0, "x1e-3": 1.0, "x1e3": 1e3, "unscaled": 1.0}
+    kc, vc = synth.make_cache(wl, DEV)
+    pos = synth.prefill_positions(wl.batch, wl.seq, device=DEV)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, wl.batch * wl.seq), w)
+    kc0, vc0 = kc.clone(), vc.clone()
+    y = layer.prefill(x, pos, kc, vc)
+    torch.cuda.synchronize()
+    w64 = G.oracle_weights(w)
+    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)
+    yg = G.f64(y)
+
+    def check(got, ref, what, s):
+        if dtype == "bf16":
+            G.assert_bf16_output(got / s, ref / s, what)
+        else:
+            G.assert_f32(got / s, ref / s, what)
+    for name, rows in groups.items():
+        idx = tuple(np.array(rows).T)
+        check(yg[idx], yo[idx], f"y, {name} rows", scale[name])
+    written = slice(0, wl.seq)
+    # the scores' spread the sharpening reaches (sequence 0, head 0, unscaled rows)
+    q0 = G.f64(x)[0, 9:40] @ G.f64(w["wq"])[:wl.head_dim].T
+    k0 = G.f64(x)[0, 9:40] @ G.f64(w["wk"])[:wl.head_dim].T
+    print(f"  score std ~ {np.std(q0 @ k0.T) / np.sqrt(wl.head_dim):.1f}", flush=True)
+    if dtype == "bf16":
+        fk, fv = G.kv_floors(x, w)
+        G.assert_bf16_storage(G.f64(kc)[:, :, written], ko[:, :, written], "K written", fk)
+        G.assert_bf16_storage(G.f64(vc)[:, :, written], vo[:, :, written], "V written", fv)
+    else:
+        G.assert_f32(G.f64(kc), ko, "K cache")
+        G.assert_f32(G.f64(vc), vo, "V cache")
+    # a decode step with a zero row and a 1e3-scaled row
+    xs = synth.make_x(wl, (wl.batch,), tensor_id=synth.TID_DECODE_BASE, device=DEV).float()
+    xs[0] = 0.0
+    xs[1] *= 1e3
+    xs = xs.to(synth.torch_dtype(wl))
+    p = wl.seq
+    ys = layer.decode(xs, torch.full((wl.batch,), p, dtype=torch.int32, device=DEV), kc, vc)
+    torch.cuda.synchronize()
+    yo_d, ko_d, vo_d = O.decoder_layer_decode(G.f64(xs), np.full(wl.batch, p), w64, ko, vo, n_heads=wl.n_heads,
+                                              n_kv_heads=wl.n_kv_heads, bf16_points=dtype == "bf16")
+    check(G.f64(ys)[0], yo_d[0], "decode y, zero row", 1.0)
+    check(G.f64(ys)[1], yo_d[1], "decode y, 1e3 row", 1e3)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_zero_output_projections_give_identity(dtype):
     wl = _wl(dtype=dtype, d=256 if dtype == "bf16" else 64, H=2 if dtype == "bf16" else 4, Hkv=2,
              f=384 if dtype == "bf16" else 96, B=2, T=70)
