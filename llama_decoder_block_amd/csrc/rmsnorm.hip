@@ -87,6 +87,44 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const TIn* __restrict_
   }
 }
 
+// Few rows (decode): one 256-thread workgroup per row, so a call of B rows
+// spreads over B CUs and each lane issues d / 2048 loads of the row (and of
+// the gain) instead of d / 512; the sum of squares goes through the four
+// waves' partial sums in LDS, added in a fixed order.  d % 2048 == 0; for 32
+// rows of 4096 the decode norm step went from ~10 to ~6.6 us (event timed).
+template <typename TIn, typename TG, typename TOut, int NV, bool FRAG>
+__global__ __launch_bounds__(256) void rmsnorm_row_kernel(const TIn* __restrict__ in, const TG* __restrict__ g,
+                                                          TOut* __restrict__ out, int d, float eps) {
+  __shared__ float part[4];
+  const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const TIn* x = in + static_cast<size_t>(row) * d;
+  float v[NV][8], gv[NV][8];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int vi = tid + j * 256;
+    load8(x + vi * 8, v[j]);
+    load8(g + vi * 8, gv[j]);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < NV; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
+  ss = warp_sum(ss);
+  if (lane == 0) part[wave] = ss;
+  __syncthreads();
+  ss = (part[0] + part[1]) + (part[2] + part[3]);
+  const float inv = rsqrtf(ss / static_cast<float>(d) + eps);
+  TOut* y = out + (FRAG ? 0 : static_cast<size_t>(row) * d);
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int vi = tid + j * 256;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[j][e] = gv[j][e] * (v[j][e] * inv);
+    store8(y + (FRAG ? frag_index(row, vi * 8, d) : vi * 8), v[j]);
+  }
+}
+
 // Any d: two passes over the row (the second read hits the cache).
 template <typename TIn, typename TG, typename TOut>
 __global__ __launch_bounds__(256) void rmsnorm_any_kernel(const TIn* __restrict__ in,
@@ -116,6 +154,24 @@ hipError_t dispatch(const void* in, const void* g, void* out, int rows, int d, f
   const TG* gg = static_cast<const TG*>(g);
   TOut* y = static_cast<TOut*>(out);
   const int nv = (d + 511) / 512;
+  if (rows <= 64 && d % 2048 == 0) {  // few rows: one workgroup per row
+    switch (d / 2048) {
+      case 1:
+        hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, 1, FRAG>), dim3(rows), block, 0, s, x, gg, y, d, eps);
+        return hipGetLastError();
+      case 2:
+        hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, 2, FRAG>), dim3(rows), block, 0, s, x, gg, y, d, eps);
+        return hipGetLastError();
+      case 4:
+        hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, 4, FRAG>), dim3(rows), block, 0, s, x, gg, y, d, eps);
+        return hipGetLastError();
+      case 8:
+        hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, 8, FRAG>), dim3(rows), block, 0, s, x, gg, y, d, eps);
+        return hipGetLastError();
+      default:
+        break;  // other widths take the one-wave-per-row kernel
+    }
+  }
   if (d % 8 == 0 && nv <= 16) {
     if (nv <= 8)
       hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 8, FRAG>), grid, block, 0, s, x, gg, y, rows, d, eps);
