@@ -157,6 +157,32 @@ def test_bf16_decode_steps(B, Hkv):
         G.assert_bf16_storage(G.f64(vc)[:, :, p], vo[:, :, p], f"decode step {s} V", fv)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_with_wide_rows(dtype):
+    """d = 2048: the calls of <= 64 rows normalise each row with a whole
+    workgroup (a separate RMSNorm kernel from the one-wave-per-row one)."""
+    from oracle import llama_oracle as O
+    wl = _wl(dtype=dtype, d=2048, H=16, Hkv=4, f=5632, B=3, T=20, steps=2, seed=23)
+    print(f"case {dtype}", flush=True)
+    w, x, kc, vc, pos, layer = _setup(wl, random_gains=True, max_tokens=3 * 20)
+    w64 = G.oracle_weights(w)
+    kc0, vc0 = kc.clone(), vc.clone()
+    layer.prefill(x, pos, kc, vc)
+    torch.cuda.synchronize()
+    _, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)
+    for s in range(wl.decode_steps):
+        p = wl.seq + s
+        xs = synth.make_x(wl, (wl.batch,), tensor_id=synth.TID_DECODE_BASE + s, device=DEV)
+        ys = layer.decode(xs, torch.full((wl.batch,), p, dtype=torch.int32, device=DEV), kc, vc)
+        torch.cuda.synchronize()
+        yo, ko, vo = O.decoder_layer_decode(G.f64(xs), np.full(wl.batch, p), w64, ko, vo, n_heads=wl.n_heads,
+                                            n_kv_heads=wl.n_kv_heads, bf16_points=dtype == "bf16")
+        if dtype == "bf16":
+            G.assert_bf16_output(G.f64(ys), yo, f"decode step {s} y")
+        else:
+            G.assert_f32(G.f64(ys), yo, f"decode step {s} y")
+
+
 def test_decode_matches_prefill_of_one_more_token():
     """Prefill T, decode token T == row T of a prefill of T+1 (within bf16)."""
     wl = _wl(d=512, H=4, Hkv=2, f=1408, B=2, T=81, seed=13)
