@@ -18,11 +18,12 @@
 // when positions are 0..T-1 and extends it to a prefill that continues a cache.
 //
 // gfx950 design.  One workgroup = 128 queries of one head; each of its 4
-// query wavefronts owns 32 queries.  When the whole grid fits in one round of
-// two workgroups per CU, the causal work is dominated by the longest query
-// tile's serial chain, so a second group of 4 wavefronts takes every other
-// K/V tile and the two running states (max, sum, O) are merged through LDS at
-// the end.  K/V tiles of 64 slots are staged in LDS (two
+// query wavefronts owns 32 queries.  When the grid holds at most two
+// workgroups per CU, the kernel time is set by the longest query tiles'
+// serial chains, so a second group of 4 wavefronts takes every other K/V tile
+// and the two running states (max, sum, O) are merged through LDS at the end;
+// such a workgroup needs 140 KB of LDS, so a CU runs one at a time and the
+// heaviest-first order balances the two rounds.  K/V tiles of 64 slots are staged in LDS (two
 // stages, register prefetch of the next tile).  Scores are computed
 // transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so each lane owns
 // one query: its row max / row sum need only a lane-pair exchange.  The K rows
@@ -79,8 +80,8 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 }
 
 // NGRP wave groups of 4 share the query tile and take every NGRP-th K/V tile
-// (NGRP = 2 halves the longest serial chain when the grid is a single round
-// of workgroups; with several rounds, two independent workgroups per CU
+// (NGRP = 2 halves the longest serial chains when the grid holds at most two
+// workgroups per CU; with more, two independent 4-wavefront workgroups per CU
 // overlap better)
 template <int NGRP>
 __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
@@ -360,7 +361,7 @@ hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf1
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidDevice;
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
-  if (n_wg <= 2 * n_cu)  // one round of two workgroups per CU
+  if (n_wg <= 2 * n_cu)  // few workgroups: halve each query tile's chain
     hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(512), 0, s, q, k_cache, v_cache, pos, o, o_frag, B, T,
                        n_heads, n_kv_heads, max_pos, bidir, scale_log2);
   else
