@@ -133,6 +133,9 @@ hipError_t launch_gemm_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, in
 hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, int K,
                               bf16_t* out, hipStream_t s);
 
+// compute units of the current device (256 if the query fails)
+int device_cu_count();
+
 // Weight-streaming versions of the same four GEMMs for M <= 64 tokens: A and
 // W both in fragment order (A holds ceil(M/32)*32 rows; rows >= M are never
 // written out, whatever they hold).  The SwiGLU output h is written in

@@ -310,13 +310,6 @@ hipError_t launch_tiled(const bf16_t* A, const bf16_t* Wp, int M, int N, int K, 
   return hipGetLastError();
 }
 
-int cu_count() {
-  int dev = 0, n_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
-    n_cu = 256;
-  return n_cu;
-}
-
 // rounds of one tile per CU for BM x BN tiles
 long rounds(int M, int N, int BM, int BN, int n_cu) {
   return ((static_cast<long>(M + BM - 1) / BM) * ((N + BN - 1) / BN) + n_cu - 1) / n_cu;
@@ -326,7 +319,7 @@ long rounds(int M, int N, int BM, int BN, int n_cu) {
 // the 13B / 70B o_proj and down shapes); take them when that wins after
 // rounding each choice up to whole rounds of one tile per CU.
 bool wide_resid_tiles(int M, int N) {
-  const int n_cu = cu_count();
+  const int n_cu = device_cu_count();
   return 8 * rounds(M, N, 128, 512, n_cu) < 5 * rounds(M, N, 128, 256, n_cu);
 }
 
@@ -334,10 +327,18 @@ bool wide_resid_tiles(int M, int N) {
 // work in ~1.2x its time (measured at the 13B and 70B shapes); the same
 // rounding rule decides.
 bool wide_qkv_tiles(int M, int N) {
-  const int n_cu = cu_count();
+  const int n_cu = device_cu_count();
   return 40 * rounds(M, N, 128, 512, n_cu) < 33 * rounds(M, N, 256, 192, n_cu);
 }
 }  // namespace
+
+int device_cu_count() {
+  int dev = 0, n_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu < 1)
+    n_cu = 256;
+  return n_cu;
+}
 
 hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, const QkvEpilogue& q, hipStream_t s) {
   EpiArgs ep{}; ep.qkv = q;
