@@ -110,6 +110,9 @@ typedef struct llama_layer llama_layer;
 /* Validate the config, allocate the handle's weights, RoPE table (cos and sin
  * of p * base^(-2i/dh), built in fp64 on the host) and scratch, and copy the
  * weights.  Blocks until the copies on `stream` are done.
+ * With the environment variable LLAMA_LAYER_CHECK=1 at creation, every later
+ * prefill/decode call of the handle first validates its positions on the
+ * device and waits for the result (a debug aid: it synchronises the stream).
  * Errors: NULL (any pointer), INVALID (non-positive sizes, H % Hkv != 0, odd
  * dh, non-finite eps/base), UNSUPPORTED (bf16 with dh != 128 or d, f not
  * multiples of 128), HIP, ALLOC. */
@@ -130,8 +133,13 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
  * bf16 precision: the attention multiplies its softmax weights (fp16, 11
  * significant bits) with the values converted to fp16, exact for value
  * entries within +-65504 (larger magnitudes saturate there).
- * Errors: NULL, INVALID (B or T < 1), CAPACITY (B*T > max_tokens or
- * T > max_pos), HIP (launch failure). */
+ * Positions are not otherwise validated: a token whose position is outside
+ * [0, max_pos) writes no cache slot and gets undefined output values (every
+ * access stays inside the buffers); repeated positions in a sequence give
+ * undefined values for the tokens involved.
+ * Errors: NULL, INVALID (B or T < 1; with LLAMA_LAYER_CHECK=1 also a
+ * position outside [0, max_pos) or repeated within its sequence), CAPACITY
+ * (B*T > max_tokens or T > max_pos), HIP (launch failure). */
 int llama_layer_prefill(llama_layer* layer, const void* x, void* y, const int32_t* positions,
                         int32_t B, int32_t T, void* k_cache, void* v_cache, void* stream);
 

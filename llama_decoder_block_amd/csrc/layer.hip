@@ -23,6 +23,8 @@
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include <algorithm>
 #include <string>
@@ -95,6 +97,7 @@ struct llama_layer {
   float* part = nullptr;  // split-K partials
   int part_seqs = 0;      // sequences the partial buffer holds at once
   SkinnyScratch sk{};     // split column groups of the weight-streaming GEMMs
+  int* check_flag = nullptr;  // LLAMA_LAYER_CHECK=1 at create: position validation result
   // per-step event timing (measurement aid)
   static constexpr int kRing = 256;
   bool prof_on = false;
@@ -132,7 +135,7 @@ void release(llama_layer* L) {
     for (auto& row : L->ev)
       for (auto& e : row) (void)hipEventDestroy(e);
   void* bufs[] = {L->wqkv, L->wo, L->wgu, L->wd, L->g1, L->g2, L->rope_cos, L->rope_sin,
-                  L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->sk.part, L->sk.cnt};
+                  L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->sk.part, L->sk.cnt, L->check_flag};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
 }
@@ -254,6 +257,8 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
   ALLOC_OR_FAIL(L->o, mt * nq * es);
   ALLOC_OR_FAIL(L->x1, mt * d * sizeof(float));
   ALLOC_OR_FAIL(L->h, mt * f * es);
+  if (const char* chk = getenv("LLAMA_LAYER_CHECK"); chk && strcmp(chk, "1") == 0)
+    ALLOC_OR_FAIL(L->check_flag, sizeof(int));
   if (cfg->dtype == LLAMA_BF16) {
     ALLOC_OR_FAIL(L->q, mt * nq * es);
     const int pf = part_floats(*cfg, &L->part_seqs);
@@ -339,11 +344,48 @@ void llama_layer_destroy(llama_layer* L) {
   delete L;
 }
 
+// Debug validation of the positions (LLAMA_LAYER_CHECK=1 when the handle is
+// created): bit 0 of *bad if a position lies outside [0, max_pos), bit 1 if
+// a position repeats within its sequence (token i against the earlier
+// tokens of its sequence: O(T^2) per sequence, a debug aid only).
+static __global__ void check_positions_kernel(const int32_t* __restrict__ pos, int B, int T, int max_pos, int* bad) {
+  const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= static_cast<long long>(B) * T) return;
+  const int p = pos[i];
+  if (p < 0 || p >= max_pos) {
+    atomicOr(bad, 1);
+    return;
+  }
+  for (long long j = i - i % T; j < i; ++j)
+    if (pos[j] == p) {
+      atomicOr(bad, 2);
+      return;
+    }
+}
+
+static int check_positions(llama_layer* L, const int32_t* pos, int B, int T, hipStream_t s) {
+  const long long n = static_cast<long long>(B) * T;
+  int bad = 0;
+  HIP_OR_RETURN(hipMemsetAsync(L->check_flag, 0, sizeof(int), s), "clear check flag");
+  hipLaunchKernelGGL(check_positions_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, pos, B, T,
+                     L->cfg.max_pos, L->check_flag);
+  HIP_OR_RETURN(hipGetLastError(), "position check launch");
+  HIP_OR_RETURN(hipMemcpyAsync(&bad, L->check_flag, sizeof(int), hipMemcpyDeviceToHost, s), "read check flag");
+  HIP_OR_RETURN(hipStreamSynchronize(s), "position check");
+  if (bad & 1) return fail(LLAMA_ERR_INVALID, "a position lies outside [0, max_pos = %d)", L->cfg.max_pos);
+  if (bad & 2) return fail(LLAMA_ERR_INVALID, "a position repeats within a sequence");
+  return LLAMA_OK;
+}
+
 static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos, int B, int T,
                      void* kc, void* vc, hipStream_t s) {
   const llama_layer_config& c = L->cfg;
   const int M = B * T;
   const int d = c.d_model, H = c.n_heads, Hkv = c.n_kv_heads, f = c.d_ff;
+  if (L->check_flag) {
+    const int st = check_positions(L, pos, B, T, s);
+    if (st != LLAMA_OK) return st;
+  }
 
   if (c.dtype == LLAMA_F32) {
     F32Layer F{};

@@ -72,6 +72,8 @@ def test_tiny_fp32_layer():
     dict(d=1024, H=8, Hkv=2, f=2816, B=1, T=1),       # single token prefill
     dict(d=512, H=4, Hkv=4, f=1408, B=1, T=64),       # 64 tokens: largest skinny call
     dict(d=512, H=4, Hkv=4, f=1408, B=1, T=65),       # 65 tokens: smallest tiled call
+    dict(d=512, H=4, Hkv=2, f=1408, B=1, T=127),      # one short of a 128-row tile
+    dict(d=512, H=4, Hkv=1, f=1408, B=1, T=1000),     # long ragged sequence, MQA
 ])
 def test_bf16_prefill_small(shape):
     wl = _wl(**shape)
@@ -328,6 +330,41 @@ def test_in_place_output():
     layer.prefill(x2, pos, kc, vc, y=x2)
     torch.cuda.synchronize()
     assert torch.equal(x2, y)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_position_check_mode(dtype, monkeypatch):
+    """LLAMA_LAYER_CHECK=1 at creation: calls with a position outside [0, max_pos)
+    or repeated within a sequence fail with INVALID before touching the cache;
+    valid calls give the same bits as a handle without the check."""
+    wl = _wl(dtype=dtype, d=256 if dtype == "bf16" else 64, H=2, Hkv=2, f=384 if dtype == "bf16" else 96,
+             B=2, T=8, steps=1)
+    print(f"case {wl}", flush=True)
+    w, x, kc, vc, pos, plain = _setup(wl)
+    monkeypatch.setenv("LLAMA_LAYER_CHECK", "1")
+    checked = lib.LlamaLayer(G.layer_config(lib, wl, wl.batch * wl.seq), w)
+    kc2, vc2 = kc.clone(), vc.clone()
+    y1 = plain.prefill(x, pos, kc, vc)
+    y2 = checked.prefill(x, pos, kc2, vc2)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(kc, kc2) and torch.equal(vc, vc2)
+    flat = pos.reshape(-1)
+    bad_cases = {"outside": (5, wl.max_pos), "negative": (9, -1), "repeats": (12, int(flat[10]))}
+    for what, (i, v) in bad_cases.items():
+        bad = pos.clone()
+        bad.view(-1)[i] = v
+        k0, v0 = kc2.clone(), vc2.clone()
+        with pytest.raises(lib.LlamaLayerError) as e:
+            checked.prefill(x, bad, kc2, vc2)
+        assert e.value.status == lib.LLAMA_ERR_INVALID, what
+        assert torch.equal(kc2, k0) and torch.equal(vc2, v0), what
+    # decode: one position per sequence
+    xd = synth.make_x(wl, (wl.batch,), tensor_id=100, device=DEV)
+    with pytest.raises(lib.LlamaLayerError) as e:
+        checked.decode(xd, torch.tensor([3, wl.max_pos], dtype=torch.int32, device=DEV), kc2, vc2)
+    assert e.value.status == lib.LLAMA_ERR_INVALID
+    checked.decode(xd, torch.tensor([wl.seq, wl.seq], dtype=torch.int32, device=DEV), kc2, vc2)
+    torch.cuda.synchronize()
 
 
 def test_capacity_and_alignment_errors():
