@@ -159,6 +159,30 @@ def test_bf16_decode_steps(B, Hkv):
         G.assert_bf16_storage(G.f64(vc)[:, :, p], vo[:, :, p], f"decode step {s} V", fv)
 
 
+@pytest.mark.parametrize("B", [3, 40, 64])
+def test_decode_gate_up_wider_than_the_grid(B):
+    """f = 8704: the gate/up projection has 272 column groups, more than the
+    CUs, so each workgroup of the weight-streaming GEMM streams a share that
+    spans parts of several groups (one or two 32-token blocks)."""
+    from oracle import llama_oracle as O
+    wl = _wl(d=512, H=4, Hkv=2, f=8704, B=B, T=9, steps=2, seed=29)
+    print(f"case B={B}", flush=True)
+    w, x, kc, vc, pos, layer = _setup(wl, random_gains=True, max_tokens=B * 9)
+    w64 = G.oracle_weights(w)
+    kc0, vc0 = kc.clone(), vc.clone()
+    layer.prefill(x, pos, kc, vc)
+    torch.cuda.synchronize()
+    _, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)
+    for s in range(wl.decode_steps):
+        p = wl.seq + s
+        xs = synth.make_x(wl, (B,), tensor_id=synth.TID_DECODE_BASE + s, device=DEV)
+        ys = layer.decode(xs, torch.full((B,), p, dtype=torch.int32, device=DEV), kc, vc)
+        torch.cuda.synchronize()
+        yo, ko, vo = O.decoder_layer_decode(G.f64(xs), np.full(B, p), w64, ko, vo, n_heads=wl.n_heads,
+                                            n_kv_heads=wl.n_kv_heads, bf16_points=True)
+        G.assert_bf16_output(G.f64(ys), yo, f"decode step {s} y")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_decode_with_wide_rows(dtype):
     """d = 2048: the calls of <= 64 rows normalise each row with a whole
