@@ -355,6 +355,25 @@ def cpu_baseline(wl, host, budget_s):
             break
         tp = min(wl.seq, tp * 2)
     tp, dt = last
+    # the same oracle limited to one thread, on a prefix sized the same way
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        t1 = 64
+        with threadpool_limits(limits=1):
+            while True:
+                t0 = time.perf_counter()
+                O.decoder_layer(x[:, :t1], pos[:, :t1], w64, kc0, kc0, n_heads=wl.n_heads,
+                                n_kv_heads=wl.n_kv_heads, eps=wl.rms_eps, rope_base=wl.rope_base)
+                d1 = time.perf_counter() - t0
+                log(f"cpu oracle, 1 thread: {t1} tokens in {d1:.2f} s")
+                if d1 >= budget_s / 6 or t1 >= tp:
+                    break
+                t1 = min(tp, t1 * 2)
+        one = {"value": wl.batch * t1 / d1, "unit": "tokens/s", "cores": 1,
+               "sample": f"first {t1} tokens, {d1:.2f} s"}
+    except ImportError:
+        pass
     cpu = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -364,7 +383,7 @@ def cpu_baseline(wl, host, budget_s):
     return {"value": wl.batch * tp / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"first {tp} of the {wl.seq} tokens of the llama7b_prefill layer call, plain "
                       f"fp64 numpy oracle, {dt:.2f} s",
-            "host_cpu": cpu, "host_logical_cpus": os.cpu_count()}
+            "host_cpu": cpu, "host_logical_cpus": os.cpu_count(), "one_thread": one}
 
 
 def main():
