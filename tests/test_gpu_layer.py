@@ -159,6 +159,37 @@ def test_bf16_decode_steps(B, Hkv):
         G.assert_bf16_storage(G.f64(vc)[:, :, p], vo[:, :, p], f"decode step {s} V", fv)
 
 
+@pytest.mark.parametrize("Hkv", [2, 4])
+def test_decode_with_ragged_cache_lengths(Hkv):
+    """One decode step where every sequence sits at a different position over a
+    random prior cache of 2048 slots (continuous batching): the short
+    sequences leave most split-K ranges of the attention empty."""
+    from oracle import llama_oracle as O
+    wl = _wl(d=512, H=4, Hkv=Hkv, f=1408, B=6, T=1, prior=2047, seed=31)
+    print(f"case Hkv={Hkv} max_pos={wl.max_pos}", flush=True)
+    w = synth.make_weights(wl, DEV, random_gains=True)
+    kc, vc = synth.make_cache(wl, DEV)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, wl.batch), w)
+    w64 = G.oracle_weights(w)
+    k64, v64 = G.f64(kc), G.f64(vc)
+    p = np.array([0, 5, 100, 1000, 2047, 1531])
+    xs = synth.make_x(wl, (wl.batch,), tensor_id=synth.TID_DECODE_BASE, device=DEV)
+    ys = layer.decode(xs, torch.tensor(p, dtype=torch.int32, device=DEV), kc, vc)
+    torch.cuda.synchronize()
+    yo, ko, vo = O.decoder_layer_decode(G.f64(xs), p, w64, k64, v64, n_heads=wl.n_heads,
+                                        n_kv_heads=wl.n_kv_heads, bf16_points=True)
+    G.assert_bf16_output(G.f64(ys), yo, "ragged decode y")
+    fk, fv = G.kv_floors(xs, w)
+    kg, vg = G.f64(kc), G.f64(vc)
+    for b in range(wl.batch):
+        G.assert_bf16_storage(kg[b, :, p[b]], ko[b, :, p[b]], f"K of sequence {b}", fk)
+        G.assert_bf16_storage(vg[b, :, p[b]], vo[b, :, p[b]], f"V of sequence {b}", fv)
+    # every other cache slot is untouched
+    kg[np.arange(wl.batch), :, p] = k64[np.arange(wl.batch), :, p]
+    vg[np.arange(wl.batch), :, p] = v64[np.arange(wl.batch), :, p]
+    assert np.array_equal(kg, k64) and np.array_equal(vg, v64)
+
+
 @pytest.mark.parametrize("B", [3, 40, 64])
 def test_decode_gate_up_wider_than_the_grid(B):
     """f = 8704: the gate/up projection has 272 column groups, more than the
