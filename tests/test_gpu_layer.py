@@ -159,13 +159,16 @@ def test_bf16_decode_steps(B, Hkv):
         G.assert_bf16_storage(G.f64(vc)[:, :, p], vo[:, :, p], f"decode step {s} V", fv)
 
 
-@pytest.mark.parametrize("Hkv", [2, 4])
-def test_decode_with_ragged_cache_lengths(Hkv):
+@pytest.mark.parametrize("dtype,Hkv", [("bf16", 2), ("bf16", 4), ("f32", 2)])
+def test_decode_with_ragged_cache_lengths(dtype, Hkv):
     """One decode step where every sequence sits at a different position over a
     random prior cache of 2048 slots (continuous batching): the short
     sequences leave most split-K ranges of the attention empty."""
     from oracle import llama_oracle as O
-    wl = _wl(d=512, H=4, Hkv=Hkv, f=1408, B=6, T=1, prior=2047, seed=31)
+    if dtype == "bf16":
+        wl = _wl(d=512, H=4, Hkv=Hkv, f=1408, B=6, T=1, prior=2047, seed=31)
+    else:
+        wl = _wl(dtype="f32", d=64, H=4, Hkv=Hkv, f=96, B=6, T=1, prior=2047, seed=31)
     print(f"case Hkv={Hkv} max_pos={wl.max_pos}", flush=True)
     w = synth.make_weights(wl, DEV, random_gains=True)
     kc, vc = synth.make_cache(wl, DEV)
@@ -177,13 +180,19 @@ def test_decode_with_ragged_cache_lengths(Hkv):
     ys = layer.decode(xs, torch.tensor(p, dtype=torch.int32, device=DEV), kc, vc)
     torch.cuda.synchronize()
     yo, ko, vo = O.decoder_layer_decode(G.f64(xs), p, w64, k64, v64, n_heads=wl.n_heads,
-                                        n_kv_heads=wl.n_kv_heads, bf16_points=True)
-    G.assert_bf16_output(G.f64(ys), yo, "ragged decode y")
-    fk, fv = G.kv_floors(xs, w)
+                                        n_kv_heads=wl.n_kv_heads, bf16_points=dtype == "bf16")
     kg, vg = G.f64(kc), G.f64(vc)
-    for b in range(wl.batch):
-        G.assert_bf16_storage(kg[b, :, p[b]], ko[b, :, p[b]], f"K of sequence {b}", fk)
-        G.assert_bf16_storage(vg[b, :, p[b]], vo[b, :, p[b]], f"V of sequence {b}", fv)
+    if dtype == "bf16":
+        G.assert_bf16_output(G.f64(ys), yo, "ragged decode y")
+        fk, fv = G.kv_floors(xs, w)
+        for b in range(wl.batch):
+            G.assert_bf16_storage(kg[b, :, p[b]], ko[b, :, p[b]], f"K of sequence {b}", fk)
+            G.assert_bf16_storage(vg[b, :, p[b]], vo[b, :, p[b]], f"V of sequence {b}", fv)
+    else:
+        G.assert_f32(G.f64(ys), yo, "ragged decode y")
+        for b in range(wl.batch):
+            G.assert_f32(kg[b, :, p[b]], ko[b, :, p[b]], f"K of sequence {b}")
+            G.assert_f32(vg[b, :, p[b]], vo[b, :, p[b]], f"V of sequence {b}")
     # every other cache slot is untouched
     kg[np.arange(wl.batch), :, p] = k64[np.arange(wl.batch), :, p]
     vg[np.arange(wl.batch), :, p] = v64[np.arange(wl.batch), :, p]
