@@ -98,6 +98,40 @@ def test_chunked_prefill_over_prior_cache(dtype):
     _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc)
 
 
+@pytest.mark.parametrize("dtype,T", [("bf16", 100), ("bf16", 20), ("f32", 9)])
+def test_chunked_prefill_with_a_different_start_per_sequence(dtype, T):
+    """Sequence 0 starts at position 0, sequence 1 continues its cache at 150
+    (tiled and weight-streaming shapes): causal limits differ per sequence."""
+    if dtype == "bf16":
+        wl = _wl(dtype="bf16", d=512, H=4, Hkv=2, f=1408, B=2, T=T, prior=150, seed=37)
+    else:
+        wl = _wl(dtype="f32", d=64, H=4, Hkv=2, f=96, B=2, T=T, prior=150, seed=37)
+    print(f"case {wl}", flush=True)
+    w, x, kc, vc, _, layer = _setup(wl)
+    pos = torch.stack([torch.arange(T), torch.arange(150, 150 + T)]).to(torch.int32).to(DEV)
+    kc0, vc0 = kc.clone(), vc.clone()
+    y = layer.prefill(x, pos, kc, vc)
+    torch.cuda.synchronize()
+    w64 = G.oracle_weights(w)
+    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)
+    kg, vg = G.f64(kc), G.f64(vc)
+    if dtype == "bf16":
+        G.assert_bf16_output(G.f64(y), yo, "y")
+        fk, fv = G.kv_floors(x, w)
+        for b, lo in ((0, 0), (1, 150)):
+            G.assert_bf16_storage(kg[b, :, lo:lo + T], ko[b, :, lo:lo + T], f"K written, sequence {b}", fk)
+            G.assert_bf16_storage(vg[b, :, lo:lo + T], vo[b, :, lo:lo + T], f"V written, sequence {b}", fv)
+    else:
+        G.assert_f32(G.f64(y), yo, "y")
+        G.assert_f32(kg, ko, "K cache")
+        G.assert_f32(vg, vo, "V cache")
+    # slots the call did not write are untouched
+    k0, v0 = G.f64(kc0), G.f64(vc0)
+    for b, lo in ((0, 0), (1, 150)):
+        np.testing.assert_array_equal(np.delete(kg[b], np.s_[lo:lo + T], axis=1), np.delete(k0[b], np.s_[lo:lo + T], axis=1))
+        np.testing.assert_array_equal(np.delete(vg[b], np.s_[lo:lo + T], axis=1), np.delete(v0[b], np.s_[lo:lo + T], axis=1))
+
+
 @pytest.mark.parametrize("shape", [
     dict(dtype="bf16", d=512, H=4, Hkv=2, f=1408, B=2, T=300),             # tiled GEMMs, ragged query tile
     dict(dtype="bf16", d=256, H=2, Hkv=2, f=384, B=3, T=5),                # weight-streaming GEMMs
