@@ -165,12 +165,15 @@ def test_attention_with_several_workgroup_rounds(bidirectional):
     G.assert_bf16_output(G.f64(y).reshape(-1, wl.d_model)[rows], yo.reshape(-1, wl.d_model)[rows], "y rows")
 
 
-@pytest.mark.parametrize("B,Hkv", [(5, 2), (1, 1), (40, 4)])
-def test_bf16_decode_steps(B, Hkv):
+@pytest.mark.parametrize("B,H,Hkv", [(5, 4, 2), (1, 4, 1), (40, 4, 4),
+                                     # query heads per kv head 3, 5, 6, 7: every decode
+                                     # attention width below 8 (5 and up: one workgroup per CU)
+                                     (3, 3, 1), (3, 10, 2), (2, 6, 1), (4, 14, 2)])
+def test_bf16_decode_steps(B, H, Hkv):
     """Prefill 37 tokens, then 3 decode steps; each step checked against the
     oracle continuing from its own cache."""
-    wl = _wl(d=512, H=4, Hkv=Hkv, f=1408, B=B, T=37, steps=3, seed=11)
-    print(f"case B={B} Hkv={Hkv}", flush=True)
+    wl = _wl(d=512, H=H, Hkv=Hkv, f=1408, B=B, T=37, steps=3, seed=11)
+    print(f"case B={B} H={H} Hkv={Hkv}", flush=True)
     w, x, kc, vc, pos, layer = _setup(wl, max_tokens=B * 37)
     w64 = G.oracle_weights(w)
     kc0, vc0 = kc.clone(), vc.clone()
