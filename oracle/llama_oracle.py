@@ -173,7 +173,7 @@ def _f64(a):
 
 def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_heads,
                   eps=1e-6, rope_base=10000.0, bf16_points=False, rows=None,
-                  bidirectional=False):
+                  bidirectional=False, kv_exact=None):
     """One pre-norm decoder layer forward over B sequences with a KV cache.
 
         X'  = x  + o_proj(CausalAttn(RoPE(q, k), v))      q,k,v = proj(RMSNorm1(x))
@@ -194,6 +194,11 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
                new token of sequence b sees every slot up to the largest
                position among the sequence's new tokens.  [LARQL: the SigLIP
                encoder's attention is the causal one without the mask.]
+    kv_exact   optional dict; receives "k" and "v" [B, Hkv, T, dh], the new
+               tokens' rotated keys and values before the cache dtype's
+               rounding (in the bf16 points mode they are computed from the
+               rounded normalised activations; the cache holds their bf16
+               rounding).  Token (b, t) is [b, :, t].
 
     Returns (y [B, T, d] (rows not asked for are NaN), k_cache', v_cache').
     """
@@ -215,7 +220,10 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
     v = xn @ W["wv"].T
     k = k.reshape(B, T, Hkv, dh).transpose(0, 2, 1, 3)               # [B,Hkv,T,dh]
     v = v.reshape(B, T, Hkv, dh).transpose(0, 2, 1, 3)
-    k = r(rope(k, pos[:, None, :], rope_base))
+    k = rope(k, pos[:, None, :], rope_base)
+    if kv_exact is not None:
+        kv_exact["k"], kv_exact["v"] = k.copy(), v.copy()
+    k = r(k)
     v = r(v)
     for b in range(B):
         kc[b][:, pos[b], :] = k[b]

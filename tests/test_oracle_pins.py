@@ -230,12 +230,39 @@ def _tiny(seed, B=2, T=6, d=32, H=4, Hkv=2, f=48, S=None, gains=True):
     return x, w, kc, vc
 
 
-def _torch_layer(x, pos, w, kc, vc, H, Hkv, eps=1e-6, base=10000.0, bidirectional=False):
+def _bf16_torch(a):
+    """fp64 -> bf16 (round to nearest, ties to even) with torch's own
+    conversions, as an independent check of the oracle's frexp/rint rounding.
+
+    torch converts fp64 to bf16 through fp32, and rounding twice can differ
+    from rounding once (a value just off a bf16 midpoint can land on it in
+    fp32).  Rounding to fp32 *to odd* first makes the second rounding exact:
+    Boldo and Melquiond, "Emulation of FMA and correctly rounded sums: proved
+    algorithms using rounding to odd" (IEEE Trans. Computers, 2008), which
+    needs at least two more bits in the intermediate format (fp32 has 24,
+    bf16 8).  Round to odd keeps exact values and otherwise takes, of the two
+    fp32 neighbours of the value, the one whose last significand bit is 1."""
+    a = torch.as_tensor(a, dtype=torch.float64)
+    f = a.to(torch.float32)                        # nearest fp32
+    back = f.to(torch.float64)
+    inexact = back != a
+    even = (f.view(torch.int32) & 1) == 0
+    away = torch.where(back < a, torch.full_like(f, math.inf), torch.full_like(f, -math.inf))
+    odd = torch.where(inexact & even, torch.nextafter(f, away), f)
+    return odd.to(torch.bfloat16).to(torch.float64)
+
+
+def _torch_layer(x, pos, w, kc, vc, H, Hkv, eps=1e-6, base=10000.0, bidirectional=False,
+                 rnd=None, kv_exact=None):
     """Independent fp64 re-derivation from library routines: F.rms_norm,
     F.linear, RoPE as complex multiplication, SDPA with enable_gqa and an
     explicit boolean position mask (bidirectional: every new token of a
-    sequence sees the slots up to the sequence's largest new position), F.silu."""
+    sequence sees the slots up to the sequence's largest new position), F.silu.
+    rnd (default: none) is applied at the bf16 layer's rounding points: the
+    normalised activations, q and k after RoPE, v, the attention output and
+    the SwiGLU product."""
     t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))  # noqa: E731
+    r = rnd or (lambda a: a)  # noqa: E731
     x, kc, vc = t(x), t(kc).clone(), t(vc).clone()
     W = {k: t(v) for k, v in w.items()}
     B, T, d = x.shape
@@ -248,11 +275,14 @@ def _torch_layer(x, pos, w, kc, vc, H, Hkv, eps=1e-6, base=10000.0, bidirectiona
         z = torch.complex(a[..., : dh // 2], a[..., dh // 2:]) * torch.exp(1j * ang)
         return torch.cat([z.real, z.imag], dim=-1)
 
-    xn = F.rms_norm(x, (d,), W["attn_norm"], eps)
+    xn = r(F.rms_norm(x, (d,), W["attn_norm"], eps))
     q = F.linear(xn, W["wq"]).view(B, T, H, dh).transpose(1, 2)
     k = F.linear(xn, W["wk"]).view(B, T, Hkv, dh).transpose(1, 2)
     v = F.linear(xn, W["wv"]).view(B, T, Hkv, dh).transpose(1, 2)
-    q, k = rot(q, pos), rot(k, pos)
+    q, k = r(rot(q, pos)), rot(k, pos)
+    if kv_exact is not None:
+        kv_exact["k"], kv_exact["v"] = k.numpy().copy(), v.numpy().copy()
+    k, v = r(k), r(v)
     for b in range(B):
         kc[b, :, pos[b]] = k[b]
         vc[b, :, pos[b]] = v[b]
@@ -260,9 +290,11 @@ def _torch_layer(x, pos, w, kc, vc, H, Hkv, eps=1e-6, base=10000.0, bidirectiona
     lim = pos.max(dim=1, keepdim=True).values.expand(B, T) if bidirectional else pos
     allowed = torch.arange(S)[None, None, :] <= lim[:, :, None]      # [B, T, S]
     o = F.scaled_dot_product_attention(q, kc, vc, attn_mask=allowed[:, None], enable_gqa=True)
-    x1 = x + F.linear(o.transpose(1, 2).reshape(B, T, H * dh), W["wo"])
-    xn2 = F.rms_norm(x1, (d,), W["ffn_norm"], eps)
-    y = x1 + F.linear(F.silu(F.linear(xn2, W["w_gate"])) * F.linear(xn2, W["w_up"]), W["w_down"])
+    o = r(o.transpose(1, 2).reshape(B, T, H * dh))
+    x1 = x + F.linear(o, W["wo"])
+    xn2 = r(F.rms_norm(x1, (d,), W["ffn_norm"], eps))
+    h = r(F.silu(F.linear(xn2, W["w_gate"])) * F.linear(xn2, W["w_up"]))
+    y = x1 + F.linear(h, W["w_down"])
     return y.numpy(), kc.numpy(), vc.numpy()
 
 
@@ -395,3 +427,77 @@ def test_bf16_points_mode_is_close_but_rounded():
     np.testing.assert_array_equal(O.bf16_round(vb), vb)
     rms = np.sqrt(np.mean(y * y))
     assert 0 < np.max(np.abs(yb - y)) < 0.05 * rms
+
+
+# ------------------------------------------------- the bf16 rounding-point mode
+
+def test_bf16_torch_rounding_helper_is_correct_rounding():
+    """The test's own fp64 -> bf16 route (round to odd, then torch's fp32 ->
+    bf16) against the exact midpoint cases where rounding twice would go wrong,
+    and against torch's fp32 -> bf16 on values fp32 holds exactly."""
+    # 1 + 2^-8 is the midpoint of 1 and 1 + 2^-7; a hair above it must round up,
+    # though its fp32 rounding (1 + 2^-8 exactly) would round to even (down)
+    vals = torch.tensor([1 + 2**-8 + 2**-40, 1 + 2**-8 - 2**-40, 1 + 2**-8, 1 + 3 * 2**-8,
+                         -(1 + 2**-8 + 2**-40)], dtype=torch.float64)
+    want = torch.tensor([1 + 2**-7, 1.0, 1.0, 1 + 2**-6, -(1 + 2**-7)], dtype=torch.float64)
+    assert torch.equal(_bf16_torch(vals), want)
+    x = torch.randn(100000, dtype=torch.float32, generator=torch.Generator().manual_seed(3))
+    assert torch.equal(_bf16_torch(x.double()), x.to(torch.bfloat16).double())
+
+
+def _bf16_case(seed=61, B=1, T=7, H=4, Hkv=2, prior=0):
+    x, w, kc, vc = _tiny(seed, B=B, T=T, H=H, Hkv=Hkv, S=prior + T + 2)
+    if prior:
+        rng = _rng(seed + 1)
+        kc[:, :, :prior] = O.bf16_round(rng.standard_normal(kc[:, :, :prior].shape))
+        vc[:, :, :prior] = O.bf16_round(rng.standard_normal(vc[:, :, :prior].shape))
+    pos = np.tile(np.arange(prior, prior + T), (B, 1))
+    return x, w, kc, vc, pos
+
+
+@pytest.mark.parametrize("B,H,Hkv,prior", [(1, 4, 2, 0), (2, 4, 4, 0), (2, 4, 1, 5)])
+def test_bf16_points_mode_matches_library_rederivation(B, H, Hkv, prior):
+    """The rounding-point mode (the reference of every bf16 comparison) against
+    the torch re-derivation with an independent bf16 rounding (_bf16_torch) at
+    the same seven points: xn, q, k, v, the attention output, xn2 and h.
+    Agreement to 1e-12: the two sides' pre-rounding values differ only by fp64
+    evaluation order (~1e-16 relative), so they round differently only for a
+    value within that distance of a bf16 midpoint (a tie; none occurs in these
+    seeded cases, about 1e-13 per element)."""
+    x, w, kc, vc, pos = _bf16_case(61 + 7 * B + Hkv + prior, B=B, H=H, Hkv=Hkv, prior=prior)
+    ex, exr = {}, {}
+    y, k2, v2 = O.decoder_layer(x, pos, w, kc, vc, n_heads=H, n_kv_heads=Hkv, bf16_points=True,
+                                kv_exact=ex)
+    yr, kr, vr = _torch_layer(x, pos, w, kc, vc, H, Hkv, rnd=_bf16_torch, kv_exact=exr)
+    np.testing.assert_allclose(y, yr, rtol=0, atol=1e-12)
+    np.testing.assert_array_equal(k2, kr)
+    np.testing.assert_array_equal(v2, vr)
+    np.testing.assert_allclose(ex["k"], exr["k"], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ex["v"], exr["v"], rtol=0, atol=1e-12)
+    # the cache holds the rounding of the exact values, and the rounding moved them
+    for b in range(B):
+        np.testing.assert_array_equal(k2[b][:, pos[b]], O.bf16_round(ex["k"][b]))
+    assert np.max(np.abs(k2[:, :, prior:prior + x.shape[1]] - ex["k"])) > 0
+
+
+_ROUNDING_POINTS = ("xn", "k", "v", "q", "o", "xn2", "h")  # the order decoder_layer rounds them in (B = 1)
+
+
+@pytest.mark.parametrize("dropped", range(len(_ROUNDING_POINTS)), ids=list(_ROUNDING_POINTS))
+def test_bf16_points_pin_catches_a_dropped_rounding(dropped, monkeypatch):
+    """Planted mistakes in the oracle: skipping any one of its seven bf16
+    rounding points makes it disagree with the re-derivation above (in y or
+    in the cache), so the pin covers every point."""
+    x, w, kc, vc, pos = _bf16_case(61 + 7 + 2)
+    yr, kr, vr = _torch_layer(x, pos, w, kc, vc, 4, 2, rnd=_bf16_torch)
+    real = O._maybe_round
+    calls = []
+
+    def mutant(a, bf16_points):
+        calls.append(len(calls))
+        return a if len(calls) - 1 == dropped else real(a, bf16_points)
+    monkeypatch.setattr(O, "_maybe_round", mutant)
+    y, k2, v2 = O.decoder_layer(x, pos, w, kc, vc, n_heads=4, n_kv_heads=2, bf16_points=True)
+    assert len(calls) == len(_ROUNDING_POINTS)
+    diff = max(np.max(np.abs(y - yr)), np.max(np.abs(k2 - kr)), np.max(np.abs(v2 - vr)))
+    assert diff > 1e-6, f"dropping the rounding of {_ROUNDING_POINTS[dropped]} went unnoticed ({diff})"
