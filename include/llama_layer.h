@@ -114,8 +114,8 @@ typedef struct llama_layer llama_layer;
  * prefill/decode call of the handle first validates its positions on the
  * device and waits for the result (a debug aid: it synchronises the stream).
  * Errors: NULL (any pointer), INVALID (non-positive sizes, H % Hkv != 0, odd
- * dh, non-finite eps/base), UNSUPPORTED (bf16 with dh != 128 or d, f not
- * multiples of 128), HIP, ALLOC. */
+ * dh, non-finite eps/base), UNSUPPORTED (bf16 with dh != 128, d or f not
+ * multiples of 128, or d above 8192 other than 16384), HIP, ALLOC. */
 int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights* w,
                        void* stream, llama_layer** out);
 

@@ -33,9 +33,9 @@
 // is transposed to [dd][slot] while it is written to LDS.  P stays in fp32 in
 // the online softmax and is fed to the PV product in fp16 (11 significant bits
 // against bf16's 8), with V converted to fp16 as it is staged.  The weights
-// are taken against a reference max that moves only when a tile's max
-// exceeds it by more than 8 (log2 units), so the output is rarely rescaled,
-// and the row sum adds the same fp16 weights the product multiplies.  The
+// are taken against the running max (the output is rescaled only when some
+// query's max moves), and the row sum adds the same fp16 weights the product
+// multiplies.  The
 // row-max exchange between the two lanes of a query is a permlane32 swap.
 // Query tiles are launched heaviest first across all heads and sequences (the
 // causal workload grows with the tile index).  Tiles that lie wholly above a wave's diagonal are skipped, and
@@ -245,15 +245,14 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
         mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
-      // Reference max m_run (log2 units; the scale is positive, so max and
-      // scaling commute).  It moves only when a tile's max exceeds it by more
-      // than 8, so the running output is rarely rescaled; the weights
-      // 2^(s - m_run + 7) then stay within 2^15 (fp16 range) and are fp16
-      // normals down to 2^-21 of the reference.  Output and sum carry the
-      // same factor, which the final division cancels.
+      // Running max m_run (log2 units; the scale is positive, so max and
+      // scaling commute).  The weights 2^(s - m_run + 7) stay within 2^7 and
+      // are fp16 normals down to 2^-21 of the max.  Output and sum carry the
+      // same factor 2^7, which the final division cancels.  The rescale is
+      // skipped when no query of the wave has a new max.
       const float m_tile = mt * scale_log2;
-      if (__any(m_tile > m_run + 8.f)) {  // wave-uniform
-        const float m_new = m_tile > m_run + 8.f ? m_tile : m_run;
+      if (__any(m_tile > m_run)) {  // wave-uniform
+        const float m_new = fmaxf(m_tile, m_run);
         const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);  // 0 from -inf
         l_run *= alpha;
 #pragma unroll

@@ -166,6 +166,10 @@ int check_config(const llama_layer_config* c) {
     if (c->head_dim != 128) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 kernels need head_dim 128");
     if (c->d_model % 128 || c->d_ff % 128)
       return fail(LLAMA_ERR_UNSUPPORTED, "bf16 kernels need d_model and d_ff multiples of 128");
+    // calls of <= 64 tokens normalise into fragment order: one wavefront per
+    // row up to d = 8192, a workgroup per row at d = 16384 (2048 x 8)
+    if (c->d_model > 8192 && c->d_model != 16384)
+      return fail(LLAMA_ERR_UNSUPPORTED, "bf16 kernels need d_model <= 8192 or d_model = 16384");
     // kernels address every operand with 32-bit byte offsets
     const double lim = 4294967295.0;
     const double d = c->d_model, f = c->d_ff, qd = 128.0 * c->n_heads,

@@ -103,6 +103,8 @@ def _cfg(**kw):
     (dict(head_dim=64), lib.LLAMA_ERR_UNSUPPORTED),                  # bf16 needs dh 128
     (dict(d_ff=1400), lib.LLAMA_ERR_UNSUPPORTED),                    # bf16 needs f % 128 == 0
     (dict(d_model=520), lib.LLAMA_ERR_UNSUPPORTED),
+    (dict(d_model=10240, n_heads=80, n_kv_heads=8), lib.LLAMA_ERR_UNSUPPORTED),  # no fragment-order norm
+    (dict(d_model=12288, n_heads=96, n_kv_heads=8), lib.LLAMA_ERR_UNSUPPORTED),
 ])
 def test_create_rejects_bad_configs(kw, status):
     st, h = _create(_cfg(**kw), _weights())

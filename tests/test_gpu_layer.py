@@ -34,14 +34,14 @@ def _setup(wl, random_gains=False, max_tokens=None, bidirectional=False):
 def _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc, bidirectional=False):
     torch.cuda.synchronize()
     w64 = G.oracle_weights(w)
-    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0, bidirectional=bidirectional)
+    ex = {}
+    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0, bidirectional=bidirectional, kv_exact=ex)
     written = slice(wl.prior, wl.prior + wl.seq)
     kg, vg = G.f64(kc), G.f64(vc)
     if wl.dtype == "bf16":
         G.assert_bf16_output(G.f64(y), yo, "y")
-        fk, fv = G.kv_floors(x, w)
-        G.assert_bf16_storage(kg[:, :, written], ko[:, :, written], "K written", fk)
-        G.assert_bf16_storage(vg[:, :, written], vo[:, :, written], "V written", fv)
+        G.assert_bf16_cache(kg[:, :, written], ex["k"], ko[:, :, written], "K written")
+        G.assert_bf16_cache(vg[:, :, written], ex["v"], vo[:, :, written], "V written")
         yp, _, _ = G.oracle_prefill(wl, w64, x, pos, kc0, vc0, bf16_points=False, bidirectional=bidirectional)
         print(f"  (vs plain oracle: y max|err|/rms = {G.rel_err(G.f64(y), yp):.5f})")
     else:
@@ -113,14 +113,14 @@ def test_chunked_prefill_with_a_different_start_per_sequence(dtype, T):
     y = layer.prefill(x, pos, kc, vc)
     torch.cuda.synchronize()
     w64 = G.oracle_weights(w)
-    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)
+    ex = {}
+    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0, kv_exact=ex)
     kg, vg = G.f64(kc), G.f64(vc)
     if dtype == "bf16":
         G.assert_bf16_output(G.f64(y), yo, "y")
-        fk, fv = G.kv_floors(x, w)
         for b, lo in ((0, 0), (1, 150)):
-            G.assert_bf16_storage(kg[b, :, lo:lo + T], ko[b, :, lo:lo + T], f"K written, sequence {b}", fk)
-            G.assert_bf16_storage(vg[b, :, lo:lo + T], vo[b, :, lo:lo + T], f"V written, sequence {b}", fv)
+            G.assert_bf16_cache(kg[b, :, lo:lo + T], ex["k"][b], ko[b, :, lo:lo + T], f"K written, sequence {b}")
+            G.assert_bf16_cache(vg[b, :, lo:lo + T], ex["v"][b], vo[b, :, lo:lo + T], f"V written, sequence {b}")
     else:
         G.assert_f32(G.f64(y), yo, "y")
         G.assert_f32(kg, ko, "K cache")
@@ -187,26 +187,31 @@ def test_bf16_decode_steps(B, H, Hkv):
         ps = torch.full((B,), p, dtype=torch.int32, device=DEV)
         ys = layer.decode(xs, ps, kc, vc)
         torch.cuda.synchronize()
+        ex = {}
         yo, ko, vo = O.decoder_layer_decode(G.f64(xs), np.full(B, p), w64, ko, vo,
                                             n_heads=wl.n_heads, n_kv_heads=wl.n_kv_heads,
-                                            bf16_points=True)
+                                            bf16_points=True, kv_exact=ex)
         G.assert_bf16_output(G.f64(ys), yo, f"decode step {s} y")
-        fk, fv = G.kv_floors(xs, w)
-        G.assert_bf16_storage(G.f64(kc)[:, :, p], ko[:, :, p], f"decode step {s} K", fk)
-        G.assert_bf16_storage(G.f64(vc)[:, :, p], vo[:, :, p], f"decode step {s} V", fv)
+        G.assert_bf16_cache(G.f64(kc)[:, :, p], ex["k"][:, :, 0], ko[:, :, p], f"decode step {s} K")
+        G.assert_bf16_cache(G.f64(vc)[:, :, p], ex["v"][:, :, 0], vo[:, :, p], f"decode step {s} V")
 
 
-@pytest.mark.parametrize("dtype,Hkv", [("bf16", 2), ("bf16", 4), ("f32", 2)])
-def test_decode_with_ragged_cache_lengths(dtype, Hkv):
+@pytest.mark.parametrize("dtype,H,Hkv", [("bf16", 4, 2), ("bf16", 4, 4), ("f32", 4, 2),
+                                          # 3 .. 8 query heads per kv head: every width of
+                                          # the decode attention kernel over several of its
+                                          # loop iterations (the prefetch hand-off)
+                                          ("bf16", 6, 2), ("bf16", 8, 2), ("bf16", 10, 2),
+                                          ("bf16", 12, 2), ("bf16", 14, 2), ("bf16", 16, 2)])
+def test_decode_with_ragged_cache_lengths(dtype, H, Hkv):
     """One decode step where every sequence sits at a different position over a
     random prior cache of 2048 slots (continuous batching): the short
     sequences leave most split-K ranges of the attention empty."""
     from oracle import llama_oracle as O
     if dtype == "bf16":
-        wl = _wl(d=512, H=4, Hkv=Hkv, f=1408, B=6, T=1, prior=2047, seed=31)
+        wl = _wl(d=128 * H, H=H, Hkv=Hkv, f=1408, B=6, T=1, prior=2047, seed=31 + H)
     else:
-        wl = _wl(dtype="f32", d=64, H=4, Hkv=Hkv, f=96, B=6, T=1, prior=2047, seed=31)
-    print(f"case Hkv={Hkv} max_pos={wl.max_pos}", flush=True)
+        wl = _wl(dtype="f32", d=64, H=H, Hkv=Hkv, f=96, B=6, T=1, prior=2047, seed=31)
+    print(f"case {dtype} H={H} Hkv={Hkv} max_pos={wl.max_pos}", flush=True)
     w = synth.make_weights(wl, DEV, random_gains=True)
     kc, vc = synth.make_cache(wl, DEV)
     layer = lib.LlamaLayer(G.layer_config(lib, wl, wl.batch), w)
@@ -216,15 +221,15 @@ def test_decode_with_ragged_cache_lengths(dtype, Hkv):
     xs = synth.make_x(wl, (wl.batch,), tensor_id=synth.TID_DECODE_BASE, device=DEV)
     ys = layer.decode(xs, torch.tensor(p, dtype=torch.int32, device=DEV), kc, vc)
     torch.cuda.synchronize()
+    ex = {}
     yo, ko, vo = O.decoder_layer_decode(G.f64(xs), p, w64, k64, v64, n_heads=wl.n_heads,
-                                        n_kv_heads=wl.n_kv_heads, bf16_points=dtype == "bf16")
+                                        n_kv_heads=wl.n_kv_heads, bf16_points=dtype == "bf16", kv_exact=ex)
     kg, vg = G.f64(kc), G.f64(vc)
+    bi = np.arange(wl.batch)
     if dtype == "bf16":
         G.assert_bf16_output(G.f64(ys), yo, "ragged decode y")
-        fk, fv = G.kv_floors(xs, w)
-        for b in range(wl.batch):
-            G.assert_bf16_storage(kg[b, :, p[b]], ko[b, :, p[b]], f"K of sequence {b}", fk)
-            G.assert_bf16_storage(vg[b, :, p[b]], vo[b, :, p[b]], f"V of sequence {b}", fv)
+        G.assert_bf16_cache(kg[bi, :, p], ex["k"][:, :, 0], ko[bi, :, p], "K of every sequence")
+        G.assert_bf16_cache(vg[bi, :, p], ex["v"][:, :, 0], vo[bi, :, p], "V of every sequence")
     else:
         G.assert_f32(G.f64(ys), yo, "ragged decode y")
         for b in range(wl.batch):
@@ -340,7 +345,8 @@ def test_extreme_inputs(dtype):
     y = layer.prefill(x, pos, kc, vc)
     torch.cuda.synchronize()
     w64 = G.oracle_weights(w)
-    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)
+    ex = {}
+    yo, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0, kv_exact=ex)
     yg = G.f64(y)
 
     def check(got, ref, what, s):
@@ -348,6 +354,11 @@ def test_extreme_inputs(dtype):
             G.assert_bf16_output(got / s, ref / s, what)
         else:
             G.assert_f32(got / s, ref / s, what)
+    # a zero row at position 0 sees only itself, whose key and value are
+    # zero: every step maps zeros to zeros, so its y is exactly zero on both
+    # sides (it is checked on its own, as its RMS is zero)
+    assert np.all(yo[1, 0] == 0.0) and np.all(yg[1, 0] == 0.0)
+    groups["zero"] = [(0, 5)]
     for name, rows in groups.items():
         idx = tuple(np.array(rows).T)
         check(yg[idx], yo[idx], f"y, {name} rows", scale[name])
@@ -357,9 +368,8 @@ def test_extreme_inputs(dtype):
     k0 = G.f64(x)[0, 9:40] @ G.f64(w["wk"])[:wl.head_dim].T
     print(f"  score std ~ {np.std(q0 @ k0.T) / np.sqrt(wl.head_dim):.1f}", flush=True)
     if dtype == "bf16":
-        fk, fv = G.kv_floors(x, w)
-        G.assert_bf16_storage(G.f64(kc)[:, :, written], ko[:, :, written], "K written", fk)
-        G.assert_bf16_storage(G.f64(vc)[:, :, written], vo[:, :, written], "V written", fv)
+        G.assert_bf16_cache(G.f64(kc)[:, :, written], ex["k"], ko[:, :, written], "K written")
+        G.assert_bf16_cache(G.f64(vc)[:, :, written], ex["v"], vo[:, :, written], "V written")
     else:
         G.assert_f32(G.f64(kc), ko, "K cache")
         G.assert_f32(G.f64(vc), vo, "V cache")
