@@ -149,6 +149,28 @@ int llama_layer_prefill(llama_layer* layer, const void* x, void* y, const int32_
 int llama_layer_decode(llama_layer* layer, const void* x, void* y, const int32_t* positions,
                        int32_t B, void* k_cache, void* v_cache, void* stream);
 
+/* Allocation-free decode, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  The same computation, kernels and results as
+ * llama_layer_decode on a bf16 layer, but the call's scratch (normalised
+ * activations, q, the attention output, the fp32 residual stream, the SwiGLU
+ * product, attention split partials, the weight-streaming GEMMs' partial
+ * tiles and counters) lives in a static device array of 32 MiB that the
+ * library holds on each GPU it runs on until the process ends, not in the
+ * handle's buffers.  The call allocates nothing and calls no allocating
+ * routine; its first call on a device looks up that device's copy of the
+ * array.  The counters are cleared by a small kernel at the start of every
+ * call.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind, so calls that overlap on one GPU (other streams, other
+ * handles) race: serialise them.
+ * Limits: B <= 64, and the call's scratch within 32 MiB (about 64 x (6 d +
+ * 4 H dh + 2 f) bytes + split partials + 8 MiB of partial tiles: every
+ * LLaMA-7B/13B/70B layer shape fits).  B is not limited by max_tokens.
+ * Errors: NULL, INVALID (B < 1, misaligned pointers), UNSUPPORTED (fp32
+ * layer), CAPACITY (B > 64 or the scratch would exceed 32 MiB), HIP. */
+int llama_layer_decode_noalloc(llama_layer* layer, const void* x, void* y, const int32_t* positions,
+                               int32_t B, void* k_cache, void* v_cache, void* stream);
+
 /* Free everything the handle owns (waits for the device first).  NULL is a no-op. */
 void llama_layer_destroy(llama_layer* layer);
 

@@ -32,7 +32,7 @@ LLAMA_ERR_ALLOC = -6
 LLAMA_F32 = 0
 LLAMA_BF16 = 1
 
-EXPORTED = ("llama_layer_create", "llama_layer_prefill", "llama_layer_decode",
+EXPORTED = ("llama_layer_create", "llama_layer_prefill", "llama_layer_decode", "llama_layer_decode_noalloc",
             "llama_layer_destroy", "llama_layer_strerror", "llama_layer_last_error",
             "llama_layer_profile", "llama_layer_profile_read", "llama_layer_step_name",
             "llama_layer_ceiling_mfma", "llama_layer_ceiling_read")
@@ -93,6 +93,8 @@ def _load():
     lib.llama_layer_prefill.restype = ctypes.c_int
     lib.llama_layer_decode.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp]
     lib.llama_layer_decode.restype = ctypes.c_int
+    lib.llama_layer_decode_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp]
+    lib.llama_layer_decode_noalloc.restype = ctypes.c_int
     lib.llama_layer_destroy.argtypes = [vp]
     lib.llama_layer_destroy.restype = None
     lib.llama_layer_strerror.argtypes = [ctypes.c_int]
@@ -192,6 +194,14 @@ def llama_layer_decode(handle, x, y, positions, B, k_cache, v_cache, stream=None
                                   _stream_ptr(stream)))
 
 
+def llama_layer_decode_noalloc(handle, x, y, positions, B, k_cache, v_cache, stream=None):
+    import torch
+    _check(LIB.llama_layer_decode_noalloc(handle, _ptr(x, "x"), _ptr(y, "y"),
+                                          _ptr(positions, "positions", torch.int32), int(B),
+                                          _ptr(k_cache, "k_cache"), _ptr(v_cache, "v_cache"),
+                                          _stream_ptr(stream)))
+
+
 def llama_layer_destroy(handle):
     LIB.llama_layer_destroy(handle)
 
@@ -249,6 +259,11 @@ class LlamaLayer:
         import torch
         y = torch.empty_like(x) if y is None else y
         llama_layer_decode(self.handle, x, y, positions, int(x.shape[0]), k_cache, v_cache, stream)
+        return y
+
+    def decode_noalloc(self, x, positions, k_cache, v_cache, y, stream=None):
+        """The allocation-free decode: y must be given (nothing is allocated)."""
+        llama_layer_decode_noalloc(self.handle, x, y, positions, int(x.shape[0]), k_cache, v_cache, stream)
         return y
 
     def close(self):

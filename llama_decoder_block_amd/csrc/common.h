@@ -140,17 +140,19 @@ int device_cu_count();
 // W both in fragment order (A holds ceil(M/32)*32 rows; rows >= M are never
 // written out, whatever they hold).  The SwiGLU output h is written in
 // fragment order, ready to be the A operand of the down projection.
-// Scratch for column groups split between workgroups: part holds
-// skinny_scratch_floats() floats, cnt cnt_len counters (one per column
-// group: N / 32 or N / 64 for the paired SwiGLU), all zero before the first
-// call; each call leaves them zero.
+// Scratch for column groups split between workgroups: part holds part_len
+// floats (skinny_scratch_floats() always suffices; a call with G workgroups
+// needs 2 G x (1 or 2 blocks) x (1 or 2 token blocks) x 1024), cnt cnt_len
+// counters (one per column group: N / 32 or N / 64 for the paired SwiGLU),
+// all zero before the first call; each call leaves them zero.
 // Calls that share a scratch must not overlap.
 constexpr int kSkinnyMaxTokens = 64;
 constexpr int kSkinnyGrid = 512;  // workgroups per call, at most
 struct SkinnyScratch {
   float* part;
   unsigned* cnt;
-  int cnt_len;  // counters available
+  int cnt_len;      // counters available
+  size_t part_len;  // floats available at part
 };
 size_t skinny_scratch_floats();
 hipError_t launch_skinny_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,

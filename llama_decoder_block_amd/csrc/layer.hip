@@ -27,6 +27,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -107,6 +108,28 @@ struct llama_layer {
   long long prof_next = 0, prof_done = 0;  // calls recorded / harvested
   double prof_ms[LLAMA_LAYER_STEPS] = {};
 };
+
+namespace {
+
+// Scratch memory of one layer call: the handle's own buffers, or slices of
+// the library's static device array (llama_layer_decode_noalloc).
+struct CallScratch {
+  void* xn;
+  void* q;
+  void* o;
+  float* x1;
+  void* h;
+  float* gu;
+  float* part;     // decode attention split partials
+  int part_seqs;   // sequences whose partials fit at once
+  SkinnyScratch sk;
+};
+
+CallScratch handle_scratch(llama_layer* L) {
+  return CallScratch{L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->part_seqs, L->sk};
+}
+
+}  // namespace
 
 namespace {
 
@@ -194,6 +217,44 @@ int part_floats(const llama_layer_config& c, int* seqs) {
 
 }  // namespace
 
+// ---- the allocation-free decode: scratch in a static device array ----
+namespace {
+
+// Holds the scratch of one llama_layer_decode_noalloc call; each GPU the
+// library runs on keeps its own copy until the process ends.  Host code uses
+// the per-device address from hipGetSymbolAddress (the array's name on the
+// host is only a stand-in).
+constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// the array's device address on device dev (the current device); looked up once
+int noalloc_scratch(int dev, unsigned char** out) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(LLAMA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(LLAMA_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = static_cast<unsigned char*>(g_scratch_ptr[dev]);
+  return LLAMA_OK;
+}
+
+// fill kernel: clears the split-group counters at the start of a call (a
+// kernel rather than hipMemsetAsync, so the call can sit in a captured graph)
+__global__ void zero_words_kernel(unsigned* __restrict__ p, int n) {
+  const int i = static_cast<int>(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* llama_layer_strerror(int status) {
@@ -273,6 +334,7 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
     const size_t groups = std::max({(nq + 2 * nkv) / 32, 2 * f / 64, d / 32});
     ALLOC_OR_FAIL(L->sk.cnt, groups * sizeof(unsigned));
     L->sk.cnt_len = static_cast<int>(groups);
+    L->sk.part_len = skinny_scratch_floats();
     HIP_OR_FAIL(hipMemsetAsync(L->sk.cnt, 0, groups * sizeof(unsigned), s), "clear counters");
   } else {
     ALLOC_OR_FAIL(L->q, mt * (nq + 2 * nkv) * es);
@@ -381,8 +443,8 @@ static int check_positions(llama_layer* L, const int32_t* pos, int B, int T, hip
   return LLAMA_OK;
 }
 
-static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos, int B, int T,
-                     void* kc, void* vc, hipStream_t s) {
+static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* y, const int32_t* pos, int B,
+                     int T, void* kc, void* vc, hipStream_t s) {
   const llama_layer_config& c = L->cfg;
   const int M = B * T;
   const int d = c.d_model, H = c.n_heads, Hkv = c.n_kv_heads, f = c.d_ff;
@@ -399,8 +461,8 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
     F.wqkv = static_cast<const float*>(L->wqkv); F.wo = static_cast<const float*>(L->wo);
     F.wgu = static_cast<const float*>(L->wgu); F.wd = static_cast<const float*>(L->wd);
     F.rope_cos = L->rope_cos; F.rope_sin = L->rope_sin;
-    F.xn = static_cast<float*>(L->xn); F.qkv = static_cast<float*>(L->q); F.attn = static_cast<float*>(L->o);
-    F.x1 = L->x1; F.gu = L->gu; F.h = static_cast<float*>(L->h);
+    F.xn = static_cast<float*>(S.xn); F.qkv = static_cast<float*>(S.q); F.attn = static_cast<float*>(S.o);
+    F.x1 = S.x1; F.gu = S.gu; F.h = static_cast<float*>(S.h);
     HIP_OR_RETURN(run_f32_layer(F, static_cast<const float*>(x), static_cast<float*>(y), pos, B, T,
                                 static_cast<float*>(kc), static_cast<float*>(vc), s),
                   "fp32 layer launch");
@@ -409,10 +471,10 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
 
   const bf16_t* xb = static_cast<const bf16_t*>(x);
   bf16_t* yb = static_cast<bf16_t*>(y);
-  bf16_t* xn = static_cast<bf16_t*>(L->xn);
-  bf16_t* q = static_cast<bf16_t*>(L->q);
-  bf16_t* o = static_cast<bf16_t*>(L->o);
-  bf16_t* h = static_cast<bf16_t*>(L->h);
+  bf16_t* xn = static_cast<bf16_t*>(S.xn);
+  bf16_t* q = static_cast<bf16_t*>(S.q);
+  bf16_t* o = static_cast<bf16_t*>(S.o);
+  bf16_t* h = static_cast<bf16_t*>(S.h);
   const bf16_t* wqkv = static_cast<const bf16_t*>(L->wqkv);
   const bf16_t* wo = static_cast<const bf16_t*>(L->wo);
   const bf16_t* wgu = static_cast<const bf16_t*>(L->wgu);
@@ -445,19 +507,19 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
   HIP_OR_RETURN(mark(0), "event record");
   HIP_OR_RETURN(launch_rmsnorm(xb, 0, L->g1, 0, xn, 0, skinny, M, d, c.rms_eps, s), "rmsnorm 1");
   HIP_OR_RETURN(mark(1), "event record");
-  HIP_OR_RETURN(skinny ? launch_skinny_qkv(xn, wqkv, M, nqkv, d, ep, L->sk, s)
+  HIP_OR_RETURN(skinny ? launch_skinny_qkv(xn, wqkv, M, nqkv, d, ep, S.sk, s)
                        : launch_gemm_qkv(xn, wqkv, M, nqkv, d, ep, s),
                 "qkv projection");
   HIP_OR_RETURN(mark(2), "event record");
   if (T == 1) {
     const size_t kv_seq = static_cast<size_t>(Hkv) * c.max_pos * 128;
-    for (int b0 = 0; b0 < B; b0 += L->part_seqs) {
-      const int nb = B - b0 < L->part_seqs ? B - b0 : L->part_seqs;
+    for (int b0 = 0; b0 < B; b0 += S.part_seqs) {
+      const int nb = B - b0 < S.part_seqs ? B - b0 : S.part_seqs;
       const int ns = decode_attn_splits(c.max_pos, nb, H, Hkv);
       HIP_OR_RETURN(launch_attn_decode(q + static_cast<size_t>(b0) * H * 128,
                                        static_cast<const bf16_t*>(kc) + b0 * kv_seq,
                                        static_cast<const bf16_t*>(vc) + b0 * kv_seq, pos + b0,
-                                       o + static_cast<size_t>(b0) * H * 128, skinny, L->part, ns, nb, H, Hkv,
+                                       o + static_cast<size_t>(b0) * H * 128, skinny, S.part, ns, nb, H, Hkv,
                                        c.max_pos, s),
                     "decode attention");
     }
@@ -467,18 +529,18 @@ static int run_layer(llama_layer* L, const void* x, void* y, const int32_t* pos,
                   "prefill attention");
   }
   HIP_OR_RETURN(mark(3), "event record");
-  HIP_OR_RETURN(skinny ? launch_skinny_resid_f32out(o, wo, M, d, H * 128, xb, L->x1, L->sk, s)
-                       : launch_gemm_resid_f32out(o, wo, M, d, H * 128, xb, L->x1, s),
+  HIP_OR_RETURN(skinny ? launch_skinny_resid_f32out(o, wo, M, d, H * 128, xb, S.x1, S.sk, s)
+                       : launch_gemm_resid_f32out(o, wo, M, d, H * 128, xb, S.x1, s),
                 "o_proj");
   HIP_OR_RETURN(mark(4), "event record");
-  HIP_OR_RETURN(launch_rmsnorm(L->x1, 1, L->g2, 0, xn, 0, skinny, M, d, c.rms_eps, s), "rmsnorm 2");
+  HIP_OR_RETURN(launch_rmsnorm(S.x1, 1, L->g2, 0, xn, 0, skinny, M, d, c.rms_eps, s), "rmsnorm 2");
   HIP_OR_RETURN(mark(5), "event record");
-  HIP_OR_RETURN(skinny ? launch_skinny_swiglu(xn, wgu, M, f, d, h, L->sk, s)
+  HIP_OR_RETURN(skinny ? launch_skinny_swiglu(xn, wgu, M, f, d, h, S.sk, s)
                        : launch_gemm_swiglu(xn, wgu, M, 2 * f, d, h, s),
                 "gate/up projection");
   HIP_OR_RETURN(mark(6), "event record");
-  HIP_OR_RETURN(skinny ? launch_skinny_resid_bf16out(h, wd, M, d, f, L->x1, yb, L->sk, s)
-                       : launch_gemm_resid_bf16out(h, wd, M, d, f, L->x1, yb, s),
+  HIP_OR_RETURN(skinny ? launch_skinny_resid_bf16out(h, wd, M, d, f, S.x1, yb, S.sk, s)
+                       : launch_gemm_resid_bf16out(h, wd, M, d, f, S.x1, yb, s),
                 "down projection");
   HIP_OR_RETURN(mark(7), "event record");
   if (ev) ++L->prof_next;
@@ -500,7 +562,7 @@ static int checked_call(llama_layer* L, const void* x, void* y, const int32_t* p
   int cur = 0;
   HIP_OR_RETURN(hipGetDevice(&cur), "hipGetDevice");
   if (cur != L->device) HIP_OR_RETURN(hipSetDevice(L->device), "hipSetDevice");
-  const int st = run_layer(L, x, y, pos, B, T, kc, vc, static_cast<hipStream_t>(stream));
+  const int st = run_layer(L, handle_scratch(L), x, y, pos, B, T, kc, vc, static_cast<hipStream_t>(stream));
   if (cur != L->device) (void)hipSetDevice(cur);
   return st;
 }
@@ -546,6 +608,70 @@ int llama_layer_prefill(llama_layer* L, const void* x, void* y, const int32_t* p
 int llama_layer_decode(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
                        void* k_cache, void* v_cache, void* stream) {
   return checked_call(L, x, y, positions, B, 1, k_cache, v_cache, stream);
+}
+
+int llama_layer_decode_noalloc(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
+                               void* k_cache, void* v_cache, void* stream) {
+  g_last_error.clear();
+  if (!L || !x || !y || !positions || !k_cache || !v_cache)
+    return fail(LLAMA_ERR_NULL, "layer, x, y, positions and caches must be non-null");
+  const llama_layer_config& c = L->cfg;
+  if (c.dtype != LLAMA_BF16) return fail(LLAMA_ERR_UNSUPPORTED, "the allocation-free decode serves bf16 layers");
+  if (B < 1) return fail(LLAMA_ERR_INVALID, "B must be >= 1 (got %d)", B);
+  if (B > kSkinnyMaxTokens)
+    return fail(LLAMA_ERR_CAPACITY, "the allocation-free decode takes at most %d sequences (got %d)",
+                kSkinnyMaxTokens, B);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(LLAMA_ERR_INVALID, "x, y and the caches must be 16-byte aligned");
+  // slices of the static array, 256-byte aligned; activations in fragment
+  // order hold whole 32-row blocks, i.e. 64 rows
+  const size_t d = c.d_model, nq = static_cast<size_t>(c.n_heads) * 128, f = c.d_ff;
+  const size_t nkv = static_cast<size_t>(c.n_kv_heads) * 128, rows = kSkinnyMaxTokens;
+  size_t off = 0;
+  auto take = [&off](size_t bytes) {
+    const size_t at = off;
+    off += (bytes + 255) & ~static_cast<size_t>(255);
+    return at;
+  };
+  const size_t o_xn = take(rows * d * 2), o_q = take(rows * nq * 2), o_o = take(rows * nq * 2),
+               o_x1 = take(rows * d * 4), o_h = take(rows * f * 2);
+  const int ns = decode_attn_splits(c.max_pos, B, c.n_heads, c.n_kv_heads);
+  const size_t o_part = take(static_cast<size_t>(B) * c.n_heads * ns * 130 * sizeof(float));
+  const int g_max = std::min(device_cu_count(), kSkinnyGrid);
+  const size_t sk_floats = static_cast<size_t>(2) * g_max * 2 * (B <= 32 ? 1 : 2) * 1024;
+  const size_t o_skp = take(sk_floats * sizeof(float));
+  const size_t groups = std::max({(nq + 2 * nkv) / 32, 2 * f / 64, d / 32});
+  const size_t o_cnt = take(groups * sizeof(unsigned));
+  if (off > kNoAllocScratchBytes)
+    return fail(LLAMA_ERR_CAPACITY, "this call needs %zu bytes of scratch; the static array holds %zu", off,
+                kNoAllocScratchBytes);
+  int cur = 0;
+  HIP_OR_RETURN(hipGetDevice(&cur), "hipGetDevice");
+  if (cur != L->device) HIP_OR_RETURN(hipSetDevice(L->device), "hipSetDevice");
+  unsigned char* base = nullptr;
+  int st = noalloc_scratch(L->device, &base);
+  if (st == LLAMA_OK) {
+    CallScratch S{};
+    S.xn = base + o_xn;
+    S.q = base + o_q;
+    S.o = base + o_o;
+    S.x1 = reinterpret_cast<float*>(base + o_x1);
+    S.h = base + o_h;
+    S.gu = nullptr;
+    S.part = reinterpret_cast<float*>(base + o_part);
+    S.part_seqs = B;
+    S.sk.part = reinterpret_cast<float*>(base + o_skp);
+    S.sk.part_len = sk_floats;
+    S.sk.cnt = reinterpret_cast<unsigned*>(base + o_cnt);
+    S.sk.cnt_len = static_cast<int>(groups);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int n = static_cast<int>(groups);
+    hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, s, S.sk.cnt, n);
+    const hipError_t e = hipGetLastError();
+    st = e != hipSuccess ? hip_fail(e, "clear counters") : run_layer(L, S, x, y, positions, B, 1, k_cache, v_cache, s);
+  }
+  if (cur != L->device) (void)hipSetDevice(cur);
+  return st;
 }
 
 }  // extern "C"

@@ -509,6 +509,7 @@ int llama_model_create(const llama_model_config* cfg, const llama_model_weights*
     const size_t groups = static_cast<size_t>(m->Vp) / 32;
     MODEL_ALLOC(m->sk.cnt, groups * sizeof(unsigned));
     m->sk.cnt_len = static_cast<int>(groups);
+    m->sk.part_len = skinny_scratch_floats();
     MODEL_HIP_FAIL(hipMemsetAsync(m->sk.cnt, 0, groups * sizeof(unsigned), s), "clear counters");
   } else {
     MODEL_HIP_FAIL(hipMemcpyAsync(m->lm, w->lm_head, V * d * es, dd, s), "copy LM head");

@@ -45,6 +45,7 @@ struct SkinnyArgs {
   const void* resid;
   void* out;
   float* part;     // 2 G partial slots of NB * TB * 1024 floats
+  size_t part_len; // floats at part
   unsigned* cnt;   // per column group, zero between launches
   int cnt_len;
   int n_valid, ld; // SK_F32OUT: columns written (< N) and the output's row stride
@@ -313,8 +314,11 @@ hipError_t launch(const bf16_t* X, const bf16_t* W, int M, int N, int K, SkinnyA
   constexpr int NB = paired ? 2 : 1;
   const int groups = N / (32 * NB);
   const int G = grid_for(groups, K / 16, device_cu_count());
-  // split groups need 2 G partial slots and a counter each
-  if (G != groups && (G > kSkinnyGrid || groups > ep.cnt_len)) return hipErrorInvalidValue;
+  // split groups need 2 G partial slots of NB x TB tiles and a counter each
+  const int TBn = M <= 32 ? 1 : 2;
+  if (G != groups && (G > kSkinnyGrid || groups > ep.cnt_len ||
+                      static_cast<size_t>(2) * G * NB * TBn * 1024 > ep.part_len))
+    return hipErrorInvalidValue;
   if (M <= 32)
     hipLaunchKernelGGL((skinny_kernel<NB, 1, kNW, paired ? 12 : 16, EPI>), dim3(G), dim3(kNW * 64), 0, s, X, W, M,
                        N, K, G, ep);
@@ -333,6 +337,7 @@ hipError_t launch_skinny_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int
   SkinnyArgs ep{};
   ep.qkv = q;
   ep.part = sc.part;
+  ep.part_len = sc.part_len;
   ep.cnt = sc.cnt;
   ep.cnt_len = sc.cnt_len;
   return launch<SK_QKV>(A, W, M, N, K, ep, s);
@@ -343,6 +348,7 @@ hipError_t launch_skinny_resid_f32out(const bf16_t* A, const bf16_t* W, int M, i
   ep.resid = resid;
   ep.out = out;
   ep.part = sc.part;
+  ep.part_len = sc.part_len;
   ep.cnt = sc.cnt;
   ep.cnt_len = sc.cnt_len;
   return launch<SK_RESID32>(A, W, M, N, K, ep, s);
@@ -353,6 +359,7 @@ hipError_t launch_skinny_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, 
   ep.resid = resid;
   ep.out = out;
   ep.part = sc.part;
+  ep.part_len = sc.part_len;
   ep.cnt = sc.cnt;
   ep.cnt_len = sc.cnt_len;
   return launch<SK_RESID16>(A, W, M, N, K, ep, s);
@@ -363,6 +370,7 @@ hipError_t launch_skinny_f32out(const bf16_t* A, const bf16_t* W, int M, int N, 
   SkinnyArgs ep{};
   ep.out = out;
   ep.part = sc.part;
+  ep.part_len = sc.part_len;
   ep.cnt = sc.cnt;
   ep.cnt_len = sc.cnt_len;
   ep.n_valid = n_valid;
@@ -374,6 +382,7 @@ hipError_t launch_skinny_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int f
   SkinnyArgs ep{};
   ep.out = out;
   ep.part = sc.part;
+  ep.part_len = sc.part_len;
   ep.cnt = sc.cnt;
   ep.cnt_len = sc.cnt_len;
   return launch<SK_SWIGLU>(A, Wgu, M, 2 * f, K, ep, s);
