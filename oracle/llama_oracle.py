@@ -23,12 +23,15 @@ Sources, cited by page title and section:
 
 Two modes:
   plain       no intermediate rounding (the gate for fp32 layers);
-  bf16 points round-to-nearest-even to bf16 (this module's own rounding) of
-              exactly the tensors a bf16 layer stores or feeds to bf16 matrix
-              products: the normalised activations, q, k, v (the cache dtype),
-              the attention output, and the SwiGLU product.  Scores, softmax
-              weights, the residual stream X' and the returned y are never
-              rounded.
+  bf16 points round-to-nearest-even (this module's own rounding) of exactly
+              the tensors a bf16 layer stores or feeds to 16-bit matrix
+              products, in the format it uses for them: bf16 for the
+              normalised activations, q, k and v (the cache dtype); fp16 for
+              the attention output and the SwiGLU product (the A operands of
+              o_proj and down, kept with 11 significant bits; the pages fix
+              bf16 weights and activations with fp32 accumulation, not the
+              format of these internal operands).  Scores, softmax weights,
+              the residual stream X' and the returned y are never rounded.
 
 Parity status: every function below is pinned by a CPU test against what the
 pages or the mathematics fix (worked examples, invariants, library routines
@@ -56,8 +59,24 @@ def bf16_round(a):
     return np.ldexp(np.rint(m * 256.0), e - 8)
 
 
-def _maybe_round(a, bf16_points: bool):
-    return bf16_round(a) if bf16_points else a
+def fp16_round(a):
+    """Round fp64 values to the nearest IEEE half-precision value, ties to
+    even, saturating at the largest finite value (+-65504).
+
+    fp16 keeps 11 significant bits for |a| >= 2^-14 (normal numbers) and a
+    fixed spacing of 2^-24 below that (subnormal numbers)."""
+    a = np.asarray(a, dtype=np.float64)
+    m, e = np.frexp(a)
+    normal = np.ldexp(np.rint(m * 2048.0), e - 11)
+    sub = np.ldexp(np.rint(np.ldexp(a, 24)), -24)
+    r = np.where(np.abs(a) >= 2.0**-14, normal, sub)
+    return np.clip(r, -65504.0, 65504.0)
+
+
+def _maybe_round(a, bf16_points: bool, fmt: str = "bf16"):
+    if not bf16_points:
+        return a
+    return fp16_round(a) if fmt == "fp16" else bf16_round(a)
 
 
 # --------------------------------------------------------------------------
@@ -211,7 +230,7 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
     H, Hkv = n_heads, n_kv_heads
     dh = W["wq"].shape[0] // H
     n_rep = H // Hkv
-    r = lambda a: _maybe_round(a, bf16_points)  # noqa: E731
+    r = lambda a, fmt="bf16": _maybe_round(a, bf16_points, fmt)  # noqa: E731
 
     xn = r(rms_norm(x, W["attn_norm"], eps))                         # [B,T,d]
 
@@ -252,10 +271,10 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
         vv = repeat_kv(vc[b][:, :S], n_rep)
         heads = [masked_softmax_attention(q[h], kk[h], vv[h], lim, np.arange(S))[0]
                  for h in range(H)]
-        o = r(np.stack(heads, axis=1).reshape(ts.size, H * dh))      # heads concatenated
+        o = r(np.stack(heads, axis=1).reshape(ts.size, H * dh), "fp16")  # heads concatenated
         x1 = xb + o @ W["wo"].T                                      # X', never rounded
         xn2 = r(rms_norm(x1, W["ffn_norm"], eps))
-        h_ = r(swiglu_hidden(xn2, W["w_gate"], W["w_up"]))
+        h_ = r(swiglu_hidden(xn2, W["w_gate"], W["w_up"]), "fp16")
         y[b, ts] = x1 + h_ @ W["w_down"].T
     return y, kc, vc
 

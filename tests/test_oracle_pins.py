@@ -230,6 +230,29 @@ def _tiny(seed, B=2, T=6, d=32, H=4, Hkv=2, f=48, S=None, gains=True):
     return x, w, kc, vc
 
 
+def _round_via_odd_fp32(a, dtype):
+    """fp64 -> dtype (bf16 or fp16) rounded to nearest even with torch's own
+    conversions, without double rounding: round to fp32 *to odd* first, then
+    let torch round fp32 -> dtype.  Boldo and Melquiond, "Emulation of FMA and
+    correctly rounded sums: proved algorithms using rounding to odd" (IEEE
+    Trans. Computers, 2008): exact when the intermediate format has at least
+    two more bits (fp32 has 24; bf16 8, fp16 11).  Round to odd keeps exact
+    values and otherwise takes, of the two fp32 neighbours of the value, the
+    one whose last significand bit is 1."""
+    a = torch.as_tensor(a, dtype=torch.float64)
+    f = a.to(torch.float32)                        # nearest fp32
+    back = f.to(torch.float64)
+    inexact = back != a
+    even = (f.view(torch.int32) & 1) == 0
+    away = torch.where(back < a, torch.full_like(f, math.inf), torch.full_like(f, -math.inf))
+    odd = torch.where(inexact & even, torch.nextafter(f, away), f)
+    return odd.to(dtype).to(torch.float64)
+
+
+def _f16_torch(a):
+    return _round_via_odd_fp32(a, torch.float16)
+
+
 def _bf16_torch(a):
     """fp64 -> bf16 (round to nearest, ties to even) with torch's own
     conversions, as an independent check of the oracle's frexp/rint rounding.
@@ -242,27 +265,21 @@ def _bf16_torch(a):
     needs at least two more bits in the intermediate format (fp32 has 24,
     bf16 8).  Round to odd keeps exact values and otherwise takes, of the two
     fp32 neighbours of the value, the one whose last significand bit is 1."""
-    a = torch.as_tensor(a, dtype=torch.float64)
-    f = a.to(torch.float32)                        # nearest fp32
-    back = f.to(torch.float64)
-    inexact = back != a
-    even = (f.view(torch.int32) & 1) == 0
-    away = torch.where(back < a, torch.full_like(f, math.inf), torch.full_like(f, -math.inf))
-    odd = torch.where(inexact & even, torch.nextafter(f, away), f)
-    return odd.to(torch.bfloat16).to(torch.float64)
+    return _round_via_odd_fp32(a, torch.bfloat16)
 
 
 def _torch_layer(x, pos, w, kc, vc, H, Hkv, eps=1e-6, base=10000.0, bidirectional=False,
-                 rnd=None, kv_exact=None):
+                 rnd=None, rnd16=None, kv_exact=None):
     """Independent fp64 re-derivation from library routines: F.rms_norm,
     F.linear, RoPE as complex multiplication, SDPA with enable_gqa and an
     explicit boolean position mask (bidirectional: every new token of a
     sequence sees the slots up to the sequence's largest new position), F.silu.
-    rnd (default: none) is applied at the bf16 layer's rounding points: the
-    normalised activations, q and k after RoPE, v, the attention output and
-    the SwiGLU product."""
+    rnd (default: none) is applied at the bf16 layer's bf16 rounding points
+    (the normalised activations, q and k after RoPE, v), rnd16 at its fp16
+    ones (the attention output and the SwiGLU product)."""
     t = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float64))  # noqa: E731
     r = rnd or (lambda a: a)  # noqa: E731
+    r16 = rnd16 or (lambda a: a)  # noqa: E731
     x, kc, vc = t(x), t(kc).clone(), t(vc).clone()
     W = {k: t(v) for k, v in w.items()}
     B, T, d = x.shape
@@ -290,10 +307,10 @@ def _torch_layer(x, pos, w, kc, vc, H, Hkv, eps=1e-6, base=10000.0, bidirectiona
     lim = pos.max(dim=1, keepdim=True).values.expand(B, T) if bidirectional else pos
     allowed = torch.arange(S)[None, None, :] <= lim[:, :, None]      # [B, T, S]
     o = F.scaled_dot_product_attention(q, kc, vc, attn_mask=allowed[:, None], enable_gqa=True)
-    o = r(o.transpose(1, 2).reshape(B, T, H * dh))
+    o = r16(o.transpose(1, 2).reshape(B, T, H * dh))
     x1 = x + F.linear(o, W["wo"])
     xn2 = r(F.rms_norm(x1, (d,), W["ffn_norm"], eps))
-    h = r(F.silu(F.linear(xn2, W["w_gate"])) * F.linear(xn2, W["w_up"]))
+    h = r16(F.silu(F.linear(xn2, W["w_gate"])) * F.linear(xn2, W["w_up"]))
     y = x1 + F.linear(h, W["w_down"])
     return y.numpy(), kc.numpy(), vc.numpy()
 
@@ -445,6 +462,30 @@ def test_bf16_torch_rounding_helper_is_correct_rounding():
     assert torch.equal(_bf16_torch(x.double()), x.to(torch.bfloat16).double())
 
 
+def test_fp16_round_matches_library_conversion():
+    """Library routine: numpy's fp32 -> fp16 conversion (round to nearest
+    even) on values fp32 holds exactly, across normal and subnormal fp16
+    ranges; ties; saturation at the largest finite value."""
+    rng = _rng(7)
+    x = np.concatenate([rng.standard_normal(100000) * s for s in (1e-6, 1e-4, 1.0, 100.0, 1e4)])
+    x32 = x.astype(np.float32).astype(np.float64)
+    np.testing.assert_array_equal(O.fp16_round(x32), x32.astype(np.float16).astype(np.float64))
+    # 1 + 2^-11 is the midpoint of 1 and 1 + 2^-10 (to even: 1); 1 + 3 2^-11 -> 1 + 2^-9
+    np.testing.assert_array_equal(O.fp16_round(np.array([1 + 2**-11, 1 + 3 * 2**-11, 1 + 2**-11 + 2**-40])),
+                                  [1.0, 1 + 2**-9, 1 + 2**-10])
+    assert O.fp16_round(np.array([1e5, -7e4])).tolist() == [65504.0, -65504.0]
+    assert O.fp16_round(np.array([2.0**-25, 3 * 2.0**-25])).tolist() == [0.0, 2.0**-23]
+
+
+def test_rounding_helper_fp16_is_correct_rounding():
+    """The test's fp64 -> fp16 route, like the bf16 one: a value a hair above
+    a midpoint must round up although its fp32 rounding lands on the midpoint."""
+    vals = torch.tensor([1 + 2**-11 + 2**-40, 1 + 2**-11 - 2**-40], dtype=torch.float64)
+    assert torch.equal(_f16_torch(vals), torch.tensor([1 + 2**-10, 1.0], dtype=torch.float64))
+    x = torch.randn(100000, dtype=torch.float32, generator=torch.Generator().manual_seed(4))
+    assert torch.equal(_f16_torch(x.double()), x.half().double())
+
+
 def _bf16_case(seed=61, B=1, T=7, H=4, Hkv=2, prior=0):
     x, w, kc, vc = _tiny(seed, B=B, T=T, H=H, Hkv=Hkv, S=prior + T + 2)
     if prior:
@@ -458,8 +499,9 @@ def _bf16_case(seed=61, B=1, T=7, H=4, Hkv=2, prior=0):
 @pytest.mark.parametrize("B,H,Hkv,prior", [(1, 4, 2, 0), (2, 4, 4, 0), (2, 4, 1, 5)])
 def test_bf16_points_mode_matches_library_rederivation(B, H, Hkv, prior):
     """The rounding-point mode (the reference of every bf16 comparison) against
-    the torch re-derivation with an independent bf16 rounding (_bf16_torch) at
-    the same seven points: xn, q, k, v, the attention output, xn2 and h.
+    the torch re-derivation with independent roundings at the same seven
+    points: bf16 (_bf16_torch) at xn, q, k, v and xn2, fp16 (_f16_torch) at
+    the attention output and h.
     Agreement to 1e-12: the two sides' pre-rounding values differ only by fp64
     evaluation order (~1e-16 relative), so they round differently only for a
     value within that distance of a bf16 midpoint (a tie; none occurs in these
@@ -468,7 +510,7 @@ def test_bf16_points_mode_matches_library_rederivation(B, H, Hkv, prior):
     ex, exr = {}, {}
     y, k2, v2 = O.decoder_layer(x, pos, w, kc, vc, n_heads=H, n_kv_heads=Hkv, bf16_points=True,
                                 kv_exact=ex)
-    yr, kr, vr = _torch_layer(x, pos, w, kc, vc, H, Hkv, rnd=_bf16_torch, kv_exact=exr)
+    yr, kr, vr = _torch_layer(x, pos, w, kc, vc, H, Hkv, rnd=_bf16_torch, rnd16=_f16_torch, kv_exact=exr)
     np.testing.assert_allclose(y, yr, rtol=0, atol=1e-12)
     np.testing.assert_array_equal(k2, kr)
     np.testing.assert_array_equal(v2, vr)
@@ -489,13 +531,13 @@ def test_bf16_points_pin_catches_a_dropped_rounding(dropped, monkeypatch):
     rounding points makes it disagree with the re-derivation above (in y or
     in the cache), so the pin covers every point."""
     x, w, kc, vc, pos = _bf16_case(61 + 7 + 2)
-    yr, kr, vr = _torch_layer(x, pos, w, kc, vc, 4, 2, rnd=_bf16_torch)
+    yr, kr, vr = _torch_layer(x, pos, w, kc, vc, 4, 2, rnd=_bf16_torch, rnd16=_f16_torch)
     real = O._maybe_round
     calls = []
 
-    def mutant(a, bf16_points):
+    def mutant(a, bf16_points, fmt="bf16"):
         calls.append(len(calls))
-        return a if len(calls) - 1 == dropped else real(a, bf16_points)
+        return a if len(calls) - 1 == dropped else real(a, bf16_points, fmt)
     monkeypatch.setattr(O, "_maybe_round", mutant)
     y, k2, v2 = O.decoder_layer(x, pos, w, kc, vc, n_heads=4, n_kv_heads=2, bf16_points=True)
     assert len(calls) == len(_ROUNDING_POINTS)
