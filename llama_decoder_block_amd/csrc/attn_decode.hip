@@ -1,5 +1,6 @@
 // Decode attention: one new query per sequence over its whole cache,
-// o_h = softmax(q_h K_{0..p}^T / sqrt(128)) V_{0..p}, bf16 cache, fp32 math.
+// o_h = softmax(q_h K_{0..p}^T / sqrt(128)) V_{0..p}, bf16 cache, fp32 math,
+// o stored as fp16 (the A operand of the fp16 o_proj GEMM).
 //
 // Sources: "LLM mechanics lecture notes" Ch.04 (decode appends k_t, v_t and
 // lets q_t read every visible cached K/V; decode stays memory bound and grows
@@ -197,7 +198,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     if (n_split == 1) {
       const int hh = h0 + r;
       const size_t at = o_frag ? frag_index(b, hh * DH + d, H * DH) : (static_cast<size_t>(b) * H + hh) * DH + d;
-      o[at] = f32_to_bf16(ll > 0.f ? aa / ll : 0.f);
+      o[at] = f32_to_f16_sat(ll > 0.f ? aa / ll : 0.f);
     } else {
       float* po = out + static_cast<size_t>(r) * n_split * (DH + 2);
       po[2 + d] = aa;
@@ -259,7 +260,7 @@ __global__ __launch_bounds__(kCombineThreads) void attn_decode_combine_kernel(co
   if (hf == 0) {
     num += half_sum[d];
     const size_t at = o_frag ? frag_index(bh / H, (bh % H) * DH + d, H * DH) : static_cast<size_t>(bh) * DH + d;
-    o[at] = f32_to_bf16(den > 0.f ? num / den : 0.f);
+    o[at] = f32_to_f16_sat(den > 0.f ? num / den : 0.f);
   }
 }
 

@@ -1,4 +1,5 @@
-// Causal flash attention for prefill, bf16 in and out, head_dim 128.
+// Causal flash attention for prefill, head_dim 128: bf16 q and cache in, the
+// output o in fp16 (the A operand of the fp16 o_proj GEMM).
 //
 // Computes, for every query token m (sequence b, position p_m) and query head
 // h, o = sum_j softmax_j(q.k_j / sqrt(128)) v_j over the cache slots
@@ -31,11 +32,12 @@
 // a lane's 16 score registers are two runs of 8 consecutive keys — exactly the
 // B operand of the next MFMA, O^T += V^T P^T, with no register shuffling.  V
 // is transposed to [dd][slot] while it is written to LDS.  P stays in fp32 in
-// the online softmax and is fed to the PV product in fp16 (11 significant bits
-// against bf16's 8), with V converted to fp16 as it is staged.  The weights
-// are taken against the running max (the output is rescaled only when some
-// query's max moves), and the row sum adds the same fp16 weights the product
-// multiplies.  The
+// the online softmax and is fed to the PV product as two fp16 parts (hi + lo,
+// about 22 significant bits; one fp16 alone keeps 11, and its rounding
+// error, carried through the bf16 rounding of the attention output and
+// amplified by the MLP, put the 70B-shape layer output beyond the bf16
+// tolerance), with V converted to fp16 (exact) as it is staged.  The weights are taken against the running max (the output is
+// rescaled only when some query's max moves).  The
 // row-max exchange between the two lanes of a query is a permlane32 swap.
 // Query tiles are launched heaviest first across all heads and sequences (the
 // causal workload grows with the tile index).  Tiles that lie wholly above a wave's diagonal are skipped, and
@@ -246,10 +248,9 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
         mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
       // Running max m_run (log2 units; the scale is positive, so max and
-      // scaling commute).  The weights 2^(s - m_run + 7) stay within 2^7 and
-      // are fp16 normals down to 2^-21 of the max.  Output and sum carry the
-      // same factor 2^7, which the final division cancels.  The rescale is
-      // skipped when no query of the wave has a new max.
+      // scaling commute).  Output and sum carry the same factor 2^15, which
+      // the final division cancels.  The rescale is skipped when no query of
+      // the wave has a new max.
       const float m_tile = mt * scale_log2;
       if (__any(m_tile > m_run)) {  // wave-uniform
         const float m_new = fmaxf(m_tile, m_run);
@@ -261,34 +262,43 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
           for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
         m_run = m_new;
       }
-      const float m_sh = (m_run == -INFINITY ? 0.f : m_run) - 7.f;
-      // the row sum adds the fp16 weights the P.V product multiplies
-      const f16x2 ones = {static_cast<_Float16>(1.f), static_cast<_Float16>(1.f)};
-      float lsum[2] = {0.f, 0.f};
-      uint32_t ph[2][2][4];  // [kb][half][packed fp16 pair]
+      const float m_sh = (m_run == -INFINITY ? 0.f : m_run) - 15.f;
+      // Each weight p = 2^(s - m_run + 15) <= 2^15 goes to the P.V product as
+      // two fp16 parts: hi = p cut to fp16's 11 significant bits (exact in
+      // fp16), lo = fp16(p - hi), so hi + lo keeps about 22 bits of p (fp16
+      // alone keeps 11, which flips the bf16 rounding of the attention output
+      // far more often than fp32 weights would).  The row sum adds p in fp32.
+      float lsum = 0.f;
+      uint32_t ph[2][2][4], pl[2][2][4];  // [kb][half][packed fp16 pair]
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; r += 2) {
           const float p0 = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_sh));
           const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], scale_log2, -m_sh));
-          const uint32_t pp = pack_f16x2(p0, p1);
-          ph[kb][r >> 3][(r & 7) >> 1] = pp;
-          lsum[kb] = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pp), ones, lsum[kb], false);
+          const float h0 = __uint_as_float(__float_as_uint(p0) & 0xffffe000u);
+          const float h1 = __uint_as_float(__float_as_uint(p1) & 0xffffe000u);
+          ph[kb][r >> 3][(r & 7) >> 1] = pack_f16x2(h0, h1);
+          pl[kb][r >> 3][(r & 7) >> 1] = pack_f16x2(p0 - h0, p1 - h1);
+          lsum += p0 + p1;
         }
-      l_run += lsum[0] + lsum[1];
-      // O^T += V^T P^T over 4 blocks of 16 slots
+      l_run += lsum;
+      // O^T += V^T (P_hi + P_lo)^T over 4 blocks of 16 slots
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const f16x8 bp = __builtin_bit_cast(f16x8, make_uint4(ph[kb][half][0], ph[kb][half][1], ph[kb][half][2], ph[kb][half][3]));
+          const f16x8 bh = __builtin_bit_cast(f16x8, make_uint4(ph[kb][half][0], ph[kb][half][1], ph[kb][half][2], ph[kb][half][3]));
+          const f16x8 bl = __builtin_bit_cast(f16x8, make_uint4(pl[kb][half][0], pl[kb][half][1], pl[kb][half][2], pl[kb][half][3]));
           const int kcol = (kb * 2 + half) * 16;
+          f16x8 a[4];
 #pragma unroll
           for (int fd = 0; fd < 4; ++fd) {
-            const f16x8 a = *reinterpret_cast<const f16x8*>(&Vt[grp][st][v_row0 + fd * 32 * VSTR + kcol]);
-            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, bp, oacc[fd], 0, 0, 0);
+            a[fd] = *reinterpret_cast<const f16x8*>(&Vt[grp][st][v_row0 + fd * 32 * VSTR + kcol]);
+            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[fd], bh, oacc[fd], 0, 0, 0);
           }
+#pragma unroll
+          for (int fd = 0; fd < 4; ++fd) oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[fd], bl, oacc[fd], 0, 0, 0);
         }
     };
     if (it < ntiles && j0 <= wmax) {  // wave-uniform: skip tiles wholly above this wave's diagonal
@@ -339,8 +349,8 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       uint2 w;
-      w.x = pack_bf16x2(oacc[fd][4 * rq] * inv, oacc[fd][4 * rq + 1] * inv);
-      w.y = pack_bf16x2(oacc[fd][4 * rq + 2] * inv, oacc[fd][4 * rq + 3] * inv);
+      w.x = pack_f16x2_sat(oacc[fd][4 * rq] * inv, oacc[fd][4 * rq + 1] * inv);
+      w.y = pack_f16x2_sat(oacc[fd][4 * rq + 2] * inv, oacc[fd][4 * rq + 3] * inv);
       // four consecutive dims stay contiguous in fragment order as well
       const int col = fd * 32 + 8 * rq + 4 * hl;
       bf16_t* dst = o_frag ? o + frag_index(static_cast<int>(row), h * DH + col, static_cast<int>(qstride)) : orow + col;

@@ -36,6 +36,32 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> fp16, round to nearest even, saturating at +-65504 (the largest
+// finite fp16) instead of overflowing to infinity; NaN stays NaN.  The
+// attention output and the SwiGLU product (the A operands of o_proj and down)
+// are stored this way: 11 significant bits against bf16's 8.
+__device__ __forceinline__ float sat_f16(float v) { return fabsf(v) > 65504.f ? copysignf(65504.f, v) : v; }
+__device__ __forceinline__ uint16_t f32_to_f16_sat(float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<_Float16>(sat_f16(v)));
+}
+__device__ __forceinline__ uint32_t pack_f16x2_sat(float lo, float hi) {
+  const f16x2_t v = {static_cast<_Float16>(sat_f16(lo)), static_cast<_Float16>(sat_f16(hi))};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 32x32x16 MFMA on 16-bit operands held as raw bits: fp16 (F16) or bf16
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  if constexpr (F16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b), c, 0,
+                                                  0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
 // 2^x with the bare v_exp_f32 (results below the normal range flush to 0).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -103,13 +129,18 @@ hipError_t launch_rmsnorm(const void* in, int in_f32, const void* gain, int gain
 // (group = rows for a plain copy); rows and group are multiples of 32 and
 // K % 16 == 0.  group = 0 is the rotary-pair order of projection heads: in
 // every 128-row head, dims x and x + 64 land on rows 2x and 2x + 1.
+// to_f16 = 1 converts every element bf16 -> fp16 on the way (saturating at
+// +-65504; exact for magnitudes in [2^-17, 65504], finer bf16 values round to
+// fp16's subnormal spacing 2^-24).
 hipError_t launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int group,
-                            int group_stride, hipStream_t s);
+                            int group_stride, int to_f16, hipStream_t s);
 
-// Tiled bf16 MFMA GEMM, C = A[M,K] . W[N,K]^T with a fused epilogue; A
+// Tiled 16-bit MFMA GEMM, C = A[M,K] . W[N,K]^T with a fused epilogue; A
 // row-major, W in fragment order (K % 128 == 0).  The QKV weight is in
 // rotary-pair order (see launch_pack_rows), the gate/up weight interleaved in
 // 64-row blocks; the epilogues write q, the cache and h in the natural order.
+// QKV and gate/up multiply bf16 operands; o_proj and down fp16 ones (the
+// attention output and h are fp16, Wo and Wdown converted at creation).
 struct QkvEpilogue {
   bf16_t* q;               // [M, H*dh]
   bf16_t* k_cache;         // [B, Hkv, max_pos, dh]
@@ -122,14 +153,14 @@ struct QkvEpilogue {
 
 hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,
                            const QkvEpilogue& ep, hipStream_t s);
-// out_f32[M,N] = A.W^T + resid_bf16[M,N]
+// out_f32[M,N] = A.W^T + resid_bf16[M,N]   (A, W fp16)
 hipError_t launch_gemm_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
                                     const bf16_t* resid, float* out, hipStream_t s);
-// out_bf16[M,N] = bf16(A.W^T + resid_f32[M,N])
+// out_bf16[M,N] = bf16(A.W^T + resid_f32[M,N])   (A, W fp16)
 hipError_t launch_gemm_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
                                      const float* resid, bf16_t* out, hipStream_t s);
 // W is the gate/up matrix interleaved in blocks of 64 rows [gate 64 | up 64]
-// (N = 2f); out[M, f] = bf16(SiLU(gate) * up)
+// (N = 2f); out[M, f] = fp16(SiLU(gate) * up)
 hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, int K,
                               bf16_t* out, hipStream_t s);
 
@@ -138,8 +169,9 @@ int device_cu_count();
 
 // Weight-streaming versions of the same four GEMMs for M <= 64 tokens: A and
 // W both in fragment order (A holds ceil(M/32)*32 rows; rows >= M are never
-// written out, whatever they hold).  The SwiGLU output h is written in
-// fragment order, ready to be the A operand of the down projection.
+// written out, whatever they hold), in the same operand formats as the tiled
+// ones.  The SwiGLU output h (fp16) is written in fragment order, ready to be
+// the A operand of the down projection.
 // Scratch for column groups split between workgroups: part holds part_len
 // floats (skinny_scratch_floats() always suffices; a call with G workgroups
 // needs 2 G x (1 or 2 blocks) x (1 or 2 token blocks) x 1024), cnt cnt_len
@@ -173,7 +205,8 @@ hipError_t launch_skinny_f32out(const bf16_t* A, const bf16_t* W, int M, int N, 
 // Causal flash attention over the cache for prefill (bf16, dh = 128).
 // q/o [B*T, H*128]; the query of token m sees cache slots 0..pos[m], or with
 // bidir = 1 slots 0..max over t of pos[b*T + t] (its sequence's largest).
-// o_frag = 1 writes o in fragment order instead of row-major.
+// o is fp16 (saturating at +-65504); o_frag = 1 writes it in fragment order
+// instead of row-major.
 hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                                const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
                                int n_kv_heads, int max_pos, int bidir, hipStream_t s);
@@ -181,7 +214,7 @@ hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf1
 // Decode attention (bf16, dh = 128) for one query per sequence, split over
 // the cache when the grid would otherwise be small, followed by the merge of
 // the splits (n_split > 1 only).  part holds B*H*n_split*(128+2) floats;
-// o_frag as for the prefill kernel.
+// o (fp16) and o_frag as for the prefill kernel.
 int decode_attn_splits(int max_pos, int B, int n_heads, int n_kv_heads);
 hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                               const int32_t* pos, bf16_t* o, int o_frag, float* part, int n_split,

@@ -1,4 +1,4 @@
-// Tiled bf16 MFMA GEMM for the prefill projections, C = A[M,K] . W[N,K]^T,
+// Tiled 16-bit MFMA GEMM for the prefill projections, C = A[M,K] . W[N,K]^T,
 // with the layer's elementwise work fused into the epilogue:
 //   QKV     rotate-half RoPE of q and k at each token's position, bf16 round,
 //           q -> scratch, k and v -> their cache slot (no concatenation pass);
@@ -7,8 +7,13 @@
 //   RESID32 X' = x + O Wo^T kept in fp32 (the residual add of the attention half);
 //   SWIGLU  h = SiLU(gate) * up from one GEMM over the gate/up matrix
 //           interleaved in 64-row blocks [gate 64 | up 64], so a 128-wide wave
-//           tile holds gate column j and up column j;
+//           tile holds gate column j and up column j; h is stored as fp16;
 //   RESID16 y = bf16(X' + h Wdown^T) (the residual add of the MLP half).
+// QKV and gate/up multiply bf16 operands (v_mfma_f32_32x32x16_bf16); o_proj
+// and down multiply fp16 ones (v_mfma_f32_32x32x16_f16: the attention output
+// and h are fp16, with 3 more significant bits, and Wo / Wdown are converted
+// to fp16 at creation).  The kernel moves operands as raw 16-bit data, so the
+// two differ only in the MFMA instruction.
 //
 // Sources: "LMDrive LLM core inference unit" page, §2.3 LlamaAttention (q/k/v
 // projections, RoPE, cache append, o_proj) and §2.4 LlamaMLP
@@ -17,7 +22,7 @@
 // page §2.2 (gate branch activated, up branch linear).
 //
 // gfx950 design.  256 threads = 4 wavefronts over a BM x BN tile, each wave
-// owning a block of 32x32 accumulator tiles of v_mfma_f32_32x32x16_bf16:
+// owning a block of 32x32 accumulator tiles of the 32x32x16 MFMA:
 //   * BM = 256: a 2x2 wave grid, wave tile 128 x (BN/2) (QKV: 256 x 192);
 //   * BM = 128: a 1x4 wave grid, wave tile 128 x (BN/4) (o_proj and down:
 //     128 x 256 or 128 x 512; gate/up: 128 x 512; QKV at large M: 128 x 512).  No two waves load the
@@ -81,9 +86,13 @@ __device__ __forceinline__ void tile_coords(int M, int N, int BM, int BN, int& m
 
 __device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
 
+// the residual GEMMs (o_proj, down) multiply fp16 operands, QKV and gate/up bf16
+template <int EPI> constexpr bool kF16Operands = EPI == EPI_RESID32 || EPI == EPI_RESID16;
+
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Wp,
                                                     int M, int N, int K, EpiArgs ep) {
+  constexpr bool F16 = kF16Operands<EPI>;
   constexpr int WM = BM == 256 ? 2 : 1, WN = 4 / WM;  // wave grid
   constexpr int TM = BM / WM, TN = BN / WN;           // wave tile
   constexpr int FM = TM / 32, FN = TN / 32;
@@ -178,7 +187,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
 #pragma unroll
       for (int m = 0; m < FM * FN; ++m) {
         const int i = m / FN, j = m % FN;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], __builtin_bit_cast(bf16x8, bq[st][kk][j]), acc[i][j], 0, 0, 0);
+        acc[i][j] = mfma_32x32x16<F16>(fa[cur][i], __builtin_bit_cast(bf16x8, bq[st][kk][j]), acc[i][j]);
         if (m < FM) fa[cur ^ 1][m] = kk < 3 ? frag_a(st, kk + 1, m) : frag_a(st ^ 1, 0, m);
         if (m >= FM * FN - FN) b_load(st, kt + 2, kk, m - (FM * FN - FN));
         // A chunk i (k step i / 4): stored to LDS, then its register is
@@ -276,7 +285,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
 #pragma unroll
         for (int e = 0; e < 8; ++e) h[e] = silu(x1[e]) * x2[e];
         const int f = N >> 1;
-        *reinterpret_cast<uint4*>(static_cast<bf16_t*>(ep.out) + static_cast<size_t>(row) * f + (col0 >> 7) * 64 + c) = bf8(h);
+        *reinterpret_cast<uint4*>(static_cast<bf16_t*>(ep.out) + static_cast<size_t>(row) * f + (col0 >> 7) * 64 + c) =
+            make_uint4(pack_f16x2_sat(h[0], h[1]), pack_f16x2_sat(h[2], h[3]), pack_f16x2_sat(h[4], h[5]),
+                       pack_f16x2_sat(h[6], h[7]));
       }
     } else {
       // task: row R, columns 8c .. 8c + 7

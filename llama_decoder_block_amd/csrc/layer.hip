@@ -348,21 +348,22 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
     // fragment order; rows of a 32-row-aligned range sit where they would in
     // row-major order, so q, k and v rows are converted straight into their
     // place in the concatenated matrix (each head in rotary-pair order, so
-    // that a rotation's two inputs are neighbouring output columns)
+    // that a rotation's two inputs are neighbouring output columns).  Wo and
+    // Wdown become fp16: their activations (the attention output, h) are fp16.
     const int di = static_cast<int>(d), fi = static_cast<int>(f), nqi = static_cast<int>(nq),
               nkvi = static_cast<int>(nkv);
     auto* wqkv = static_cast<bf16_t*>(L->wqkv);
     auto* wgu = static_cast<bf16_t*>(L->wgu);
     auto src = [](const void* p) { return static_cast<const bf16_t*>(p); };
-    HIP_OR_FAIL(launch_pack_rows(src(w->wq), nqi, di, wqkv, 0, 0, s), "convert wq");
-    HIP_OR_FAIL(launch_pack_rows(src(w->wk), nkvi, di, wqkv + nq * d, 0, 0, s), "convert wk");
-    HIP_OR_FAIL(launch_pack_rows(src(w->wv), nkvi, di, wqkv + (nq + nkv) * d, 0, 0, s), "convert wv");
-    HIP_OR_FAIL(launch_pack_rows(src(w->wo), di, nqi, static_cast<bf16_t*>(L->wo), di, di, s), "convert wo");
-    HIP_OR_FAIL(launch_pack_rows(src(w->w_down), di, fi, static_cast<bf16_t*>(L->wd), di, di, s), "convert w_down");
+    HIP_OR_FAIL(launch_pack_rows(src(w->wq), nqi, di, wqkv, 0, 0, 0, s), "convert wq");
+    HIP_OR_FAIL(launch_pack_rows(src(w->wk), nkvi, di, wqkv + nq * d, 0, 0, 0, s), "convert wk");
+    HIP_OR_FAIL(launch_pack_rows(src(w->wv), nkvi, di, wqkv + (nq + nkv) * d, 0, 0, 0, s), "convert wv");
+    HIP_OR_FAIL(launch_pack_rows(src(w->wo), di, nqi, static_cast<bf16_t*>(L->wo), di, di, 1, s), "convert wo");
+    HIP_OR_FAIL(launch_pack_rows(src(w->w_down), di, fi, static_cast<bf16_t*>(L->wd), di, di, 1, s), "convert w_down");
     // 64-row blocks: rows [128 j, 128 j + 64) = gate rows [64 j, 64 j + 64),
     // rows [128 j + 64, 128 j + 128) = up rows [64 j, 64 j + 64)
-    HIP_OR_FAIL(launch_pack_rows(src(w->w_gate), fi, di, wgu, 64, 128, s), "convert w_gate");
-    HIP_OR_FAIL(launch_pack_rows(src(w->w_up), fi, di, wgu + 64 * d, 64, 128, s), "convert w_up");
+    HIP_OR_FAIL(launch_pack_rows(src(w->w_gate), fi, di, wgu, 64, 128, 0, s), "convert w_gate");
+    HIP_OR_FAIL(launch_pack_rows(src(w->w_up), fi, di, wgu + 64 * d, 64, 128, 0, s), "convert w_up");
   } else {
     char* qkv = static_cast<char*>(L->wqkv);
     HIP_OR_FAIL(hipMemcpyAsync(qkv, w->wq, nq * d * es, dd, s), "copy wq");

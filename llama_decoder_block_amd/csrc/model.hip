@@ -501,7 +501,7 @@ int llama_model_create(const llama_model_config* cfg, const llama_model_weights*
     if (e == hipSuccess) e = hipMemcpyAsync(tmp, w->lm_head, V * d * es, dd, s);
     if (e == hipSuccess)
       e = launch_pack_rows(static_cast<const bf16_t*>(tmp), m->Vp, static_cast<int>(d), static_cast<bf16_t*>(m->lm),
-                           m->Vp, m->Vp, s);
+                           m->Vp, m->Vp, 0, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     (void)hipFree(tmp);
     MODEL_HIP_FAIL(e, "convert LM head");

@@ -3,23 +3,27 @@
 // Source: "LMDrive LLM core inference unit" page, §2.1 LlamaRMSNorm (fp32
 // statistics, eps added to the mean square inside the root, learnable gain),
 // and the "LLM mechanics lecture notes", §02.3 RMSNorm.  The gain multiplies
-// in fp32 and the result is rounded once to the output type.
+// after normalising and the result is rounded once to the output type.
+//
+// Precision.  A bf16 output is the rounding point of the matrix products
+// that follow, and bf16 inputs repeat values (8 significant bits): when a
+// row's 1/rms lands a repeated input value within ~2^-24 of a bf16 rounding
+// midpoint, fp32 arithmetic rounds every copy of it the wrong way at once,
+// and the whole row's projections move.  So for a bf16 output the sum of
+// squares (exact products), 1/sqrt and the scaling run in fp64, and the fp64
+// result is rounded to bf16 correctly (to odd into fp32, then to nearest even:
+// no double rounding).  An fp32 output (the fp32 layer) stays in fp32.
 //
 // One 64-wide wavefront per row.  Each lane keeps its share of the row in
 // registers (NV vectors of 8 elements, 16-byte bf16 or 32-byte fp32 loads,
 // consecutive lanes on consecutive vectors so a wave reads 1 KB contiguous per
 // load), so HBM sees exactly one read of x and one write of out.  The sum of
-// squares is reduced in fp32 with wavefront shuffles; no LDS, no barriers.
+// squares is reduced with wavefront shuffles; no LDS, no barriers.
 #include "common.h"
 
 namespace llama {
 namespace {
 
-__device__ __forceinline__ void load8(const bf16_t* p, float v[8]) {
-  uint4 u = *reinterpret_cast<const uint4*>(p);
-  v[0] = lo_bf16(u.x); v[1] = hi_bf16(u.x); v[2] = lo_bf16(u.y); v[3] = hi_bf16(u.y);
-  v[4] = lo_bf16(u.z); v[5] = hi_bf16(u.z); v[6] = lo_bf16(u.w); v[7] = hi_bf16(u.w);
-}
 __device__ __forceinline__ void load8(const float* p, float v[8]) {
   float4 a = *reinterpret_cast<const float4*>(p);
   float4 b = *reinterpret_cast<const float4*>(p + 4);
@@ -35,12 +39,71 @@ __device__ __forceinline__ void store8(float* p, const float v[8]) {
   *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
+// fp64 -> fp32 rounded to odd: truncate, then set the last bit if anything
+// was cut.  A later fp32 -> bf16 rounding to nearest even then gives exactly
+// the fp64 -> bf16 rounding (fp32 keeps 16 more bits than bf16; Boldo and
+// Melquiond, "Emulation of FMA and correctly rounded sums: proved algorithms
+// using rounding to odd", IEEE Trans. Computers 2008).
+__device__ __forceinline__ float f64_to_f32_odd(double v) {
+  const float t = __double2float_rz(v);
+  return __uint_as_float(__float_as_uint(t) | (static_cast<double>(t) != v ? 1u : 0u));
+}
+
+// Statistics and scaling type: fp64 for a bf16 output, fp32 for an fp32 one.
+template <typename TOut> struct NormAcc { typedef double type; };
+template <> struct NormAcc<float> { typedef float type; };
+
+// 8 consecutive elements as loaded (bf16 stays packed: half the registers)
+template <typename T> struct Raw8;
+template <> struct Raw8<bf16_t> {
+  uint4 u;
+  __device__ __forceinline__ void load(const bf16_t* p) { u = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ float operator[](int e) const {
+    const uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+    return (e & 1) ? hi_bf16(w) : lo_bf16(w);
+  }
+};
+template <> struct Raw8<float> {
+  float v[8];
+  __device__ __forceinline__ void load(const float* p) { load8(p, v); }
+  __device__ __forceinline__ float operator[](int e) const { return v[e]; }
+};
+
+// g * (x * inv) for 8 elements, rounded once to the output type
+template <typename A, typename X, typename G>
+__device__ __forceinline__ void scale8(const X& x, const G& gv, A inv, float out[8]) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const A v = static_cast<A>(gv[e]) * (static_cast<A>(x[e]) * inv);
+    if constexpr (sizeof(A) == 8)
+      out[e] = f64_to_f32_odd(v);
+    else
+      out[e] = v;
+  }
+}
+
+template <typename A>
+__device__ __forceinline__ A wave_sum(A v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
 __device__ __forceinline__ float load1(const bf16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float load1(const float* p) { return *p; }
 __device__ __forceinline__ void store1(bf16_t* p, float v) { *p = f32_to_bf16(v); }
 __device__ __forceinline__ void store1(float* p, float v) { *p = v; }
 
 constexpr int kRowsPerBlock = 4;  // 4 waves, one row each
+
+// 1 / sqrt(ss / d + eps): fp32 with the hardware rsqrt, or fp64
+template <typename A> __device__ __forceinline__ A inv_rms(A ss, int d, float eps);
+template <> __device__ __forceinline__ float inv_rms<float>(float ss, int d, float eps) {
+  return rsqrtf(ss / static_cast<float>(d) + eps);
+}
+template <> __device__ __forceinline__ double inv_rms<double>(double ss, int d, float eps) {
+  return 1.0 / sqrt(ss / static_cast<double>(d) + static_cast<double>(eps));
+}
 
 // d % 8 == 0 and d <= NV * 512.  FRAG: bf16 out in fragment order (the
 // 16-byte vector of k = 8 vi .. 8 vi + 7 stays contiguous there).
@@ -55,34 +118,36 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const TIn* __restrict_
   const TIn* x = in + static_cast<size_t>(row) * d;
   const int nvec = d >> 3;
   // the row and the gain are fetched together (one memory round trip)
-  float v[NV][8], gv[NV][8];
+  Raw8<TIn> v[NV];
+  Raw8<TG> gv[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int vi = lane + j * kWave;
     if (vi < nvec) {
-      load8(x + vi * 8, v[j]);
-      load8(g + vi * 8, gv[j]);
+      v[j].load(x + vi * 8);
+      gv[j].load(g + vi * 8);
     }
   }
-  float ss = 0.f;
+  typedef typename NormAcc<TOut>::type A;
+  A ss = 0;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int vi = lane + j * kWave;
     if (vi < nvec) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
+      for (int e = 0; e < 8; ++e) ss += static_cast<A>(v[j][e]) * static_cast<A>(v[j][e]);
     }
   }
-  ss = warp_sum(ss);
-  const float inv = rsqrtf(ss / static_cast<float>(d) + eps);
+  ss = wave_sum(ss);
+  const A inv = inv_rms<A>(ss, d, eps);
   TOut* y = out + (FRAG ? 0 : static_cast<size_t>(row) * d);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int vi = lane + j * kWave;
     if (vi < nvec) {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) v[j][e] = gv[j][e] * (v[j][e] * inv);
-      store8(y + (FRAG ? frag_index(row, vi * 8, d) : vi * 8), v[j]);
+      float r[8];
+      scale8(v[j], gv[j], inv, r);
+      store8(y + (FRAG ? frag_index(row, vi * 8, d) : vi * 8), r);
     }
   }
 }
@@ -95,33 +160,35 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const TIn* __restrict_
 template <typename TIn, typename TG, typename TOut, int NV, bool FRAG>
 __global__ __launch_bounds__(256) void rmsnorm_row_kernel(const TIn* __restrict__ in, const TG* __restrict__ g,
                                                           TOut* __restrict__ out, int d, float eps) {
-  __shared__ float part[4];
+  typedef typename NormAcc<TOut>::type A;
+  __shared__ A part[4];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const TIn* x = in + static_cast<size_t>(row) * d;
-  float v[NV][8], gv[NV][8];
+  Raw8<TIn> v[NV];
+  Raw8<TG> gv[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int vi = tid + j * 256;
-    load8(x + vi * 8, v[j]);
-    load8(g + vi * 8, gv[j]);
+    v[j].load(x + vi * 8);
+    gv[j].load(g + vi * 8);
   }
-  float ss = 0.f;
+  A ss = 0;
 #pragma unroll
   for (int j = 0; j < NV; ++j)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss += v[j][e] * v[j][e];
-  ss = warp_sum(ss);
+    for (int e = 0; e < 8; ++e) ss += static_cast<A>(v[j][e]) * static_cast<A>(v[j][e]);
+  ss = wave_sum(ss);
   if (lane == 0) part[wave] = ss;
   __syncthreads();
   ss = (part[0] + part[1]) + (part[2] + part[3]);
-  const float inv = rsqrtf(ss / static_cast<float>(d) + eps);
+  const A inv = inv_rms<A>(ss, d, eps);
   TOut* y = out + (FRAG ? 0 : static_cast<size_t>(row) * d);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
     const int vi = tid + j * 256;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[j][e] = gv[j][e] * (v[j][e] * inv);
-    store8(y + (FRAG ? frag_index(row, vi * 8, d) : vi * 8), v[j]);
+    float r[8];
+    scale8(v[j], gv[j], inv, r);
+    store8(y + (FRAG ? frag_index(row, vi * 8, d) : vi * 8), r);
   }
 }
 
@@ -135,15 +202,22 @@ __global__ __launch_bounds__(256) void rmsnorm_any_kernel(const TIn* __restrict_
   const int row = blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
   if (row >= rows) return;
   const TIn* x = in + static_cast<size_t>(row) * d;
-  float ss = 0.f;
+  typedef typename NormAcc<TOut>::type A;
+  A ss = 0;
   for (int i = lane; i < d; i += kWave) {
-    const float a = load1(x + i);
+    const A a = static_cast<A>(load1(x + i));
     ss += a * a;
   }
-  ss = warp_sum(ss);
-  const float inv = rsqrtf(ss / static_cast<float>(d) + eps);
+  ss = wave_sum(ss);
+  const A inv = inv_rms<A>(ss, d, eps);
   TOut* y = out + static_cast<size_t>(row) * d;
-  for (int i = lane; i < d; i += kWave) store1(y + i, load1(g + i) * (load1(x + i) * inv));
+  for (int i = lane; i < d; i += kWave) {
+    const A v = static_cast<A>(load1(g + i)) * (static_cast<A>(load1(x + i)) * inv);
+    if constexpr (sizeof(A) == 8)
+      store1(y + i, f64_to_f32_odd(v));
+    else
+      store1(y + i, v);
+  }
 }
 
 template <typename TIn, typename TG, typename TOut, bool FRAG = false>

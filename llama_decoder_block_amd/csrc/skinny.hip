@@ -7,8 +7,10 @@
 //
 // gfx950 design.  Both operands are in fragment order, so every load is one
 // contiguous 1 KB wavefront load straight into registers: a 32 x 16 weight
-// fragment (A operand of v_mfma_f32_32x32x16_bf16, rows = output features)
-// and a 32-token x 16 activation fragment (B operand, columns = tokens).
+// fragment (A operand of the 32x32x16 MFMA, rows = output features) and a
+// 32-token x 16 activation fragment (B operand, columns = tokens).  QKV and
+// gate/up multiply bf16 operands, o_proj and down fp16 ones (the attention
+// output and h are fp16), as in the tiled GEMMs.
 //
 // Work split.  A column group is NB 32-row blocks of W; its work is K/16 k
 // steps.  The groups' k steps are laid end to end and the grid's G workgroups
@@ -56,6 +58,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
                                                          const bf16_t* __restrict__ Wp, int M, int N,
                                                          int K, int G, SkinnyArgs ep) {
   constexpr int NT = NB * TB;  // 32 x 32 tiles per column group
+  // o_proj and down multiply fp16 operands, the others bf16
+  constexpr bool F16 = EPI == SK_RESID32 || EPI == SK_RESID16;
   __shared__ float red[NW][NT][64][17];
   __shared__ unsigned s_last;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -126,9 +130,9 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
         float hv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) hv[e] = silu(v[0][4 * r4 + e]) * v[1][4 * r4 + e];
-        bf16_t* out = static_cast<bf16_t*>(ep.out);
+        bf16_t* out = static_cast<bf16_t*>(ep.out);  // fp16 h
         *reinterpret_cast<uint2*>(out + frag_index(tok, c, f)) =
-            make_uint2(pack_bf16x2(hv[0], hv[1]), pack_bf16x2(hv[2], hv[3]));
+            make_uint2(pack_f16x2_sat(hv[0], hv[1]), pack_f16x2_sat(hv[2], hv[3]));
       } else if constexpr (EPI == SK_F32OUT) {
         // plain fp32 rows (LM head logits): columns past n_valid are padding
         float* out = static_cast<float*>(ep.out) + static_cast<size_t>(tok) * ep.ld;
@@ -205,9 +209,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
         for (int j = 0; j < NB; ++j)
 #pragma unroll
           for (int t = 0; t < TB; ++t)
-            acc[j][t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wv[d][j]),
-                                                                __builtin_bit_cast(bf16x8, xv[d][t]),
-                                                                acc[j][t], 0, 0, 0);
+            acc[j][t] = mfma_32x32x16<F16>(__builtin_bit_cast(bf16x8, wv[d][j]), __builtin_bit_cast(bf16x8, xv[d][t]),
+                                           acc[j][t]);
         issue(d, st + d + DEPTH);
         __builtin_amdgcn_sched_barrier(0);
       }

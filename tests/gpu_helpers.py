@@ -58,39 +58,52 @@ def bf16_ulp(a):
     return np.where(a > 0, np.ldexp(1.0, e - 8), 0.0)
 
 
-def assert_bf16_output(got, ref, what=""):
-    """The bf16 gate: max |got - ref| <= 0.02 x RMS(ref), where ref is the
-    rounding-point oracle's unrounded output.  Printed beside it: the error
-    beyond the half bf16 ulp that rounding an exact result to bf16 costs (a
-    diagnostic of the compute error alone; not the gate)."""
+def _gate(got, ref, what, extra=""):
+    """max |got - ref| <= 0.02 x RMS(ref), element by element, where ref is
+    the oracle's unrounded value.  The one exception is an element whose
+    correctly rounded bf16 value is itself farther from ref than that (the
+    format cannot do better there: e.g. |ref| >= 8 at RMS 1.4): it must then
+    be exactly that value.  Returns the raw max |err| / RMS."""
     got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
-    e = rel_err(got, ref)
     r = max(rms(ref), 1e-30)
-    beyond = float(np.max(np.maximum(np.abs(got - ref) - bf16_ulp(ref) / 2, 0.0)) / r)
-    mean = float(np.mean(np.abs(got - ref)) / r)
-    print(f"  {what}: max|err|/rms = {e:.5f} (gate {BF16_RMS_GATE}); mean {mean:.2e}; "
-          f"beyond the output's half ulp {beyond:.5f}", flush=True)
+    err = np.abs(got - ref)
+    nearest = O.bf16_round(ref)
+    tol = BF16_RMS_GATE * r
+    beyond_format = np.abs(nearest - ref) > tol
+    ok = (err <= tol) | (beyond_format & (got == nearest))
+    e = float(np.max(err) / r)
+    beyond = float(np.max(np.maximum(err - bf16_ulp(ref) / 2, 0.0)) / r)
+    mean = float(np.mean(err) / r)
+    print(f"  {what}: max|err|/rms = {e:.5f} (gate {BF16_RMS_GATE}); mean {mean:.2e}; beyond the "
+          f"output's half ulp {beyond:.5f}; {int(beyond_format.sum())} entries whose nearest bf16 is "
+          f"beyond the gate{extra}", flush=True)
     assert np.all(np.isfinite(got)), what
-    assert e <= BF16_RMS_GATE, f"{what}: max|err|/rms = {e} > {BF16_RMS_GATE}"
+    bad = np.nonzero(~ok)
+    assert bad[0].size == 0, (f"{what}: {bad[0].size} elements off by more than {BF16_RMS_GATE} x RMS, e.g. "
+                              f"index {tuple(int(i[0]) for i in bad)}: got {got[tuple(i[0] for i in bad)]}, "
+                              f"oracle {ref[tuple(i[0] for i in bad)]}")
+    return e
+
+
+def assert_bf16_output(got, ref, what=""):
+    """The bf16 gate on a layer output (see _gate), against the rounding-point
+    oracle's unrounded output.  The error beyond the half bf16 ulp that
+    rounding an exact result costs is printed as a diagnostic."""
+    return _gate(got, ref, what)
 
 
 def assert_bf16_cache(got, exact, rounded, what=""):
-    """Cache entries written by a bf16 call.  Gate: max |got - exact| <=
-    0.02 x RMS(exact) against the oracle's unrounded keys/values (kv_exact).
-    Also: both sides store the bf16 rounding of values that agree to
-    accumulation noise, so at most 5% of the entries may differ from the
-    oracle's own rounding at all (a systematic rounding error, such as
-    truncation or double rounding, flips far more)."""
+    """Cache entries written by a bf16 call: the same gate (see _gate) against
+    the oracle's unrounded keys/values (kv_exact).  Also: both sides store
+    the bf16 rounding of values that agree to accumulation noise, so at most
+    5% of the entries may differ from the oracle's own rounding at all (a
+    systematic rounding error, such as truncation or double rounding, flips
+    far more)."""
     got, exact, rounded = (np.asarray(a, np.float64) for a in (got, exact, rounded))
-    e = rel_err(got, exact)
     flips = int(np.count_nonzero(got != rounded))
-    over_ulp = float(np.max(np.abs(got - rounded) / np.maximum(bf16_ulp(rounded), 1e-30)))
-    print(f"  {what}: max|err|/rms = {e:.5f} (gate {BF16_RMS_GATE}) against the unrounded oracle; "
-          f"{flips}/{got.size} entries differ from its bf16 rounding, by at most {over_ulp:.2f} ulp",
-          flush=True)
-    assert np.all(np.isfinite(got)), what
-    assert e <= BF16_RMS_GATE, f"{what}: max|err|/rms = {e} > {BF16_RMS_GATE}"
+    e = _gate(got, exact, what, f"; {flips}/{got.size} entries differ from the oracle's bf16 rounding")
     assert flips <= 0.05 * got.size, f"{what}: {flips} of {got.size} entries differ"
+    return e
 
 
 def assert_f32(got, ref, what=""):
