@@ -279,6 +279,56 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
     return y, kc, vc
 
 
+# --------------------------------------------------------------------------
+# Paged KV cache  ["Llama MLP deep dive" §6.4 (PagedAttention named as the
+# KV-memory lever); Notes Ch.04 (the cache as [layers, 2, B, T, Hkv, dh]
+# memory that grows with context)]
+# --------------------------------------------------------------------------
+
+def gather_pages(pool, block_table, page_size, capacity):
+    """The contiguous cache [B, Hkv, capacity, dh] a paged one stands for.
+
+    pool [n_pages, Hkv, page_size, dh]; block_table [B, blocks_per_seq] of
+    page ids: slot p of sequence b lives in page block_table[b, p // page_size]
+    at row p % page_size.  capacity <= blocks_per_seq * page_size."""
+    pool = _f64(pool)
+    bt = np.asarray(block_table, dtype=np.int64)
+    B, nblk = bt.shape
+    n_pages, Hkv, ps, dh = pool.shape
+    assert ps == page_size and capacity <= nblk * page_size
+    out = np.zeros((B, Hkv, capacity, dh))
+    for b in range(B):
+        for p in range(capacity):
+            out[b, :, p] = pool[bt[b, p // page_size], :, p % page_size]
+    return out
+
+
+def scatter_pages(cache, pool, block_table, page_size, slots):
+    """Write slots[b] (a list of positions) of the contiguous cache [B, Hkv, S,
+    dh] back into a copy of the page pool; returns the new pool."""
+    pool = _f64(pool).copy()
+    cache = _f64(cache)
+    bt = np.asarray(block_table, dtype=np.int64)
+    for b, ps_ in enumerate(slots):
+        for p in ps_:
+            pool[bt[b, p // page_size], :, p % page_size] = cache[b, :, p]
+    return pool
+
+
+def decoder_layer_paged(x, positions, weights, k_pool, v_pool, block_table, page_size, capacity, **kw):
+    """The decoder layer over a paged cache: gather the pages into the
+    contiguous layout, run decoder_layer, write the new tokens' slots back.
+    Returns (y, k_pool', v_pool'); kv_exact (if given) as in decoder_layer."""
+    x = _f64(x)
+    pos = np.asarray(_f64(positions), dtype=np.int64).reshape(x.shape[0], x.shape[1])
+    kc = gather_pages(k_pool, block_table, page_size, capacity)
+    vc = gather_pages(v_pool, block_table, page_size, capacity)
+    y, kc, vc = decoder_layer(x, pos, weights, kc, vc, **kw)
+    slots = [list(pos[b]) for b in range(pos.shape[0])]
+    return (y, scatter_pages(kc, k_pool, block_table, page_size, slots),
+            scatter_pages(vc, v_pool, block_table, page_size, slots))
+
+
 def decoder_layer_decode(x, positions, weights, k_cache, v_cache, **kw):
     """One decode step: x [B, d], positions [B] (= each sequence's cache length).
     The same layer with T = 1; returns (y [B, d], k_cache', v_cache')."""

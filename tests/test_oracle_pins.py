@@ -543,3 +543,59 @@ def test_bf16_points_pin_catches_a_dropped_rounding(dropped, monkeypatch):
     assert len(calls) == len(_ROUNDING_POINTS)
     diff = max(np.max(np.abs(y - yr)), np.max(np.abs(k2 - kr)), np.max(np.abs(v2 - vr)))
     assert diff > 1e-6, f"dropping the rounding of {_ROUNDING_POINTS[dropped]} went unnoticed ({diff})"
+
+
+# ----------------------------------------------------------- paged KV cache
+
+def test_gather_pages_hand_worked():
+    """Two sequences, pages of 2 slots, one kv head of width 1: the page pool
+    holds the values 10 * page + row, and the block tables [2, 0] and [1, 3]
+    lay sequence 0's slots 0..3 over pages 2, 2, 0, 0 and sequence 1's over
+    1, 1, 3, 3."""
+    pool = np.array([[[[10 * pg + r] for r in range(2)]] for pg in range(4)], dtype=np.float64)  # [4,1,2,1]
+    got = O.gather_pages(pool, [[2, 0], [1, 3]], 2, 4)
+    np.testing.assert_array_equal(got[:, 0, :, 0], [[20, 21, 0, 1], [10, 11, 30, 31]])
+
+
+def test_scatter_then_gather_is_identity_on_written_slots():
+    rng = _rng(70)
+    B, Hkv, ps, dh, nblk = 3, 2, 4, 5, 3
+    perm = rng.permutation(B * nblk + 2)[:B * nblk].reshape(B, nblk)   # distinct pages, two spare
+    pool = rng.standard_normal((B * nblk + 2, Hkv, ps, dh))
+    cache = rng.standard_normal((B, Hkv, ps * nblk, dh))
+    slots = [[0, 5, 11], [3], [4, 7, 8, 9]]
+    new = O.scatter_pages(cache, pool, perm, ps, slots)
+    back = O.gather_pages(new, perm, ps, ps * nblk)
+    for b in range(B):
+        np.testing.assert_array_equal(back[b][:, slots[b]], cache[b][:, slots[b]])
+        others = [p for p in range(ps * nblk) if p not in slots[b]]
+        np.testing.assert_array_equal(back[b][:, others], O.gather_pages(pool, perm, ps, ps * nblk)[b][:, others])
+    # pages no sequence maps are untouched
+    spare = sorted(set(range(B * nblk + 2)) - set(perm.ravel().tolist()))
+    np.testing.assert_array_equal(new[spare], pool[spare])
+
+
+def test_paged_layer_equals_contiguous_layer():
+    """A prefill over a prior cache, then a decode step, on a shuffled page
+    table equal the contiguous layer on the gathered cache (the paging only
+    moves where slots live)."""
+    H, Hkv, T, prior, ps = 4, 2, 5, 6, 4
+    x, w, _, _ = _tiny(71, B=2, T=T, H=H, Hkv=Hkv)
+    dh = 32 // H
+    nblk = 4                                               # capacity 16 >= prior + T + 1
+    rng = _rng(72)
+    bt = rng.permutation(2 * nblk + 3)[:2 * nblk].reshape(2, nblk)
+    kp = rng.standard_normal((2 * nblk + 3, Hkv, ps, dh))
+    vp = rng.standard_normal((2 * nblk + 3, Hkv, ps, dh))
+    pos = np.tile(np.arange(prior, prior + T), (2, 1))
+    kw = dict(n_heads=H, n_kv_heads=Hkv, bf16_points=True)
+    y, kp2, vp2 = O.decoder_layer_paged(x, pos, w, kp, vp, bt, ps, nblk * ps, **kw)
+    kc, vc = O.gather_pages(kp, bt, ps, nblk * ps), O.gather_pages(vp, bt, ps, nblk * ps)
+    yc, kc2, vc2 = O.decoder_layer(x, pos, w, kc, vc, **kw)
+    np.testing.assert_array_equal(y, yc)
+    np.testing.assert_array_equal(O.gather_pages(kp2, bt, ps, nblk * ps), kc2)
+    np.testing.assert_array_equal(O.gather_pages(vp2, bt, ps, nblk * ps), vc2)
+    xd = _rng(73).standard_normal((2, 32))
+    yd, _, _ = O.decoder_layer_paged(xd[:, None], np.full((2, 1), prior + T), w, kp2, vp2, bt, ps, nblk * ps, **kw)
+    ydc, _, _ = O.decoder_layer_decode(xd, np.full(2, prior + T), w, kc2, vc2, **kw)
+    np.testing.assert_array_equal(yd[:, 0], ydc)
