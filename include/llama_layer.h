@@ -149,6 +149,36 @@ int llama_layer_prefill(llama_layer* layer, const void* x, void* y, const int32_
 int llama_layer_decode(llama_layer* layer, const void* x, void* y, const int32_t* positions,
                        int32_t B, void* k_cache, void* v_cache, void* stream);
 
+/* ---- paged KV cache ----
+ * The same prefill and decode over a paged cache, the KV-memory scheme the
+ * "Llama MLP deep dive" page names (§6.4, PagedAttention) beside the "LLM
+ * mechanics lecture notes" Ch.04 cache accounting: the K and V of all
+ * sequences live in two caller-owned page pools, and a per-sequence block
+ * table says which page holds which slots.  The results are those of the
+ * contiguous calls on the cache the pages stand for (bit for bit, for the
+ * same max_pos: the kernels and their order of work are the same).
+ * k_pages, v_pages  [n_pages, Hkv, page_size, head_dim] (layer dtype,
+ *            16-byte aligned): row r of kv head g in page i at element
+ *            ((i*Hkv + g)*page_size + r)*head_dim.
+ * block_table [B, blocks_per_seq] int32 (device): slot p of sequence b lives
+ *            in page block_table[b*blocks_per_seq + p/page_size], row
+ *            p % page_size.  Pages may be shared between sequences only for
+ *            slots no call of this batch writes.
+ * page_size  a positive multiple of 64 slots.
+ * A sequence holds min(blocks_per_seq*page_size, max_pos) slots; positions
+ * are below that.  Page ids in use must lie in [0, n_pages) (precondition;
+ * an id outside writes nothing and reads in-bounds garbage, never faults;
+ * LLAMA_LAYER_CHECK=1 validates them).  bf16 layers only.
+ * Errors: as prefill/decode, plus NULL (block_table), INVALID (page_size not
+ * a positive multiple of 64, blocks_per_seq or n_pages < 1), UNSUPPORTED (fp32
+ * layer, a pool above 4 GiB), CAPACITY (T above the slots a sequence holds). */
+int llama_layer_prefill_paged(llama_layer* layer, const void* x, void* y, const int32_t* positions, int32_t B,
+                              int32_t T, void* k_pages, void* v_pages, const int32_t* block_table,
+                              int32_t blocks_per_seq, int32_t page_size, int32_t n_pages, void* stream);
+int llama_layer_decode_paged(llama_layer* layer, const void* x, void* y, const int32_t* positions, int32_t B,
+                             void* k_pages, void* v_pages, const int32_t* block_table, int32_t blocks_per_seq,
+                             int32_t page_size, int32_t n_pages, void* stream);
+
 /* Allocation-free decode, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  The same computation, kernels and results as

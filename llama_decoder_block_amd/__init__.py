@@ -33,6 +33,7 @@ LLAMA_F32 = 0
 LLAMA_BF16 = 1
 
 EXPORTED = ("llama_layer_create", "llama_layer_prefill", "llama_layer_decode", "llama_layer_decode_noalloc",
+            "llama_layer_prefill_paged", "llama_layer_decode_paged",
             "llama_layer_destroy", "llama_layer_strerror", "llama_layer_last_error",
             "llama_layer_profile", "llama_layer_profile_read", "llama_layer_step_name",
             "llama_layer_ceiling_mfma", "llama_layer_ceiling_read")
@@ -93,6 +94,10 @@ def _load():
     lib.llama_layer_prefill.restype = ctypes.c_int
     lib.llama_layer_decode.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp]
     lib.llama_layer_decode.restype = ctypes.c_int
+    lib.llama_layer_prefill_paged.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, i32, i32, i32, vp]
+    lib.llama_layer_prefill_paged.restype = ctypes.c_int
+    lib.llama_layer_decode_paged.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, i32, i32, i32, vp]
+    lib.llama_layer_decode_paged.restype = ctypes.c_int
     lib.llama_layer_decode_noalloc.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp]
     lib.llama_layer_decode_noalloc.restype = ctypes.c_int
     lib.llama_layer_destroy.argtypes = [vp]
@@ -194,6 +199,29 @@ def llama_layer_decode(handle, x, y, positions, B, k_cache, v_cache, stream=None
                                   _stream_ptr(stream)))
 
 
+def llama_layer_prefill_paged(handle, x, y, positions, B, T, k_pages, v_pages, block_table, page_size,
+                              stream=None):
+    """Prefill over page pools [n_pages, Hkv, page_size, dh]; block_table
+    [B, blocks_per_seq] int32 on the device."""
+    import torch
+    _check(LIB.llama_layer_prefill_paged(handle, _ptr(x, "x"), _ptr(y, "y"),
+                                         _ptr(positions, "positions", torch.int32), int(B), int(T),
+                                         _ptr(k_pages, "k_pages"), _ptr(v_pages, "v_pages"),
+                                         _ptr(block_table, "block_table", torch.int32),
+                                         int(block_table.shape[-1]), int(page_size), int(k_pages.shape[0]),
+                                         _stream_ptr(stream)))
+
+
+def llama_layer_decode_paged(handle, x, y, positions, B, k_pages, v_pages, block_table, page_size, stream=None):
+    import torch
+    _check(LIB.llama_layer_decode_paged(handle, _ptr(x, "x"), _ptr(y, "y"),
+                                        _ptr(positions, "positions", torch.int32), int(B),
+                                        _ptr(k_pages, "k_pages"), _ptr(v_pages, "v_pages"),
+                                        _ptr(block_table, "block_table", torch.int32),
+                                        int(block_table.shape[-1]), int(page_size), int(k_pages.shape[0]),
+                                        _stream_ptr(stream)))
+
+
 def llama_layer_decode_noalloc(handle, x, y, positions, B, k_cache, v_cache, stream=None):
     import torch
     _check(LIB.llama_layer_decode_noalloc(handle, _ptr(x, "x"), _ptr(y, "y"),
@@ -259,6 +287,23 @@ class LlamaLayer:
         import torch
         y = torch.empty_like(x) if y is None else y
         llama_layer_decode(self.handle, x, y, positions, int(x.shape[0]), k_cache, v_cache, stream)
+        return y
+
+    def prefill_paged(self, x, positions, k_pages, v_pages, block_table, y=None, stream=None):
+        """x [B, T, d]; pools [n_pages, Hkv, page, dh] (page size read from
+        their shape); block_table [B, blocks_per_seq] int32."""
+        import torch
+        B, T = int(x.shape[0]), int(x.shape[1])
+        y = torch.empty_like(x) if y is None else y
+        llama_layer_prefill_paged(self.handle, x, y, positions, B, T, k_pages, v_pages, block_table,
+                                  int(k_pages.shape[2]), stream)
+        return y
+
+    def decode_paged(self, x, positions, k_pages, v_pages, block_table, y=None, stream=None):
+        import torch
+        y = torch.empty_like(x) if y is None else y
+        llama_layer_decode_paged(self.handle, x, y, positions, int(x.shape[0]), k_pages, v_pages, block_table,
+                                 int(k_pages.shape[2]), stream)
         return y
 
     def decode_noalloc(self, x, positions, k_cache, v_cache, y, stream=None):

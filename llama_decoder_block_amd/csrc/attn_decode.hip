@@ -53,11 +53,11 @@ __device__ __forceinline__ void softmax_merge(float& m1, float& l1, float* a1, f
   m1 = m;
 }
 
-template <int R>
+template <int R, bool PAGED>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ pos, float* __restrict__ part,
-    bf16_t* __restrict__ o, int o_frag, int H, int Hkv, int max_pos, int L, int n_split,
+    bf16_t* __restrict__ o, int o_frag, int H, int Hkv, int max_pos, int span, KvPaging pg, int L, int n_split,
     float scale_log2) {
   __shared__ float red_ml[4][R][2];
   __shared__ float red_o[4][R][DH];
@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   const int dc = lane & 15;                // 8-dim chunk of a row
   const int sub = wave * 4 + (lane >> 4);  // row group: slots = sub (mod 16)
 
-  const int p = min(pos[b], max_pos - 1);
+  const int p = min(pos[b], span - 1);
   const int j_begin = s * L;
   const int j_end = min(j_begin + L, p + 1);
   const int n = j_end - j_begin;
@@ -95,9 +95,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int e = 0; e < 8; ++e) qv[r][e] *= scale_log2;
   }
 
-  const size_t slice = (static_cast<size_t>(b) * Hkv + g) * max_pos * DH;
+  const size_t slice = PAGED ? 0 : (static_cast<size_t>(b) * Hkv + g) * max_pos * DH;
   const bf16_t* K = k_cache + slice + static_cast<size_t>(j_begin) * DH + dc * 8;
   const bf16_t* V = v_cache + slice + static_cast<size_t>(j_begin) * DH + dc * 8;
+  // Paged: the 64 slots of one iteration, s0 .. s0 + 63 with s0 = j_begin +
+  // j - sub (j_begin and L are multiples of 64), lie in one page.  Slot s0 + i
+  // is row (page Hkv + g) page + s0 % page + i of the pool; as an offset from
+  // K's row for slot j_begin + j (the contiguous case's offset j), add this.
+  auto page_shift = [&](int j) -> long long {
+    const int s0 = j_begin + (j - sub);  // uniform
+    const int bi = min(s0 / pg.page, pg.blocks_per_seq - 1);  // (a slot past the split reads nothing)
+    int blk = __builtin_amdgcn_readfirstlane(pg.block_table[static_cast<size_t>(b) * pg.blocks_per_seq + bi]);
+    blk = min(max(blk, 0), pg.n_pages - 1);  // an invalid page id reads some page, never out of bounds
+    return (static_cast<long long>(blk) * Hkv + g) * pg.page + s0 % pg.page - s0;
+  };
 
   float m[R], l[R], acc[R][8];
 #pragma unroll
@@ -110,11 +121,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 
   // the 4 K and 4 V rows of this row group's next slots j, j + 16, ...
   auto fetch = [&](int j, uint4 (&ku)[4], uint4 (&vu)[4]) {
+    const long long base = PAGED ? page_shift(j) : 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bool ok = j + 16 * u < n;
-      ku[u] = ok ? *reinterpret_cast<const uint4*>(K + static_cast<size_t>(j + 16 * u) * DH) : make_uint4(0, 0, 0, 0);
-      vu[u] = ok ? *reinterpret_cast<const uint4*>(V + static_cast<size_t>(j + 16 * u) * DH) : make_uint4(0, 0, 0, 0);
+      const long long r = base + j + 16 * u;
+      ku[u] = ok ? *reinterpret_cast<const uint4*>(K + r * DH) : make_uint4(0, 0, 0, 0);
+      vu[u] = ok ? *reinterpret_cast<const uint4*>(V + r * DH) : make_uint4(0, 0, 0, 0);
     }
   };
   // the rows of the next iteration are fetched before this one's arithmetic
@@ -271,7 +284,7 @@ int split_len(int max_pos, int B, int Hkv, int chunks, int R) {
   const long long target = target_wgs(R);
   if (wgs >= target) return max_pos;
   long long L = (static_cast<long long>(max_pos) * wgs + target - 1) / target;
-  L = (L + 15) / 16 * 16;  // whole row-group steps
+  L = (L + 63) / 64 * 64;  // whole iterations (so a paged iteration stays in one page)
   if (L < 64) L = 64;
   if (L > max_pos) L = max_pos;
   return static_cast<int>(L);
@@ -285,28 +298,49 @@ int heads_per_block(int n_rep) {
 
 }  // namespace
 
-int decode_attn_splits(int max_pos, int B, int n_heads, int n_kv_heads) {
+int decode_attn_splits(int span, int B, int n_heads, int n_kv_heads) {
   const int n_rep = n_heads / n_kv_heads;
   const int R = heads_per_block(n_rep);
-  const int L = split_len(max_pos, B, n_kv_heads, n_rep / R, R);
-  return (max_pos + L - 1) / L;
+  const int L = split_len(span, B, n_kv_heads, n_rep / R, R);
+  return (span + L - 1) / L;
+}
+
+// A split is at least 64 slots and at least span * wgs / target_wgs slots,
+// so any span <= max_pos has at most min(ceil(max_pos / 64),
+// ceil(target_wgs / wgs)) splits.
+int decode_attn_max_splits(int max_pos, int B, int n_heads, int n_kv_heads) {
+  const int n_rep = n_heads / n_kv_heads;
+  const int R = heads_per_block(n_rep);
+  const long long wgs = static_cast<long long>(B) * n_kv_heads * (n_rep / R);
+  const long long target = target_wgs(R);
+  if (wgs >= target) return 1;
+  const long long a = (max_pos + 63) / 64, c = (target + wgs - 1) / wgs;
+  return static_cast<int>(a < c ? a : c);
 }
 
 hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                               const int32_t* pos, bf16_t* o, int o_frag, float* part, int n_split,
-                              int B, int n_heads, int n_kv_heads, int max_pos, hipStream_t s) {
+                              int B, int n_heads, int n_kv_heads, int max_pos, int span, const KvPaging& pg,
+                              hipStream_t s) {
   if (o_frag && B > kSkinnyMaxTokens) return hipErrorInvalidValue;
+  if (pg.block_table && (pg.page % 64 || pg.page <= 0 || span > pg.blocks_per_seq * pg.page))
+    return hipErrorInvalidValue;
   const int n_rep = n_heads / n_kv_heads;
   const int R = heads_per_block(n_rep);
-  const int L = split_len(max_pos, B, n_kv_heads, n_rep / R, R);
-  if ((max_pos + L - 1) / L != n_split) return hipErrorInvalidValue;
+  const int L = split_len(span, B, n_kv_heads, n_rep / R, R);
+  if ((span + L - 1) / L != n_split) return hipErrorInvalidValue;
   const dim3 grid(n_split, n_kv_heads * (n_rep / R), B);
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
+  const bool paged = pg.block_table != nullptr;
   switch (R) {
-#define LLAMA_DEC_CASE(RR)                                                                              \
-  case RR:                                                                                              \
-    hipLaunchKernelGGL(attn_decode_kernel<RR>, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, part,  \
-                       o, o_frag, n_heads, n_kv_heads, max_pos, L, n_split, scale_log2);                \
+#define LLAMA_DEC_CASE(RR)                                                                                      \
+  case RR:                                                                                                      \
+    if (paged)                                                                                                  \
+      hipLaunchKernelGGL((attn_decode_kernel<RR, true>), grid, dim3(256), 0, s, q, k_cache, v_cache, pos, part, \
+                         o, o_frag, n_heads, n_kv_heads, max_pos, span, pg, L, n_split, scale_log2);            \
+    else                                                                                                        \
+      hipLaunchKernelGGL((attn_decode_kernel<RR, false>), grid, dim3(256), 0, s, q, k_cache, v_cache, pos,      \
+                         part, o, o_frag, n_heads, n_kv_heads, max_pos, span, pg, L, n_split, scale_log2);      \
     break;
     LLAMA_DEC_CASE(1) LLAMA_DEC_CASE(2) LLAMA_DEC_CASE(3) LLAMA_DEC_CASE(4)
     LLAMA_DEC_CASE(5) LLAMA_DEC_CASE(6) LLAMA_DEC_CASE(7) LLAMA_DEC_CASE(8)

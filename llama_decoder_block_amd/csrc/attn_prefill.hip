@@ -85,11 +85,12 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 // (NGRP = 2 halves the longest serial chains when the grid holds at most two
 // workgroups per CU; with more, two independent 4-wavefront workgroups per CU
 // overlap better)
-template <int NGRP>
+template <int NGRP, bool PAGED>
 __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
     const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ pos, bf16_t* __restrict__ o,
-    int o_frag, int n_seq, int T, int H, int Hkv, int max_pos, int bidir, float scale_log2) {
+    int o_frag, int n_seq, int T, int H, int Hkv, int max_pos, int span, KvPaging pg, int bidir,
+    float scale_log2) {
   __shared__ __attribute__((aligned(16))) bf16_t Ks[NGRP][2][BKV * KSTR];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[NGRP][2][DH * VSTR];
 
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
     for (int w = 0; w < 4 * NGRP; ++w) sm = max(sm, s_seq[w]);
     if (valid) pq = sm;
   }
-  pq = min(pq, max_pos - 1);
+  pq = min(pq, span - 1);
 
   // wave / workgroup position range
   int wmax = pq, wmin = valid ? pq : 0x7fffffff;
@@ -154,7 +155,9 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
 
   // ---- K / V tile staging (buffer loads over this (b, g) cache slice), each
   // group for its own tiles: every thread loads 4 K and 4 V chunks of 16 bytes.
-  const size_t slice = (static_cast<size_t>(b) * Hkv + g) * max_pos * DH;
+  // (paged: one page per tile at most, since pages hold a multiple of 64
+  // slots; a tile whose page id is out of range reads zeros)
+  const size_t slice = PAGED ? 0 : (static_cast<size_t>(b) * Hkv + g) * max_pos * DH;
   const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k_cache + slice, static_cast<uint32_t>(max_pos) * DH * 2u);
   const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v_cache + slice, static_cast<uint32_t>(max_pos) * DH * 2u);
   // V: thread (vkg, vdg) loads slots 4 vkg .. 4 vkg + 3 at dims 8 vdg .. 8 vdg + 7
@@ -165,11 +168,23 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
   const int kr = tid >> 4, kc = tid & 15;
   uint4 kreg[4], vreg[4];
   auto gload = [&](int j0) {
-    const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j0) * DH * 2u);  // tile offset, uniform
+    __amdgpu_buffer_rsrc_t krs = k_rs, vrs = v_rs;
+    uint32_t so = static_cast<uint32_t>(j0) * DH * 2u;
+    if constexpr (PAGED) {  // the tile's page (uniform)
+      const int bi = j0 / pg.page;
+      const int blk = __builtin_amdgcn_readfirstlane(pg.block_table[static_cast<size_t>(b) * pg.blocks_per_seq + bi]);
+      const bool ok = blk >= 0 && blk < pg.n_pages;
+      const size_t base = ok ? (static_cast<size_t>(blk) * Hkv + g) * pg.page * DH : 0;
+      const uint32_t bytes = ok ? static_cast<uint32_t>(pg.page) * DH * 2u : 0u;
+      krs = make_rsrc(k_cache + base, bytes);
+      vrs = make_rsrc(v_cache + base, bytes);
+      so = static_cast<uint32_t>(j0 % pg.page) * DH * 2u;
+    }
+    so = __builtin_amdgcn_readfirstlane(so);  // tile offset, uniform
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(v_rs, ((4 * vkg + i) * DH + vdg * 8) * 2u, so);
+    for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(vrs, ((4 * vkg + i) * DH + vdg * 8) * 2u, so);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(k_rs, ((kr + 16 * i) * DH + kc * 8) * 2u, so);
+    for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(krs, ((kr + 16 * i) * DH + kc * 8) * 2u, so);
   };
   auto lstore = [&](int st) {
     // V goes to LDS as fp16 (the P.V product runs in fp16 so that P keeps
@@ -362,7 +377,10 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
 
 hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                                const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
-                               int n_kv_heads, int max_pos, int bidir, hipStream_t s) {
+                               int n_kv_heads, int max_pos, int span, const KvPaging& pg, int bidir,
+                               hipStream_t s) {
+  if (pg.block_table && (pg.page % BKV || pg.page <= 0 || span > pg.blocks_per_seq * pg.page))
+    return hipErrorInvalidValue;
   if (o_frag && B * T > kSkinnyMaxTokens) return hipErrorInvalidValue;
   const int n_wg = (T + BQ - 1) / BQ * n_heads * B;
   const dim3 grid(static_cast<unsigned>(n_wg));
@@ -370,12 +388,16 @@ hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf1
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidDevice;
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
-  if (n_wg <= 2 * n_cu)  // few workgroups: halve each query tile's chain
-    hipLaunchKernelGGL(attn_prefill_kernel<2>, grid, dim3(512), 0, s, q, k_cache, v_cache, pos, o, o_frag, B, T,
-                       n_heads, n_kv_heads, max_pos, bidir, scale_log2);
-  else
-    hipLaunchKernelGGL(attn_prefill_kernel<1>, grid, dim3(256), 0, s, q, k_cache, v_cache, pos, o, o_frag, B, T,
-                       n_heads, n_kv_heads, max_pos, bidir, scale_log2);
+#define LLAMA_ATTN_LAUNCH(NG, PG)                                                                          \
+  hipLaunchKernelGGL((attn_prefill_kernel<NG, PG>), grid, dim3(256 * NG), 0, s, q, k_cache, v_cache, pos, o, \
+                     o_frag, B, T, n_heads, n_kv_heads, max_pos, span, pg, bidir, scale_log2)
+  const bool two = n_wg <= 2 * n_cu;  // few workgroups: halve each query tile's chain
+  if (pg.block_table) {
+    if (two) LLAMA_ATTN_LAUNCH(2, true); else LLAMA_ATTN_LAUNCH(1, true);
+  } else {
+    if (two) LLAMA_ATTN_LAUNCH(2, false); else LLAMA_ATTN_LAUNCH(1, false);
+  }
+#undef LLAMA_ATTN_LAUNCH
   return hipGetLastError();
 }
 

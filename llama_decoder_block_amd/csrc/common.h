@@ -141,14 +141,37 @@ hipError_t launch_pack_rows(const bf16_t* src, int rows, int K, bf16_t* dst, int
 // 64-row blocks; the epilogues write q, the cache and h in the natural order.
 // QKV and gate/up multiply bf16 operands; o_proj and down fp16 ones (the
 // attention output and h are fp16, Wo and Wdown converted at creation).
+// Where the cache slots of a call live.  Contiguous (block_table null):
+// caches [B, Hkv, max_pos, 128], slot p of sequence b, kv head g at row
+// (b Hkv + g) max_pos + p.  Paged: pools [n_pages, Hkv, page, 128]; slot p of
+// sequence b sits in page block_table[b blocks_per_seq + p / page], kv head g
+// at row (page_id Hkv + g) page + p % page; page is a multiple of 64.  span:
+// the slots a sequence can hold (max_pos, or min(blocks_per_seq page, max_pos)).
+struct KvPaging {
+  const int32_t* block_table;  // [B, blocks_per_seq] page ids, or null
+  int blocks_per_seq, page, n_pages;
+};
+
+// Row (in 128-element rows) of slot p, kv head g, sequence b; -1 for a slot
+// without a valid page (paged only; contiguous slots are in range by the
+// caller's check of p).
+__device__ __forceinline__ long long kv_row(const KvPaging& pg, int b, int g, int Hkv, int max_pos, int p) {
+  if (!pg.block_table) return (static_cast<long long>(b) * Hkv + g) * max_pos + p;
+  const int blk = pg.block_table[static_cast<long long>(b) * pg.blocks_per_seq + p / pg.page];
+  if (blk < 0 || blk >= pg.n_pages) return -1;
+  return (static_cast<long long>(blk) * Hkv + g) * pg.page + p % pg.page;
+}
+
 struct QkvEpilogue {
   bf16_t* q;               // [M, H*dh]
-  bf16_t* k_cache;         // [B, Hkv, max_pos, dh]
+  bf16_t* k_cache;         // contiguous caches or page pools (see KvPaging)
   bf16_t* v_cache;
   const int32_t* pos;      // [M]
   const float* rope_cos;   // [max_pos, dh/2]
   const float* rope_sin;
   int T, n_heads, n_kv_heads, max_pos;
+  int span;                // positions >= span write no slot
+  KvPaging pg;
 };
 
 hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,
@@ -207,18 +230,25 @@ hipError_t launch_skinny_f32out(const bf16_t* A, const bf16_t* W, int M, int N, 
 // bidir = 1 slots 0..max over t of pos[b*T + t] (its sequence's largest).
 // o is fp16 (saturating at +-65504); o_frag = 1 writes it in fragment order
 // instead of row-major.
+// max_pos: the contiguous caches' slots per (sequence, kv head); span: the
+// slots a query may see (max_pos, or the paged capacity); pg: paging.
 hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                                const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
-                               int n_kv_heads, int max_pos, int bidir, hipStream_t s);
+                               int n_kv_heads, int max_pos, int span, const KvPaging& pg, int bidir,
+                               hipStream_t s);
 
 // Decode attention (bf16, dh = 128) for one query per sequence, split over
 // the cache when the grid would otherwise be small, followed by the merge of
 // the splits (n_split > 1 only).  part holds B*H*n_split*(128+2) floats;
 // o (fp16) and o_frag as for the prefill kernel.
-int decode_attn_splits(int max_pos, int B, int n_heads, int n_kv_heads);
+// The split structure depends on span (the slots a sequence can hold) only;
+// decode_attn_max_splits bounds the splits of every span <= max_pos.
+int decode_attn_splits(int span, int B, int n_heads, int n_kv_heads);
+int decode_attn_max_splits(int max_pos, int B, int n_heads, int n_kv_heads);
 hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
                               const int32_t* pos, bf16_t* o, int o_frag, float* part, int n_split,
-                              int B, int n_heads, int n_kv_heads, int max_pos, hipStream_t s);
+                              int B, int n_heads, int n_kv_heads, int max_pos, int span, const KvPaging& pg,
+                              hipStream_t s);
 
 // fp32 path (any shape).
 struct F32Layer {

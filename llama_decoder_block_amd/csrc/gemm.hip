@@ -264,10 +264,10 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
         if (kind == 0) {
           dst = q.q + static_cast<size_t>(row) * (q.n_heads * 128) + hh * 128;
         } else {
-          if (p < 0 || p >= q.max_pos) continue;
-          const int b = row / q.T;
-          bf16_t* cache = kind == 1 ? q.k_cache : q.v_cache;
-          dst = cache + (static_cast<size_t>(b * q.n_kv_heads + hh) * q.max_pos + p) * 128;
+          if (p < 0 || p >= q.span) continue;
+          const long long kr = kv_row(q.pg, row / q.T, hh, q.n_kv_heads, q.max_pos, p);
+          if (kr < 0) continue;  // no valid page for this slot
+          dst = (kind == 1 ? q.k_cache : q.v_cache) + kr * 128;
         }
         *reinterpret_cast<uint2*>(dst + x0) = make_uint2(pack_bf16x2(x1[0], x1[1]), pack_bf16x2(x1[2], x1[3]));
         *reinterpret_cast<uint2*>(dst + x0 + 64) = make_uint2(pack_bf16x2(x2[0], x2[1]), pack_bf16x2(x2[2], x2[3]));

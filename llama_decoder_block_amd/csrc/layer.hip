@@ -125,6 +125,15 @@ struct CallScratch {
   SkinnyScratch sk;
 };
 
+// The call's cache: contiguous [B, Hkv, max_pos, 128] K and V (pg null), or
+// page pools with a block table; span = the slots a sequence can hold.
+struct KvArgs {
+  void* k;
+  void* v;
+  KvPaging pg;
+  int span;
+};
+
 CallScratch handle_scratch(llama_layer* L) {
   return CallScratch{L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->part_seqs, L->sk};
 }
@@ -208,7 +217,8 @@ int part_floats(const llama_layer_config& c, int* seqs) {
   const int s = c.max_tokens < kDecodeChunk ? c.max_tokens : kDecodeChunk;
   long long best = 0;
   for (int b = 1; b <= s; ++b) {
-    const long long n = static_cast<long long>(b) * c.n_heads * decode_attn_splits(c.max_pos, b, c.n_heads, c.n_kv_heads) * 130;
+    // (the bound over every span <= max_pos: a paged call's span can be smaller)
+    const long long n = static_cast<long long>(b) * c.n_heads * decode_attn_max_splits(c.max_pos, b, c.n_heads, c.n_kv_heads) * 130;
     if (n > best) best = n;
   }
   *seqs = s;
@@ -412,14 +422,17 @@ void llama_layer_destroy(llama_layer* L) {
 }
 
 // Debug validation of the positions (LLAMA_LAYER_CHECK=1 when the handle is
-// created): bit 0 of *bad if a position lies outside [0, max_pos), bit 1 if
-// a position repeats within its sequence (token i against the earlier
-// tokens of its sequence: O(T^2) per sequence, a debug aid only).
-static __global__ void check_positions_kernel(const int32_t* __restrict__ pos, int B, int T, int max_pos, int* bad) {
+// created): bit 0 of *bad if a position lies outside [0, span), bit 1 if a
+// position repeats within its sequence (token i against the earlier tokens
+// of its sequence: O(T^2) per sequence, a debug aid only), bit 2 (paged) if
+// a page the token writes or reads (slots 0 .. its position) has an id
+// outside [0, n_pages).
+static __global__ void check_positions_kernel(const int32_t* __restrict__ pos, int B, int T, int span, KvPaging pg,
+                                              int* bad) {
   const long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i >= static_cast<long long>(B) * T) return;
   const int p = pos[i];
-  if (p < 0 || p >= max_pos) {
+  if (p < 0 || p >= span) {
     atomicOr(bad, 1);
     return;
   }
@@ -428,29 +441,40 @@ static __global__ void check_positions_kernel(const int32_t* __restrict__ pos, i
       atomicOr(bad, 2);
       return;
     }
+  if (pg.block_table) {
+    const int32_t* row = pg.block_table + (i / T) * pg.blocks_per_seq;
+    for (int bi = 0; bi <= p / pg.page; ++bi)
+      if (row[bi] < 0 || row[bi] >= pg.n_pages) {
+        atomicOr(bad, 4);
+        return;
+      }
+  }
 }
 
-static int check_positions(llama_layer* L, const int32_t* pos, int B, int T, hipStream_t s) {
+static int check_positions(llama_layer* L, const int32_t* pos, int B, int T, const KvArgs& kv, hipStream_t s) {
   const long long n = static_cast<long long>(B) * T;
   int bad = 0;
   HIP_OR_RETURN(hipMemsetAsync(L->check_flag, 0, sizeof(int), s), "clear check flag");
   hipLaunchKernelGGL(check_positions_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, pos, B, T,
-                     L->cfg.max_pos, L->check_flag);
+                     kv.span, kv.pg, L->check_flag);
   HIP_OR_RETURN(hipGetLastError(), "position check launch");
   HIP_OR_RETURN(hipMemcpyAsync(&bad, L->check_flag, sizeof(int), hipMemcpyDeviceToHost, s), "read check flag");
   HIP_OR_RETURN(hipStreamSynchronize(s), "position check");
-  if (bad & 1) return fail(LLAMA_ERR_INVALID, "a position lies outside [0, max_pos = %d)", L->cfg.max_pos);
+  if (bad & 1) return fail(LLAMA_ERR_INVALID, "a position lies outside [0, %d)", kv.span);
   if (bad & 2) return fail(LLAMA_ERR_INVALID, "a position repeats within a sequence");
+  if (bad & 4) return fail(LLAMA_ERR_INVALID, "a block table entry in use lies outside [0, n_pages = %d)", kv.pg.n_pages);
   return LLAMA_OK;
 }
 
 static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* y, const int32_t* pos, int B,
-                     int T, void* kc, void* vc, hipStream_t s) {
+                     int T, const KvArgs& kv, hipStream_t s) {
+  void* kc = kv.k;
+  void* vc = kv.v;
   const llama_layer_config& c = L->cfg;
   const int M = B * T;
   const int d = c.d_model, H = c.n_heads, Hkv = c.n_kv_heads, f = c.d_ff;
   if (L->check_flag) {
-    const int st = check_positions(L, pos, B, T, s);
+    const int st = check_positions(L, pos, B, T, kv, s);
     if (st != LLAMA_OK) return st;
   }
 
@@ -494,6 +518,8 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
   ep.n_heads = H;
   ep.n_kv_heads = Hkv;
   ep.max_pos = c.max_pos;
+  ep.span = kv.span;
+  ep.pg = kv.pg;
 
   hipEvent_t* ev = nullptr;
   if (L->prof_on) {
@@ -513,20 +539,25 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
                 "qkv projection");
   HIP_OR_RETURN(mark(2), "event record");
   if (T == 1) {
-    const size_t kv_seq = static_cast<size_t>(Hkv) * c.max_pos * 128;
+    // sequences in chunks of part_seqs (one chunk for <= 64 tokens, whose o is
+    // in fragment order): contiguous caches or block-table rows move with b0
+    const bool paged = kv.pg.block_table != nullptr;
+    const size_t kv_seq = paged ? 0 : static_cast<size_t>(Hkv) * c.max_pos * 128;
     for (int b0 = 0; b0 < B; b0 += S.part_seqs) {
       const int nb = B - b0 < S.part_seqs ? B - b0 : S.part_seqs;
-      const int ns = decode_attn_splits(c.max_pos, nb, H, Hkv);
+      const int ns = decode_attn_splits(kv.span, nb, H, Hkv);
+      KvPaging pgc = kv.pg;
+      if (paged) pgc.block_table += static_cast<size_t>(b0) * pgc.blocks_per_seq;
       HIP_OR_RETURN(launch_attn_decode(q + static_cast<size_t>(b0) * H * 128,
                                        static_cast<const bf16_t*>(kc) + b0 * kv_seq,
                                        static_cast<const bf16_t*>(vc) + b0 * kv_seq, pos + b0,
                                        o + static_cast<size_t>(b0) * H * 128, skinny, S.part, ns, nb, H, Hkv,
-                                       c.max_pos, s),
+                                       c.max_pos, kv.span, pgc, s),
                     "decode attention");
     }
   } else {
     HIP_OR_RETURN(launch_attn_prefill(q, static_cast<const bf16_t*>(kc), static_cast<const bf16_t*>(vc), pos,
-                                      o, skinny, B, T, H, Hkv, c.max_pos, c.bidirectional, s),
+                                      o, skinny, B, T, H, Hkv, c.max_pos, kv.span, kv.pg, c.bidirectional, s),
                   "prefill attention");
   }
   HIP_OR_RETURN(mark(3), "event record");
@@ -548,24 +579,45 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
   return LLAMA_OK;
 }
 
+// Argument checks shared by every call; kv.pg.block_table non-null for the
+// paged calls (their page arguments are checked by the caller).
 static int checked_call(llama_layer* L, const void* x, void* y, const int32_t* pos, int B, int T,
-                        void* kc, void* vc, void* stream) {
-  g_last_error.clear();
-  if (!L || !x || !y || !pos || !kc || !vc)
+                        const KvArgs& kv, void* stream) {
+  if (!L || !x || !y || !pos || !kv.k || !kv.v)
     return fail(LLAMA_ERR_NULL, "layer, x, y, positions and caches must be non-null");
   if (B < 1 || T < 1) return fail(LLAMA_ERR_INVALID, "B and T must be >= 1 (got %d, %d)", B, T);
   if (static_cast<long long>(B) * T > L->cfg.max_tokens)
     return fail(LLAMA_ERR_CAPACITY, "B*T = %lld exceeds max_tokens = %d", static_cast<long long>(B) * T,
                 L->cfg.max_tokens);
-  if (T > L->cfg.max_pos) return fail(LLAMA_ERR_CAPACITY, "T = %d exceeds max_pos = %d", T, L->cfg.max_pos);
-  if (!aligned16(x) || !aligned16(y) || !aligned16(kc) || !aligned16(vc))
+  if (T > kv.span) return fail(LLAMA_ERR_CAPACITY, "T = %d exceeds the %d slots a sequence holds", T, kv.span);
+  if (!aligned16(x) || !aligned16(y) || !aligned16(kv.k) || !aligned16(kv.v))
     return fail(LLAMA_ERR_INVALID, "x, y and the caches must be 16-byte aligned");
   int cur = 0;
   HIP_OR_RETURN(hipGetDevice(&cur), "hipGetDevice");
   if (cur != L->device) HIP_OR_RETURN(hipSetDevice(L->device), "hipSetDevice");
-  const int st = run_layer(L, handle_scratch(L), x, y, pos, B, T, kc, vc, static_cast<hipStream_t>(stream));
+  const int st = run_layer(L, handle_scratch(L), x, y, pos, B, T, kv, static_cast<hipStream_t>(stream));
   if (cur != L->device) (void)hipSetDevice(cur);
   return st;
+}
+
+static KvArgs contiguous_kv(const llama_layer* L, void* kc, void* vc) {
+  return KvArgs{kc, vc, KvPaging{nullptr, 0, 0, 0}, L ? L->cfg.max_pos : 0};
+}
+
+static int paged_kv(const llama_layer* L, void* kp, void* vp, const int32_t* block_table, int blocks_per_seq,
+                    int page_size, int n_pages, KvArgs* out) {
+  if (!L || !block_table) return fail(LLAMA_ERR_NULL, "layer and block_table must be non-null");
+  if (L->cfg.dtype != LLAMA_BF16) return fail(LLAMA_ERR_UNSUPPORTED, "the paged cache serves bf16 layers");
+  if (page_size <= 0 || page_size % 64)
+    return fail(LLAMA_ERR_INVALID, "page_size must be a positive multiple of 64 (got %d)", page_size);
+  if (blocks_per_seq < 1 || n_pages < 1)
+    return fail(LLAMA_ERR_INVALID, "blocks_per_seq and n_pages must be >= 1 (got %d, %d)", blocks_per_seq, n_pages);
+  const long long cap = static_cast<long long>(blocks_per_seq) * page_size;
+  if (static_cast<long long>(n_pages) * L->cfg.n_kv_heads * page_size * 256 > 4294967295LL)
+    return fail(LLAMA_ERR_UNSUPPORTED, "a page pool exceeds 4 GiB (32-bit buffer offsets)");
+  *out = KvArgs{kp, vp, KvPaging{block_table, blocks_per_seq, page_size, n_pages},
+                static_cast<int>(cap < L->cfg.max_pos ? cap : L->cfg.max_pos)};
+  return LLAMA_OK;
 }
 
 int llama_layer_profile(llama_layer* L, int enable) {
@@ -603,12 +655,32 @@ const char* llama_layer_step_name(int step) {
 
 int llama_layer_prefill(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
                         int32_t T, void* k_cache, void* v_cache, void* stream) {
-  return checked_call(L, x, y, positions, B, T, k_cache, v_cache, stream);
+  g_last_error.clear();
+  return checked_call(L, x, y, positions, B, T, contiguous_kv(L, k_cache, v_cache), stream);
 }
 
 int llama_layer_decode(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
                        void* k_cache, void* v_cache, void* stream) {
-  return checked_call(L, x, y, positions, B, 1, k_cache, v_cache, stream);
+  g_last_error.clear();
+  return checked_call(L, x, y, positions, B, 1, contiguous_kv(L, k_cache, v_cache), stream);
+}
+
+int llama_layer_prefill_paged(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B, int32_t T,
+                              void* k_pages, void* v_pages, const int32_t* block_table, int32_t blocks_per_seq,
+                              int32_t page_size, int32_t n_pages, void* stream) {
+  g_last_error.clear();
+  KvArgs kv{};
+  const int st = paged_kv(L, k_pages, v_pages, block_table, blocks_per_seq, page_size, n_pages, &kv);
+  return st != LLAMA_OK ? st : checked_call(L, x, y, positions, B, T, kv, stream);
+}
+
+int llama_layer_decode_paged(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
+                             void* k_pages, void* v_pages, const int32_t* block_table, int32_t blocks_per_seq,
+                             int32_t page_size, int32_t n_pages, void* stream) {
+  g_last_error.clear();
+  KvArgs kv{};
+  const int st = paged_kv(L, k_pages, v_pages, block_table, blocks_per_seq, page_size, n_pages, &kv);
+  return st != LLAMA_OK ? st : checked_call(L, x, y, positions, B, 1, kv, stream);
 }
 
 int llama_layer_decode_noalloc(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
@@ -669,7 +741,8 @@ int llama_layer_decode_noalloc(llama_layer* L, const void* x, void* y, const int
     const int n = static_cast<int>(groups);
     hipLaunchKernelGGL(zero_words_kernel, dim3((n + 255) / 256), dim3(256), 0, s, S.sk.cnt, n);
     const hipError_t e = hipGetLastError();
-    st = e != hipSuccess ? hip_fail(e, "clear counters") : run_layer(L, S, x, y, positions, B, 1, k_cache, v_cache, s);
+    st = e != hipSuccess ? hip_fail(e, "clear counters")
+                         : run_layer(L, S, x, y, positions, B, 1, contiguous_kv(L, k_cache, v_cache), s);
   }
   if (cur != L->device) (void)hipSetDevice(cur);
   return st;

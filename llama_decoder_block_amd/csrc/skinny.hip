@@ -116,10 +116,10 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
         if (kind == 0) {
           dst = q.q + static_cast<size_t>(tok) * (q.n_heads * 128) + hh * 128;
         } else {
-          if (p < 0 || p >= q.max_pos) continue;
-          const int b = tok / q.T;
-          bf16_t* cache = kind == 1 ? q.k_cache : q.v_cache;
-          dst = cache + (static_cast<size_t>(b * q.n_kv_heads + hh) * q.max_pos + p) * 128;
+          if (p < 0 || p >= q.span) continue;
+          const long long kr = kv_row(q.pg, tok / q.T, hh, q.n_kv_heads, q.max_pos, p);
+          if (kr < 0) continue;  // no valid page for this slot
+          dst = (kind == 1 ? q.k_cache : q.v_cache) + kr * 128;
         }
         *reinterpret_cast<uint32_t*>(dst + x0) = pack_bf16x2(lo[0], lo[1]);
         *reinterpret_cast<uint32_t*>(dst + x0 + 64) = pack_bf16x2(hi[0], hi[1]);

@@ -130,6 +130,9 @@ def test_calls_reject_null_handle():
     p = ctypes.c_void_p(4096)
     assert lib.LIB.llama_layer_prefill(None, p, p, p, 1, 1, p, p, None) == lib.LLAMA_ERR_NULL
     assert lib.LIB.llama_layer_decode(None, p, p, p, 1, p, p, None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_decode_noalloc(None, p, p, p, 1, p, p, None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_prefill_paged(None, p, p, p, 1, 1, p, p, p, 1, 64, 1, None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_decode_paged(None, p, p, p, 1, p, p, p, 1, 64, 1, None) == lib.LLAMA_ERR_NULL
     lib.LIB.llama_layer_destroy(None)  # no-op
 
 
