@@ -12,12 +12,19 @@ Also reported on the same line:
                 layer's flops): algorithmic flops / its average duration,
                 timed live with HIP events on the library's stream during the
                 timed steps, against the 2.5 PFLOP/s dense bf16 MFMA peak;
+                layer_mfma_frac is the whole layer call's fraction;
   decode        LLaMA-7B-shape decode step (32 sequences at position 4095):
-                algorithmic bytes / step time against 8 TB/s HBM;
+                algorithmic bytes / step time against 8 TB/s HBM, with the
+                oracle's rate on a sample of it (decode.cpu_baseline);
+  decode_paged  the same step over a paged KV cache (pages of 64 slots in
+                shuffled order);
+  other_configs the 7B shape with bidirectional attention, the 13B-shape
+                prefill, the 70B-shape GQA prefill and its 64 decode steps,
+                and greedy generation with a 32-layer 7B-shape stack;
   cpu_baseline  the CPU oracle on a bounded prefix of the same prefill
                 workload, on this host's cores.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--headline-only]
 """
 from __future__ import annotations
 
@@ -184,6 +191,54 @@ def bench_decode(lib, synth, steps, warmup):
             "cache_flush_between_steps": "512 MB read",
             "step_ms_by_kernel": breakdown,
             "step_ms_by_kernel_note": "separate untimed pass with HIP events around every step"}
+
+
+def bench_decode_paged(lib, synth, steps, warmup, page=64):
+    """The 7B decode workload over a paged cache: the same K/V scattered into
+    pages of `page` slots in shuffled order (a block table per sequence),
+    timed like the contiguous decode (median of event-timed steps, caches
+    evicted by a 512 MB read before each)."""
+    import torch
+    wl = synth.WORKLOADS["llama7b_decode"]
+    B, p = wl.batch, wl.prior
+    w = synth.make_weights(wl, "cuda")
+    x = synth.make_x(wl, (B,), device="cuda")
+    pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+    kc, vc = synth.make_cache(wl, "cuda")
+    nb = wl.max_pos // page
+    perm = torch.randperm(B * nb, generator=torch.Generator().manual_seed(11))
+    bt = perm.view(B, nb).to(torch.int32).cuda()
+    kp = torch.empty(B * nb, wl.n_kv_heads, page, wl.head_dim, dtype=kc.dtype, device="cuda")
+    vp = torch.empty_like(kp)
+    idx = bt.view(-1).long()
+    kp[idx] = kc.view(B, wl.n_kv_heads, nb, page, wl.head_dim).transpose(1, 2).reshape(B * nb, wl.n_kv_heads, page,
+                                                                                         wl.head_dim)
+    vp[idx] = vc.view(B, wl.n_kv_heads, nb, page, wl.head_dim).transpose(1, 2).reshape(B * nb, wl.n_kv_heads, page,
+                                                                                         wl.head_dim)
+    del kc, vc
+    y = torch.empty_like(x)
+    layer = lib.LlamaLayer(layer_config(lib, wl, B), w)
+    flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ramp_clocks(lambda: layer.decode_paged(x, pos, kp, vp, bt, y=y))
+    for _ in range(warmup):
+        layer.decode_paged(x, pos, kp, vp, bt, y=y)
+    times = []
+    for _ in range(steps):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        layer.decode_paged(x, pos, kp, vp, bt, y=y)
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in times)
+    med = ms[len(ms) // 2]
+    nbytes = decode_bytes(wl, B, p)
+    layer.close()
+    return {"workload": "llama7b_decode, paged KV cache", "page_slots": page, "pages": B * nb, "batch": B,
+            "position": p, "ms_per_step_median": med, "bytes_per_step": nbytes, "GBps": nbytes / med / 1e6,
+            "hbm_frac": nbytes / med / 1e6 / PEAK_HBM_GBPS, "tokens_per_s": B / med * 1e3}
 
 
 def measure_ceilings(lib, runs=5):
@@ -386,6 +441,50 @@ def cpu_baseline(wl, host, budget_s):
             "host_cpu": cpu, "host_logical_cpus": os.cpu_count(), "one_thread": one}
 
 
+def cpu_baseline_decode(budget_s):
+    """The oracle as it stands on a bounded sample of the 7B decode workload:
+    the first k of its 32 sequences (k doubled from 1 until one run takes a
+    third of the budget), each at position 4095 over its 4095 prior slots.
+    Reported as effective GB/s over the algorithmic bytes of that sample
+    (weights and gains once, the k sequences' prior K/V, appended K/V, x and y)."""
+    import numpy as np
+    import torch
+    import synth
+    from oracle import llama_oracle as O
+    wl = synth.WORKLOADS["llama7b_decode"]
+    p = wl.prior
+    w = synth.make_weights(wl, "cuda")
+    w64 = {k: v.detach().cpu().double().numpy() for k, v in w.items()}
+    del w
+    x = synth.make_x(wl, (wl.batch,), device="cuda").cpu().double().numpy()
+    kc, vc = synth.make_cache(wl, "cuda")
+    k, last = 1, None
+    while True:
+        k64 = kc[:k].cpu().double().numpy()
+        v64 = vc[:k].cpu().double().numpy()
+        t0 = time.perf_counter()
+        O.decoder_layer_decode(x[:k], np.full(k, p), w64, k64, v64, n_heads=wl.n_heads, n_kv_heads=wl.n_kv_heads)
+        dt = time.perf_counter() - t0
+        last = (k, dt)
+        log(f"cpu oracle decode: {k} sequences in {dt:.2f} s")
+        if dt >= budget_s / 3 or k >= wl.batch:
+            break
+        k = min(wl.batch, 2 * k)
+    k, dt = last
+    nbytes = decode_bytes(wl, k, p)
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": _blas_threads(), "kind": "oracle",
+            "sample": f"first {k} of the 32 sequences of the llama7b_decode step (position 4095), plain fp64 "
+                      f"numpy oracle, {dt:.2f} s; bytes = weights + those sequences' K/V + x, y"}
+
+
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max((i.get("num_threads", 1) for i in threadpool_info()), default=1))
+    except Exception:
+        return os.cpu_count()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -395,8 +494,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
-    ap.add_argument("--other-configs", action="store_true",
-                    help="also time the 13B-shape prefill and the 70B-shape GQA prefill + 64 decode steps")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other configs (13B prefill, 70B GQA prefill + 64 decode steps, the "
+                         "bidirectional variant, the generation stack, the paged decode)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -448,7 +548,10 @@ def main():
                      "achieved": gu_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gu_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic_from_profile(kernel_src),
-                     "flops_per_launch": gu_flops, "avg_launch_ms": gu_ms},
+                     "flops_per_launch": gu_flops, "avg_launch_ms": gu_ms,
+                     "layer_mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                     "note": "achieved/frac: the dominant kernel (gate/up + SwiGLU, 43% of the layer's flops); "
+                             "layer_mfma_frac: the whole layer call's algorithmic flops / its wall time"},
         "layer": {"flops_per_step": flops, "tflops": flops / (ms_per_step * 1e-3) / 1e12,
                   "mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                   "step_ms_by_kernel": step_avg,
@@ -456,6 +559,8 @@ def main():
     }
     if not args.no_decode:
         out["decode"] = bench_decode(lib, synth, args.decode_steps, 3)
+        if not args.headline_only:
+            out["decode_paged"] = bench_decode_paged(lib, synth, args.decode_steps, 3)
     # fractions of what this GPU sustains (the roofline above uses the published peaks)
     ceil = measure_ceilings(lib)
     ceil["prefill_layer_frac_of_mfma_loop"] = out["layer"]["tflops"] / ceil["mfma_loop_tflops"]
@@ -463,11 +568,13 @@ def main():
     if "decode" in out:
         ceil["decode_frac_of_stream_read"] = out["decode"]["GBps"] / ceil["stream_read_GBps"]
     out["ceilings"] = ceil
-    if args.other_configs:
+    if not args.headline_only:
         out["other_configs"] = bench_other_configs(lib, synth, max(3, args.steps // 4), 2)
         out["other_configs"]["llama7b_generate"] = bench_generate(lib, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_budget_s)
+        if "decode" in out:
+            out["decode"]["cpu_baseline"] = cpu_baseline_decode(args.cpu_budget_s / 2)
     print(json.dumps(out), flush=True)
 
 

@@ -10,9 +10,12 @@
 // row's 1/rms lands a repeated input value within ~2^-24 of a bf16 rounding
 // midpoint, fp32 arithmetic rounds every copy of it the wrong way at once,
 // and the whole row's projections move.  So for a bf16 output the sum of
-// squares (exact products), 1/sqrt and the scaling run in fp64, and the fp64
-// result is rounded to bf16 correctly (to odd into fp32, then to nearest even:
-// no double rounding).  An fp32 output (the fp32 layer) stays in fp32.
+// squares (exact products) and 1/sqrt run in fp64, and each element is
+// rounded to bf16 as its exact value would be: from fp32 where the fp32
+// value is provably on the right side of the rounding midpoint, else
+// recomputed in fp64 and rounded correctly (to odd into fp32, then to
+// nearest even: no double rounding).  An fp32 output (the fp32 layer) stays
+// in fp32.
 //
 // One 64-wide wavefront per row.  Each lane keeps its share of the row in
 // registers (NV vectors of 8 elements, 16-byte bf16 or 32-byte fp32 loads,
@@ -69,16 +72,27 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ float operator[](int e) const { return v[e]; }
 };
 
-// g * (x * inv) for 8 elements, rounded once to the output type
+// g * (x * inv) for 8 elements, as fp32 values whose bf16 rounding (to
+// nearest even) is the rounding of the exact product.  fp32 output: plain
+// fp32.  bf16 output (A = double): computed in fp32 from inv rounded to fp32,
+// three roundings of 2^-24 each, so the fp32 value is within 3 fp32 ulps of
+// the exact one; unless it lies within 8 ulps of a bf16 rounding midpoint
+// (low 16 bits 0x8000), both round to the same bf16 value.  The rare ones
+// near a midpoint are redone in fp64 and rounded to odd (see f64_to_f32_odd).
 template <typename A, typename X, typename G>
 __device__ __forceinline__ void scale8(const X& x, const G& gv, A inv, float out[8]) {
+  if constexpr (sizeof(A) == 8) {
+    const float inv32 = static_cast<float>(inv);
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const A v = static_cast<A>(gv[e]) * (static_cast<A>(x[e]) * inv);
-    if constexpr (sizeof(A) == 8)
-      out[e] = f64_to_f32_odd(v);
-    else
-      out[e] = v;
+    for (int e = 0; e < 8; ++e) {
+      const float v = gv[e] * (x[e] * inv32);
+      const int off = static_cast<int>(__float_as_uint(v) & 0xffffu) - 0x8000;
+      out[e] = (off < -8 || off > 8) ? v
+                                     : f64_to_f32_odd(static_cast<double>(gv[e]) * (static_cast<double>(x[e]) * inv));
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = gv[e] * (x[e] * inv);
   }
 }
 
@@ -214,7 +228,7 @@ __global__ __launch_bounds__(256) void rmsnorm_any_kernel(const TIn* __restrict_
   for (int i = lane; i < d; i += kWave) {
     const A v = static_cast<A>(load1(g + i)) * (static_cast<A>(load1(x + i)) * inv);
     if constexpr (sizeof(A) == 8)
-      store1(y + i, f64_to_f32_odd(v));
+      store1(y + i, f64_to_f32_odd(v));  // (any-width fallback: fp64 throughout)
     else
       store1(y + i, v);
   }
