@@ -32,7 +32,7 @@
 // K advances in 64-wide slabs.
 //   * W is stored in fragment order, so a wave fetches each 32 x 16 weight
 //     fragment it needs with one contiguous 1 KB buffer load straight into
-//     registers (a two-deep ring per k step); W never touches LDS.
+//     registers (a ring two or four slabs deep); W never touches LDS.
 //   * A (activations, row-major) is staged through registers into two LDS
 //     stages of BM rows x 128 bytes; the 16-byte column chunk c of row r is
 //     stored at c ^ ((r >> 1) & 7) so the fragment reads of 32 consecutive
@@ -89,7 +89,7 @@ __device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
 // the residual GEMMs (o_proj, down) multiply fp16 operands, QKV and gate/up bf16
 template <int EPI> constexpr bool kF16Operands = EPI == EPI_RESID32 || EPI == EPI_RESID16;
 
-template <int BM, int BN, int EPI>
+template <int BM, int BN, int EPI, int RING>
 __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Wp,
                                                     int M, int N, int K, EpiArgs ep) {
   constexpr bool F16 = kF16Operands<EPI>;
@@ -123,14 +123,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   for (int i = 0; i < NA; ++i)
     a_goff[i] = (static_cast<uint32_t>(m0 + 32 * i + (tid >> 3)) * K + (tid & 7) * 8) * 2u;
   const int a_woff = (tid >> 3) * 128 + (((tid & 7) ^ ((tid >> 4) & 7)) << 4);
-  uint4 sa[NA];
-  auto a_gload = [&](int i, int kt) { sa[i] = buf_load16(a_rs, a_goff[i], static_cast<uint32_t>(kt) * (BK * 2u)); };
-  auto a_lstore = [&](int i, int st) { *reinterpret_cast<uint4*>(stage_base(st) + a_woff + i * 32 * 128) = sa[i]; };
+  // AD register sets: with RING == 4 two, so an A load is issued 2.25 slabs
+  // before its LDS store (slab s is held in set s & 1), else one (1.25 slabs)
+  constexpr int AD = RING == 4 ? 2 : 1;
+  uint4 sa[AD][NA];
+  auto a_gload = [&](int set, int i, int kt) {
+    sa[set][i] = buf_load16(a_rs, a_goff[i], static_cast<uint32_t>(kt) * (BK * 2u));
+  };
+  auto a_lstore = [&](int set, int i, int st) {
+    *reinterpret_cast<uint4*>(stage_base(st) + a_woff + i * 32 * 128) = sa[set][i];
+  };
   // B fragments: this wave's FN n-blocks, straight from the fragment-ordered weights
   uint32_t b_off[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) b_off[j] = static_cast<uint32_t>((n0 >> 5) + wn * FN + j) * KB * 1024u + lane * 16u;
-  uint4 bq[2][4][FN];
+  uint4 bq[RING][4][FN];
   auto b_load = [&](int set, int kt, int kk, int j) {
     bq[set][kk][j] = buf_load16(b_rs, b_off[j], static_cast<uint32_t>(kt * 4 + kk) * 1024u);
   };
@@ -153,33 +160,41 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   bf16x8 fa[2][FM];
 
-  const int nk = K / BK;  // even
-  // prologue: A slab 0 -> stage 0, A slab 1 -> registers; B k-steps 0, 1 -> ring
+  const int nk = K / BK;  // a multiple of RING
+  // prologue: A slab 0 -> stage 0, A slabs 1 .. AD -> registers; B slabs
+  // 0 .. RING-1 -> ring
 #pragma unroll
-  for (int i = 0; i < NA; ++i) a_gload(i, 0);
+  for (int i = 0; i < NA; ++i) a_gload(0, i, 0);
 #pragma unroll
-  for (int i = 0; i < NA; ++i) a_lstore(i, 0);
+  for (int i = 0; i < NA; ++i) a_lstore(0, i, 0);
 #pragma unroll
-  for (int i = 0; i < NA; ++i) a_gload(i, 1);
+  for (int i = 0; i < NA; ++i) a_gload(AD == 2 ? 1 : 0, i, 1);
+  if constexpr (AD == 2) {
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk)
+    for (int i = 0; i < NA; ++i) a_gload(0, i, 2);
+  }
 #pragma unroll
-    for (int j = 0; j < FN; ++j) { b_load(0, 0, kk, j); b_load(1, 1, kk, j); }
+  for (int b = 0; b < RING; ++b)
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) b_load(b, b, kk, j);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < FM; ++i) fa[0][i] = frag_a(0, 0, i);
 
-  // Slab kt (LDS stage and B ring set kt & 1).  k steps 0-1: A slab kt+1
-  // goes from registers into the other stage (free: its last reads finished
-  // before the previous barrier), each register refilled with slab kt+2
-  // right after; k steps 0-3: B k-step kt+2 replaces the ring slots it frees.
+  // Slab kt (LDS stage kt & 1, B ring set kt % RING).  k steps 0-1: A slab
+  // kt+1 goes from registers into the other stage (free: its last reads
+  // finished before the previous barrier), each register refilled with slab
+  // kt+1+AD right after; k steps 0-3: B slab kt+RING replaces the ring slots
+  // it frees, so a weight load has RING - 1 slabs of MFMA work to arrive.
   // The A fragments of the next k step are read one MFMA slot ahead.  One
   // barrier per slab, before k step 3: it publishes the other stage (the
   // LDS writes are complete: lgkmcnt) and retires this stage's reads; then
   // the first fragments of slab kt+1 are read.  Every wait on a global load
   // is the compiler's own (register dependencies), so none depends on load
   // timing.
-  auto slab = [&](const int st, int kt) {
+  auto slab = [&](const int st, const int bs, int kt) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int cur = kk & 1;
@@ -187,25 +202,30 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
 #pragma unroll
       for (int m = 0; m < FM * FN; ++m) {
         const int i = m / FN, j = m % FN;
-        acc[i][j] = mfma_32x32x16<F16>(fa[cur][i], __builtin_bit_cast(bf16x8, bq[st][kk][j]), acc[i][j]);
+        acc[i][j] = mfma_32x32x16<F16>(fa[cur][i], __builtin_bit_cast(bf16x8, bq[bs][kk][j]), acc[i][j]);
         if (m < FM) fa[cur ^ 1][m] = kk < 3 ? frag_a(st, kk + 1, m) : frag_a(st ^ 1, 0, m);
-        if (m >= FM * FN - FN) b_load(st, kt + 2, kk, m - (FM * FN - FN));
+        if (m >= FM * FN - FN) b_load(bs, kt + RING, kk, m - (FM * FN - FN));
         // A chunk i (k step i / 4): stored to LDS, then its register is
-        // refilled with the same chunk of slab kt+2 two slots later, so every
-        // A load has a whole slab to arrive
+        // refilled with the same chunk of slab kt+1+AD two slots later, so
+        // every A load has AD slabs to arrive
         if (kk < 2) {
           constexpr int s2 = FM * FN / (NA / 2);  // slots per chunk
           const int i = kk * (NA / 2) + m / s2;
-          if (m % s2 == s2 / 2 - 1) a_lstore(i, st ^ 1);
-          if (m % s2 == s2 - 1) a_gload(i, kt + 2);
+          const int as = AD == 2 ? (st ^ 1) : 0;  // the set holding slab kt+1
+          if (m % s2 == s2 / 2 - 1) a_lstore(as, i, st ^ 1);
+          if (m % s2 == s2 - 1) a_gload(as, i, kt + 1 + AD);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  for (int kt = 0; kt < nk; kt += 2) {
-    slab(0, kt);
-    slab(1, kt + 1);
+  for (int kt = 0; kt < nk; kt += RING) {
+    slab(0, 0, kt);
+    slab(1, 1, kt + 1);
+    if constexpr (RING == 4) {
+      slab(0, 2, kt + 2);
+      slab(1, 3, kt + 3);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
 
@@ -314,10 +334,21 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   }
 }
 
+// Weight ring depth: a wave tile with 8 MFMAs per k step (128 x 256 tiles)
+// gets a 4-slab ring, so a weight load that misses L2 still has ~3 slabs of
+// MFMA work (~0.4 us per slab) to arrive; wider tiles do 12-16 MFMAs per k step and
+// keep 2 slabs (their registers go to the accumulators).  A 4-slab ring
+// needs K % 256 == 0, else the 2-slab ring runs.
 template <int BM, int BN, int EPI>
 hipError_t launch_tiled(const bf16_t* A, const bf16_t* Wp, int M, int N, int K, const EpiArgs& ep, hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI>), dim3(tiles), dim3(256), 0, s, A, Wp, M, N, K, ep);
+  if constexpr (BM == 128 && BN == 256) {
+    if (K % 256 == 0) {
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, 4>), dim3(tiles), dim3(256), 0, s, A, Wp, M, N, K, ep);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, 2>), dim3(tiles), dim3(256), 0, s, A, Wp, M, N, K, ep);
   return hipGetLastError();
 }
 
