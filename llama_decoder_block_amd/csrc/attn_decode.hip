@@ -126,8 +126,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int u = 0; u < 4; ++u) {
       const bool ok = j + 16 * u < n;
       const long long r = base + j + 16 * u;
-      ku[u] = ok ? *reinterpret_cast<const uint4*>(K + r * DH) : make_uint4(0, 0, 0, 0);
-      vu[u] = ok ? *reinterpret_cast<const uint4*>(V + r * DH) : make_uint4(0, 0, 0, 0);
+      ku[u] = ok ? load16_nt(K + r * DH) : make_uint4(0, 0, 0, 0);
+      vu[u] = ok ? load16_nt(V + r * DH) : make_uint4(0, 0, 0, 0);
     }
   };
   // the rows of the next iteration are fetched before this one's arithmetic

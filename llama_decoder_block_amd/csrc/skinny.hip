@@ -187,7 +187,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
         const uint32_t off = ((static_cast<uint32_t>(nb0 + 2 * j) * KB + kb) << 10) + lane * 16u;
-        wv[slot][j] = buf_load16(w_rs, ok ? off : w_bytes, 0);
+        wv[slot][j] = buf_load16_nt(w_rs, ok ? off : w_bytes, 0);
       }
 #pragma unroll
       for (int t = 0; t < TB; ++t) {
