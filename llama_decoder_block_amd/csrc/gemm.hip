@@ -247,8 +247,41 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
     return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
                       pack_bf16x2(v[6], v[7]));
   };
+  // QKV: a lane's tasks keep their row offset and columns in every pass, so
+  // the positions of all its task rows are fetched once, before the first
+  // pass, and the RoPE cos/sin of pass i + 1 are fetched while pass i runs
+  // (in place of two dependent global loads per task and pass)
+  constexpr int NTQ = EPI == EPI_QKV ? TN / 16 : 1;  // tasks per lane and pass
+  int qpos[FM][NTQ];
+  f32x4 qcos[2][NTQ], qsin[2][NTQ];
+  auto qkv_cs = [&](int i, int buf) {
+    const QkvEpilogue& q = ep.qkv;
+#pragma unroll
+    for (int k = 0; k < NTQ; ++k) {
+      const int task = lane + 64 * k, c = 8 * (task % (TN / 8));
+      const int x0 = ((col0 + c) & 127) >> 1;
+      const int pt = min(max(qpos[i][k], 0), q.max_pos - 1);
+      const float4 c4 = *reinterpret_cast<const float4*>(q.rope_cos + static_cast<size_t>(pt) * 64 + x0);
+      const float4 s4 = *reinterpret_cast<const float4*>(q.rope_sin + static_cast<size_t>(pt) * 64 + x0);
+      qcos[buf][k] = f32x4{c4.x, c4.y, c4.z, c4.w};
+      qsin[buf][k] = f32x4{s4.x, s4.y, s4.z, s4.w};
+    }
+  };
+  if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int k = 0; k < NTQ; ++k) {
+        const int row = m0 + wm * TM + i * 32 + (lane + 64 * k) / (TN / 8);
+        qpos[i][k] = row < M ? ep.qkv.pos[row] : 0;
+      }
+    qkv_cs(0, 0);
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    if constexpr (EPI == EPI_QKV) {
+      if (i + 1 < FM) qkv_cs(i + 1, (i + 1) & 1);
+    }
     // registers -> LDS: acc[i][j][r] is row 8 (r/4) + hr + r%4, column 32 j + lc
 #pragma unroll
     for (int j = 0; j < FN; ++j)
@@ -270,12 +303,9 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
         const int head = col >> 7, x0 = (col & 127) >> 1;
         const int kind = head < q.n_heads ? 0 : (head < q.n_heads + q.n_kv_heads ? 1 : 2);
         const int hh = kind == 0 ? head : (kind == 1 ? head - q.n_heads : head - q.n_heads - q.n_kv_heads);
-        const int p = q.pos[row];
+        const int p = qpos[i][k];
         if (kind != 2) {
-          const int pt = min(max(p, 0), q.max_pos - 1);
-          const float4 c4 = *reinterpret_cast<const float4*>(q.rope_cos + static_cast<size_t>(pt) * 64 + x0);
-          const float4 s4 = *reinterpret_cast<const float4*>(q.rope_sin + static_cast<size_t>(pt) * 64 + x0);
-          const f32x4 cs = {c4.x, c4.y, c4.z, c4.w}, sn = {s4.x, s4.y, s4.z, s4.w};
+          const f32x4 cs = qcos[i & 1][k], sn = qsin[i & 1][k];
           const f32x4 y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
           x1 = y1;
           x2 = y2;
