@@ -277,10 +277,33 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
       }
     qkv_cs(0, 0);
   }
+  // residual epilogues: the residual rows of pass i + 1 are fetched while
+  // pass i runs (8 bf16 or 8 fp32 per task: one or two 16-byte loads)
+  constexpr bool RESID = EPI == EPI_RESID32 || EPI == EPI_RESID16;
+  constexpr int NTR = RESID ? TN / 16 : 1, RW = EPI == EPI_RESID16 ? 2 : 1;
+  uint4 rres[2][NTR][RW];
+  auto resid_fetch = [&](int i, int buf) {
+#pragma unroll
+    for (int k = 0; k < NTR; ++k) {
+      const int task = lane + 64 * k, R = task / (TN / 8), c = 8 * (task % (TN / 8));
+      const int row = m0 + wm * TM + i * 32 + R, col = col0 + c;
+      const bool ok = row < M && col < N;
+      const size_t at = ok ? static_cast<size_t>(row) * N + col : 0;
+#pragma unroll
+      for (int w = 0; w < RW; ++w)
+        rres[buf][k][w] = EPI == EPI_RESID16
+                              ? *reinterpret_cast<const uint4*>(static_cast<const float*>(ep.resid) + at + 4 * w)
+                              : *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(ep.resid) + at);
+    }
+  };
+  if constexpr (RESID) resid_fetch(0, 0);
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     if constexpr (EPI == EPI_QKV) {
       if (i + 1 < FM) qkv_cs(i + 1, (i + 1) & 1);
+    }
+    if constexpr (RESID) {
+      if (i + 1 < FM) resid_fetch(i + 1, (i + 1) & 1);
     }
     // registers -> LDS: acc[i][j][r] is row 8 (r/4) + hr + r%4, column 32 j + lc
 #pragma unroll
@@ -349,14 +372,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
         const f32x8 a = ld8(R, c);
         const size_t at = static_cast<size_t>(row) * N + col;
         if constexpr (EPI == EPI_RESID32) {
-          const uint4 rb = *reinterpret_cast<const uint4*>(static_cast<const bf16_t*>(ep.resid) + at);
+          const uint4 rb = rres[i & 1][k][0];
           float* o = static_cast<float*>(ep.out) + at;
           *reinterpret_cast<float4*>(o) = make_float4(a[0] + lo_bf16(rb.x), a[1] + hi_bf16(rb.x), a[2] + lo_bf16(rb.y), a[3] + hi_bf16(rb.y));
           *reinterpret_cast<float4*>(o + 4) = make_float4(a[4] + lo_bf16(rb.z), a[5] + hi_bf16(rb.z), a[6] + lo_bf16(rb.w), a[7] + hi_bf16(rb.w));
         } else {
-          const float* rp = static_cast<const float*>(ep.resid) + at;
-          const float4 r0 = *reinterpret_cast<const float4*>(rp), r1 = *reinterpret_cast<const float4*>(rp + 4);
-          const f32x8 rs = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+          const uint4 r0 = rres[i & 1][k][0], r1 = rres[i & 1][k][RW - 1];
+          const f32x8 rs = {__uint_as_float(r0.x), __uint_as_float(r0.y), __uint_as_float(r0.z), __uint_as_float(r0.w),
+                            __uint_as_float(r1.x), __uint_as_float(r1.y), __uint_as_float(r1.z), __uint_as_float(r1.w)};
           *reinterpret_cast<uint4*>(static_cast<bf16_t*>(ep.out) + at) = bf8(a + rs);
         }
       }
