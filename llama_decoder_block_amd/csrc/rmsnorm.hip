@@ -17,11 +17,13 @@
 // nearest even: no double rounding).  An fp32 output (the fp32 layer) stays
 // in fp32.
 //
-// One 64-wide wavefront per row.  Each lane keeps its share of the row in
-// registers (NV vectors of 8 elements, 16-byte bf16 or 32-byte fp32 loads,
-// consecutive lanes on consecutive vectors so a wave reads 1 KB contiguous per
-// load), so HBM sees exactly one read of x and one write of out.  The sum of
-// squares is reduced with wavefront shuffles; no LDS, no barriers.
+// A workgroup of 4 (d a multiple of 2048) or 2 (d = 3072, 5120, 6144 or
+// 7168) wavefronts per row, else one 64-wide wavefront per row.  Each lane
+// keeps its share of the row in registers (NV vectors of 8 elements, 16-byte
+// bf16 or 32-byte fp32 loads, consecutive lanes on consecutive vectors so a
+// wave reads 1 KB contiguous per load), so HBM sees exactly one read of x and
+// one write of out.  The sum of squares is reduced with wavefront shuffles
+// and, across the waves of a row, through LDS in a fixed order.
 #include "common.h"
 
 namespace llama {
@@ -166,23 +168,26 @@ __global__ __launch_bounds__(256) void rmsnorm_vec_kernel(const TIn* __restrict_
   }
 }
 
-// Few rows (decode): one 256-thread workgroup per row, so a call of B rows
-// spreads over B CUs and each lane issues d / 2048 loads of the row (and of
-// the gain) instead of d / 512; the sum of squares goes through the four
-// waves' partial sums in LDS, added in a fixed order.  d % 2048 == 0; for 32
-// rows of 4096 the decode norm step went from ~10 to ~6.6 us (event timed).
-template <typename TIn, typename TG, typename TOut, int NV, bool FRAG>
-__global__ __launch_bounds__(256) void rmsnorm_row_kernel(const TIn* __restrict__ in, const TG* __restrict__ g,
-                                                          TOut* __restrict__ out, int d, float eps) {
+// One workgroup of W wavefronts per row: each lane issues d / (512 W) loads
+// of the row (and of the gain) instead of d / 512, so a CU has several
+// times the loads in flight of the one-wave-per-row kernel; the sum of
+// squares goes through the waves' partial sums in LDS, added in a fixed
+// order.  d = NV * 512 * W.  Measured against one wave per row: 32 decode
+// rows of 4096 ~10 -> ~6.6 us (event timed); the 7B prefill norms (2048
+// rows) 16.2 / 16.4 -> 12.0 / 13.3 us, the 70B ones (4096 rows of 8192)
+// 50.2 / 52.8 -> 29.7 / 37.1 us.
+template <typename TIn, typename TG, typename TOut, int NV, bool FRAG, int W>
+__global__ __launch_bounds__(64 * W) void rmsnorm_row_kernel(const TIn* __restrict__ in, const TG* __restrict__ g,
+                                                             TOut* __restrict__ out, int d, float eps) {
   typedef typename NormAcc<TOut>::type A;
-  __shared__ A part[4];
+  __shared__ A part[W];
   const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const TIn* x = in + static_cast<size_t>(row) * d;
   Raw8<TIn> v[NV];
   Raw8<TG> gv[NV];
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int vi = tid + j * 256;
+    const int vi = tid + j * 64 * W;
     v[j].load(x + vi * 8);
     gv[j].load(g + vi * 8);
   }
@@ -194,12 +199,14 @@ __global__ __launch_bounds__(256) void rmsnorm_row_kernel(const TIn* __restrict_
   ss = wave_sum(ss);
   if (lane == 0) part[wave] = ss;
   __syncthreads();
-  ss = (part[0] + part[1]) + (part[2] + part[3]);
+  ss = part[0];
+#pragma unroll
+  for (int w = 1; w < W; ++w) ss += part[w];
   const A inv = inv_rms<A>(ss, d, eps);
   TOut* y = out + (FRAG ? 0 : static_cast<size_t>(row) * d);
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int vi = tid + j * 256;
+    const int vi = tid + j * 64 * W;
     float r[8];
     scale8(v[j], gv[j], inv, r);
     store8(y + (FRAG ? frag_index(row, vi * 8, d) : vi * 8), r);
@@ -242,24 +249,24 @@ hipError_t dispatch(const void* in, const void* g, void* out, int rows, int d, f
   const TG* gg = static_cast<const TG*>(g);
   TOut* y = static_cast<TOut*>(out);
   const int nv = (d + 511) / 512;
-  if (rows <= 64 && d % 2048 == 0) {  // few rows: one workgroup per row
+#define LLAMA_NORM_ROW(NV, W)                                                                              \
+  case NV:                                                                                                   \
+    hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, NV, FRAG, W>), dim3(rows), dim3(64 * W), 0, s, x, gg, \
+                       y, d, eps);                                                                           \
+    return hipGetLastError();
+  if (d % 2048 == 0) {  // a workgroup of 4 wavefronts per row
     switch (d / 2048) {
-      case 1:
-        hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, 1, FRAG>), dim3(rows), block, 0, s, x, gg, y, d, eps);
-        return hipGetLastError();
-      case 2:
-        hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, 2, FRAG>), dim3(rows), block, 0, s, x, gg, y, d, eps);
-        return hipGetLastError();
-      case 4:
-        hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, 4, FRAG>), dim3(rows), block, 0, s, x, gg, y, d, eps);
-        return hipGetLastError();
-      case 8:
-        hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, 8, FRAG>), dim3(rows), block, 0, s, x, gg, y, d, eps);
-        return hipGetLastError();
-      default:
-        break;  // other widths take the one-wave-per-row kernel
+      LLAMA_NORM_ROW(1, 4) LLAMA_NORM_ROW(2, 4) LLAMA_NORM_ROW(4, 4) LLAMA_NORM_ROW(8, 4)
+      default: break;
     }
   }
+  if (d % 1024 == 0) {  // 2 wavefronts per row
+    switch (d / 1024) {
+      LLAMA_NORM_ROW(3, 2) LLAMA_NORM_ROW(5, 2) LLAMA_NORM_ROW(6, 2) LLAMA_NORM_ROW(7, 2)
+      default: break;  // other widths take the one-wave-per-row kernel
+    }
+  }
+#undef LLAMA_NORM_ROW
   if (d % 8 == 0 && nv <= 16) {
     if (nv <= 8)
       hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 8, FRAG>), grid, block, 0, s, x, gg, y, rows, d, eps);
