@@ -80,8 +80,52 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
   const __amdgpu_buffer_rsrc_t w_rs = make_rsrc(Wp, w_bytes);
   const __amdgpu_buffer_rsrc_t x_rs = make_rsrc(Xp, x_bytes);
 
+  // The epilogue's inputs that do not depend on the sums (the position and
+  // RoPE cos/sin, or the residual), for token block t of group g: fetched
+  // when the workgroup starts on the group, so the epilogue at the end of the
+  // kernel does not wait on them.  rr[j][r4]: the cos and sin pairs (QKV),
+  // 4 bf16 (o_proj) or 4 fp32 (down) of the residual.
+  static_assert(TB <= NW, "a wavefront finishes at most one token block of a group");
+  struct EpiIn {
+    int p;
+    uint4 rr[NB][4];
+  };
+  auto epi_fetch = [&](int g, int t) {
+    EpiIn in{};
+    const int nb0 = NB == 2 ? (g >> 1) * 4 + (g & 1) : g;
+    const int tok = t * 32 + (lane & 31);
+    const int tk = tok < M ? tok : 0;
+    if constexpr (EPI == SK_QKV) {
+      const QkvEpilogue& q = ep.qkv;
+      in.p = q.pos[tk];
+      const int pt = min(max(in.p, 0), q.max_pos - 1);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int x0 = ((nb0 & 3) * 32 + 8 * r4 + 4 * (lane >> 5)) >> 1;
+        const float2 c = *reinterpret_cast<const float2*>(q.rope_cos + static_cast<size_t>(pt) * 64 + x0);
+        const float2 sn = *reinterpret_cast<const float2*>(q.rope_sin + static_cast<size_t>(pt) * 64 + x0);
+        in.rr[0][r4] = make_uint4(__float_as_uint(c.x), __float_as_uint(c.y), __float_as_uint(sn.x),
+                                  __float_as_uint(sn.y));
+      }
+    } else if constexpr (EPI == SK_RESID32 || EPI == SK_RESID16) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          const size_t at = static_cast<size_t>(tk) * N + (nb0 + 2 * j) * 32 + 8 * r4 + 4 * (lane >> 5);
+          if constexpr (EPI == SK_RESID32) {
+            const uint2 rb = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(ep.resid) + at);
+            in.rr[j][r4] = make_uint4(rb.x, rb.y, 0u, 0u);
+          } else {
+            in.rr[j][r4] = *reinterpret_cast<const uint4*>(static_cast<const float*>(ep.resid) + at);
+          }
+        }
+    }
+    return in;
+  };
+
   // the epilogue of token block t of group g, from the finished sums v[j][r]
-  auto finish = [&](int g, int t, const float (&v)[NB][16]) {
+  auto finish = [&](int g, int t, const float (&v)[NB][16], const EpiIn& in) {
     const int nb0 = NB == 2 ? (g >> 1) * 4 + (g & 1) : g;
     const int tok = t * 32 + (lane & 31);
     if (tok >= M) return;
@@ -98,13 +142,12 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
         const int x0 = ((nb0 & 3) * 32 + fib) >> 1;
         const int kind = head < q.n_heads ? 0 : (head < q.n_heads + q.n_kv_heads ? 1 : 2);
         const int hh = kind == 0 ? head : (kind == 1 ? head - q.n_heads : head - q.n_heads - q.n_kv_heads);
-        const int p = q.pos[tok];
-        const int pt = min(max(p, 0), q.max_pos - 1);
+        const int p = in.p;
         float lo[2] = {v[0][4 * r4], v[0][4 * r4 + 2]}, hi[2] = {v[0][4 * r4 + 1], v[0][4 * r4 + 3]};
         if (kind != 2) {
-          const float2 c = *reinterpret_cast<const float2*>(q.rope_cos + static_cast<size_t>(pt) * 64 + x0);
-          const float2 s = *reinterpret_cast<const float2*>(q.rope_sin + static_cast<size_t>(pt) * 64 + x0);
-          const float cc[2] = {c.x, c.y}, ss[2] = {s.x, s.y};
+          const uint4 w = in.rr[0][r4];
+          const float cc[2] = {__uint_as_float(w.x), __uint_as_float(w.y)};
+          const float ss[2] = {__uint_as_float(w.z), __uint_as_float(w.w)};
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
             const float x1 = lo[e], x2 = hi[e];
@@ -145,12 +188,13 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
           const int col = (nb0 + 2 * j) * 32 + fib;
           const size_t at = static_cast<size_t>(tok) * N + col;
           if constexpr (EPI == SK_RESID32) {
-            const uint2 rb = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(ep.resid) + at);
+            const uint2 rb = make_uint2(in.rr[j][r4].x, in.rr[j][r4].y);
             *reinterpret_cast<float4*>(static_cast<float*>(ep.out) + at) =
                 make_float4(v[j][4 * r4] + lo_bf16(rb.x), v[j][4 * r4 + 1] + hi_bf16(rb.x),
                             v[j][4 * r4 + 2] + lo_bf16(rb.y), v[j][4 * r4 + 3] + hi_bf16(rb.y));
           } else {
-            const float4 rf = *reinterpret_cast<const float4*>(static_cast<const float*>(ep.resid) + at);
+            const float4 rf = make_float4(__uint_as_float(in.rr[j][r4].x), __uint_as_float(in.rr[j][r4].y),
+                                          __uint_as_float(in.rr[j][r4].z), __uint_as_float(in.rr[j][r4].w));
             *reinterpret_cast<uint2*>(static_cast<bf16_t*>(ep.out) + at) =
                 make_uint2(pack_bf16x2(v[j][4 * r4] + rf.x, v[j][4 * r4 + 1] + rf.y),
                            pack_bf16x2(v[j][4 * r4 + 2] + rf.z, v[j][4 * r4 + 3] + rf.w));
@@ -170,6 +214,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
     const int k1 = static_cast<int>(min(static_cast<long long>(KB), u1 - static_cast<long long>(g) * KB));
     u = static_cast<long long>(g) * KB + k1;
     const int nb0 = NB == 2 ? (g >> 1) * 4 + (g & 1) : g;
+    // this wave's token block of the group: its epilogue inputs, in flight during the stream
+    const EpiIn pre = wave < TB ? epi_fetch(g, wave) : EpiIn{};
 
     f32x16 acc[NB][TB];
 #pragma unroll
@@ -241,7 +287,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
       for (int t = wave; t < TB; t += NW) {
         float v[NB][16];
         wave_sum(t, v);
-        finish(g, t, v);
+        finish(g, t, v, pre);
       }
       continue;
     }
@@ -282,7 +328,7 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
             v[j][r] += __hip_atomic_load(src + ((j * TB + t) * 16 + r) * 64 + lane, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
       }
-      finish(g, t, v);
+      finish(g, t, v, pre);
     }
     if (tid == 0) __hip_atomic_store(ep.cnt + g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
