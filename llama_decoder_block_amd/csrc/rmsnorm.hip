@@ -17,8 +17,10 @@
 // nearest even: no double rounding).  An fp32 output (the fp32 layer) stays
 // in fp32.
 //
-// A workgroup of 4 (d a multiple of 2048) or 2 (d = 3072, 5120, 6144 or
-// 7168) wavefronts per row, else one 64-wide wavefront per row.  Each lane
+// A workgroup of d / 512 wavefronts per row for calls of <= 64 rows (d =
+// 2048, 4096, 5120 or 8192), else of 4 (d a multiple of 2048) or 2 (d =
+// 3072, 5120, 6144 or 7168) wavefronts per row, else one 64-wide wavefront
+// per row.  Each lane
 // keeps its share of the row in registers (NV vectors of 8 elements, 16-byte
 // bf16 or 32-byte fp32 loads, consecutive lanes on consecutive vectors so a
 // wave reads 1 KB contiguous per load), so HBM sees exactly one read of x and
@@ -249,11 +251,25 @@ hipError_t dispatch(const void* in, const void* g, void* out, int rows, int d, f
   const TG* gg = static_cast<const TG*>(g);
   TOut* y = static_cast<TOut*>(out);
   const int nv = (d + 511) / 512;
+#define LLAMA_NORM_ROW_W(W)                                                                                \
+  case W:                                                                                                    \
+    hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, 1, FRAG, W>), dim3(rows), dim3(64 * W), 0, s, x, gg, \
+                       y, d, eps);                                                                           \
+    return hipGetLastError();
 #define LLAMA_NORM_ROW(NV, W)                                                                              \
   case NV:                                                                                                   \
     hipLaunchKernelGGL((rmsnorm_row_kernel<TIn, TG, TOut, NV, FRAG, W>), dim3(rows), dim3(64 * W), 0, s, x, gg, \
                        y, d, eps);                                                                           \
     return hipGetLastError();
+  // decode-sized calls (few rows, each a workgroup): one 16-byte vector per
+  // lane, d / 512 wavefronts per row, so a row's loads all go out at once
+  // (a single 70B row, 8192 wide: 9.7 / 9.4 -> 8.3 / 8.7 us per norm)
+  if (rows <= 64 && d % 512 == 0) {
+    switch (d / 512) {
+      LLAMA_NORM_ROW_W(4) LLAMA_NORM_ROW_W(8) LLAMA_NORM_ROW_W(10) LLAMA_NORM_ROW_W(16)
+      default: break;
+    }
+  }
   if (d % 2048 == 0) {  // a workgroup of 4 wavefronts per row
     switch (d / 2048) {
       LLAMA_NORM_ROW(1, 4) LLAMA_NORM_ROW(2, 4) LLAMA_NORM_ROW(4, 4) LLAMA_NORM_ROW(8, 4)
@@ -267,6 +283,7 @@ hipError_t dispatch(const void* in, const void* g, void* out, int rows, int d, f
     }
   }
 #undef LLAMA_NORM_ROW
+#undef LLAMA_NORM_ROW_W
   if (d % 8 == 0 && nv <= 16) {
     if (nv <= 8)
       hipLaunchKernelGGL((rmsnorm_vec_kernel<TIn, TG, TOut, 8, FRAG>), grid, block, 0, s, x, gg, y, rows, d, eps);
