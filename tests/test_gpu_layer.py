@@ -291,6 +291,33 @@ def test_decode_with_wide_rows(dtype):
             G.assert_f32(G.f64(ys), yo, f"decode step {s} y")
 
 
+@pytest.mark.parametrize("d", [3072, 5120])
+def test_rmsnorm_row_widths(d):
+    """Widths that take the RMSNorm kernels with 2 wavefronts per row
+    (prefill rows: d/1024 = 3 or 5 vectors per lane) and, for decode rows,
+    2 (d = 3072) or d/512 = 10 (d = 5120) wavefronts per row: a prefill of 70
+    tokens (tiled GEMMs) and two single-sequence decode steps against the
+    oracle."""
+    from oracle import llama_oracle as O
+    wl = _wl(d=d, H=d // 128, Hkv=8, f=1024, B=1, T=70, steps=2, seed=31 + d // 1024)
+    print(f"case d={d}", flush=True)
+    w, x, kc, vc, pos, layer = _setup(wl, random_gains=True)
+    kc0, vc0 = kc.clone(), vc.clone()
+    y = layer.prefill(x, pos, kc, vc)
+    _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc)
+    w64 = G.oracle_weights(w)
+    _, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)  # the oracle continues from its own cache
+    for s in range(wl.decode_steps):
+        p = wl.seq + s
+        xs = synth.make_x(wl, (wl.batch,), tensor_id=synth.TID_DECODE_BASE + s, device=DEV)
+        ys = layer.decode(xs, torch.full((wl.batch,), p, dtype=torch.int32, device=DEV), kc, vc)
+        torch.cuda.synchronize()
+        yo, ko, vo = O.decoder_layer_decode(G.f64(xs), np.full(wl.batch, p), w64, ko, vo, n_heads=wl.n_heads,
+                                            n_kv_heads=wl.n_kv_heads, bf16_points=True)
+        G.assert_bf16_output(G.f64(ys), yo, f"d={d} decode step {s} y")
+    layer.close()
+
+
 def test_decode_matches_prefill_of_one_more_token():
     """Prefill T, decode token T == row T of a prefill of T+1 (within bf16)."""
     wl = _wl(d=512, H=4, Hkv=2, f=1408, B=2, T=81, seed=13)
