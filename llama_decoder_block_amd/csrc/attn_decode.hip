@@ -8,7 +8,8 @@
 // softmax, weighted sum of values; repeat_kv grouped-query attention, here
 // kv-head indexing so a K/V row read serves all query heads of its group).
 //
-// gfx950 design: the cache is streamed once at HBM rate, K and V together.
+// gfx950 design: the cache is streamed once at HBM rate, K and V together,
+// with nontemporal loads (each row is read once per call).
 //   * workgroup (split s, kv head g, sequence b) takes slots
 //     [s L, (s+1) L) ∩ [0, p]; the split length is chosen so the grid holds
 //     about 1024 workgroups (4 per CU; at 3 or 4 query heads per workgroup

@@ -27,8 +27,8 @@
 // them to complete, and counts itself in on the group's counter; the last
 // one reads all partials back, adds them in range order (so the result does
 // not depend on arrival order) and runs the epilogue, then re-arms the
-// counter.  Each weight byte is read exactly once; the activations (<= 64 x
-// K bf16) are re-read by every workgroup from L2.
+// counter.  Each weight byte is read exactly once (nontemporal loads); the
+// activations (<= 64 x K bf16) are re-read by every workgroup from L2.
 //
 // Pairing: the QKV weight's heads are in rotary-pair order (dims x and x + 64
 // on rows 2x and 2x + 1), so a rotation's two inputs are neighbouring
