@@ -36,12 +36,17 @@
 // about 22 significant bits; one fp16 alone keeps 11, and its rounding
 // error, carried through the bf16 rounding of the attention output and
 // amplified by the MLP, put the 70B-shape layer output beyond the bf16
-// tolerance), with V converted to fp16 (exact) as it is staged.  The weights are taken against the running max (the output is
-// rescaled only when some query's max moves).  The
-// row-max exchange between the two lanes of a query is a permlane32 swap.
-// Query tiles are launched heaviest first across all heads and sequences (the
-// causal workload grows with the tile index).  Tiles that lie wholly above a wave's diagonal are skipped, and
-// the -inf mask is applied only on tiles that cross it.
+// tolerance), with V converted to fp16 (exact) as it is staged.  The weights
+// are taken against a reference max that lags the running max by at most 8
+// (log2 units), so the output is rescaled only when some query's max moves
+// past it, which after the first tile is rare; the weights then stay below
+// 2^15, inside fp16's range.  The row-max exchange between the two lanes of a
+// query is a permlane32 swap.  The Q fragments and each group's first K/V
+// tile are loaded before the positions are read, so the kernel's start does
+// not wait on three memory round trips in a row.  Query tiles are launched
+// heaviest first across all heads and sequences (the causal workload grows
+// with the tile index).  Tiles that lie wholly above a wave's diagonal are
+// skipped, and the -inf mask is applied only on tiles that cross it.
 #include "common.h"
 
 #include <math.h>
@@ -81,6 +86,21 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// p0, p1 -> fp16 pairs hi = p rounded toward zero, lo = fp16(p - hi) (the
+// difference is exact in fp32; one rounding to fp16, to nearest even)
+__device__ __forceinline__ void split_f16(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(p0, p1));
+  uint32_t l;
+  asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "=v"(l) : "v"(p0), "v"(hi));
+  asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]" : "+v"(l) : "v"(p1), "v"(hi));
+  lo = l;
+}
+
+// lazy rescaling: the reference max a wave's weights are taken against moves
+// only when some query's tile max exceeds it by more than kLazy (log2 units);
+// weights are 2^(s - ref + 15 - kLazy) <= 2^15, within fp16's range
+constexpr float kLazy = 8.f;
+
 // NGRP wave groups of 4 share the query tile and take every NGRP-th K/V tile
 // (NGRP = 2 halves the longest serial chains when the grid holds at most two
 // workgroups per CU; with more, two independent 4-wavefront workgroups per CU
@@ -112,34 +132,6 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
   const int t = qt * BQ + wave * 32 + lq;
   const bool valid = t < T;
   const size_t row = static_cast<size_t>(b) * T + (valid ? t : 0);
-  int pq = valid ? pos[row] : -1;
-  if (bidir) {  // uniform: every query of the sequence sees up to its largest position in the call
-    int sm = -1;
-    for (int i = static_cast<int>(threadIdx.x); i < T; i += static_cast<int>(blockDim.x))
-      sm = max(sm, pos[static_cast<size_t>(b) * T + i]);
-#pragma unroll
-    for (int sft = 32; sft >= 1; sft >>= 1) sm = max(sm, __shfl_xor(sm, sft, 64));
-    __shared__ int s_seq[4 * NGRP];
-    if (lane == 0) s_seq[threadIdx.x >> 6] = sm;
-    __syncthreads();
-    for (int w = 0; w < 4 * NGRP; ++w) sm = max(sm, s_seq[w]);
-    if (valid) pq = sm;
-  }
-  pq = min(pq, span - 1);
-
-  // wave / workgroup position range
-  int wmax = pq, wmin = valid ? pq : 0x7fffffff;
-#pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) {
-    wmax = max(wmax, __shfl_xor(wmax, s, 64));
-    wmin = min(wmin, __shfl_xor(wmin, s, 64));
-  }
-  __shared__ int s_max[4];
-  if (lane == 0 && grp == 0) s_max[wave] = wmax;
-  __syncthreads();
-  const int gmax = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
-  if (gmax < 0) return;  // no valid query in the whole tile (uniform)
-  const int ntiles = gmax / BKV + 1;
 
   // ---- Q fragments (B operand of S^T = K Q^T): lane holds query lq, dims s*16 + hl*8 .. +8
   const size_t qstride = static_cast<size_t>(H) * DH;
@@ -182,9 +174,9 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
     }
     so = __builtin_amdgcn_readfirstlane(so);  // tile offset, uniform
 #pragma unroll
-    for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(vrs, ((4 * vkg + i) * DH + vdg * 8) * 2u, so);
+    for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(vrs, (4 * vkg * DH + vdg * 8) * 2u, so + i * DH * 2u);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(krs, ((kr + 16 * i) * DH + kc * 8) * 2u, so);
+    for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(krs, (kr * DH + kc * 8) * 2u, so + 16 * i * DH * 2u);
   };
   auto lstore = [&](int st) {
     // V goes to LDS as fp16 (the P.V product runs in fp16 so that P keeps
@@ -207,6 +199,40 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
     for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&Ks[grp][st][(kr + 16 * i) * KSTR + kc * 8]) = kreg[i];
   };
 
+  // the group's first K/V tile, in flight while the positions are read (a
+  // tile at or past the span is not needed: every tile a query sees starts
+  // below it, and a paged table has no entry there)
+  if (grp * BKV < span) gload(grp * BKV);
+
+  int pq = valid ? pos[row] : -1;
+  if (bidir) {  // uniform: every query of the sequence sees up to its largest position in the call
+    int sm = -1;
+    for (int i = static_cast<int>(threadIdx.x); i < T; i += static_cast<int>(blockDim.x))
+      sm = max(sm, pos[static_cast<size_t>(b) * T + i]);
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) sm = max(sm, __shfl_xor(sm, sft, 64));
+    __shared__ int s_seq[4 * NGRP];
+    if (lane == 0) s_seq[threadIdx.x >> 6] = sm;
+    __syncthreads();
+    for (int w = 0; w < 4 * NGRP; ++w) sm = max(sm, s_seq[w]);
+    if (valid) pq = sm;
+  }
+  pq = min(pq, span - 1);
+
+  // wave / workgroup position range
+  int wmax = pq, wmin = valid ? pq : 0x7fffffff;
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) {
+    wmax = max(wmax, __shfl_xor(wmax, s, 64));
+    wmin = min(wmin, __shfl_xor(wmin, s, 64));
+  }
+  __shared__ int s_max[4];
+  if (lane == 0 && grp == 0) s_max[wave] = wmax;
+  __syncthreads();
+  const int gmax = max(max(s_max[0], s_max[1]), max(s_max[2], s_max[3]));
+  if (gmax < 0) return;  // no valid query in the whole tile (uniform)
+  const int ntiles = gmax / BKV + 1;
+
   f32x16 oacc[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -214,10 +240,7 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
     for (int r = 0; r < 16; ++r) oacc[i][r] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  if (grp < ntiles) {
-    gload(grp * BKV);
-    lstore(0);
-  }
+  if (grp < ntiles) lstore(0);
   __syncthreads();
 
   const int k_row0 = kappa(lq) * KSTR + hl * 8;
@@ -262,12 +285,12 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
         mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
       }
-      // Running max m_run (log2 units; the scale is positive, so max and
-      // scaling commute).  Output and sum carry the same factor 2^15, which
-      // the final division cancels.  The rescale is skipped when no query of
-      // the wave has a new max.
+      // Reference max m_run (log2 units; the scale is positive, so max and
+      // scaling commute).  Output and sum carry the same factor
+      // 2^(15 - kLazy - m_run), which the final division cancels.  The rescale is skipped unless some query
+      // of the wave has a tile max more than kLazy above its reference m_run.
       const float m_tile = mt * scale_log2;
-      if (__any(m_tile > m_run)) {  // wave-uniform
+      if (__any(m_tile > m_run + kLazy)) {  // wave-uniform
         const float m_new = fmaxf(m_tile, m_run);
         const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);  // 0 from -inf
         l_run *= alpha;
@@ -277,10 +300,10 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
           for (int r = 0; r < 16; ++r) oacc[i][r] *= alpha;
         m_run = m_new;
       }
-      const float m_sh = (m_run == -INFINITY ? 0.f : m_run) - 15.f;
-      // Each weight p = 2^(s - m_run + 15) <= 2^15 goes to the P.V product as
-      // two fp16 parts: hi = p cut to fp16's 11 significant bits (exact in
-      // fp16), lo = fp16(p - hi), so hi + lo keeps about 22 bits of p (fp16
+      const float m_sh = (m_run == -INFINITY ? 0.f : m_run) - (15.f - kLazy);
+      // Each weight p = 2^(s - m_run + 15 - kLazy) <= 2^15 goes to the P.V
+      // product as two fp16 parts: hi = p cut to fp16's 11 significant bits,
+      // lo = fp16(p - hi), so hi + lo keeps about 22 bits of p (fp16
       // alone keeps 11, which flips the bf16 rounding of the attention output
       // far more often than fp32 weights would).  The row sum adds p in fp32.
       float lsum = 0.f;
@@ -291,10 +314,7 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
         for (int r = 0; r < 16; r += 2) {
           const float p0 = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_sh));
           const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], scale_log2, -m_sh));
-          const float h0 = __uint_as_float(__float_as_uint(p0) & 0xffffe000u);
-          const float h1 = __uint_as_float(__float_as_uint(p1) & 0xffffe000u);
-          ph[kb][r >> 3][(r & 7) >> 1] = pack_f16x2(h0, h1);
-          pl[kb][r >> 3][(r & 7) >> 1] = pack_f16x2(p0 - h0, p1 - h1);
+          split_f16(p0, p1, ph[kb][r >> 3][(r & 7) >> 1], pl[kb][r >> 3][(r & 7) >> 1]);
           lsum += p0 + p1;
         }
       l_run += lsum;
