@@ -165,6 +165,39 @@ def test_attention_with_several_workgroup_rounds(bidirectional):
     G.assert_bf16_output(G.f64(y).reshape(-1, wl.d_model)[rows], yo.reshape(-1, wl.d_model)[rows], "y rows")
 
 
+@pytest.mark.parametrize("shape", [
+    # 8 query-tile workgroups: the kernel with two wave groups per tile; all rows checked
+    # (slot 70 and 250 are tiles of the second group, 150 of the first)
+    dict(d=512, H=4, Hkv=2, B=2, T=100, prior=300, slots=(70, 150, 250), rows=None),
+    # 576 workgroups: one wave group per tile, several rounds; sampled rows
+    dict(d=1024, H=8, Hkv=2, B=8, T=1100, prior=200, slots=(70, 100, 150), rows=5),
+])
+def test_planted_keys_move_the_reference_max(shape):
+    """Keys of a prior cache scaled by 40, 40 and 4 at three slots past the
+    first key tile: the scores against them reach hundreds, so many queries'
+    maxima jump far past the value their weights were taken against when the
+    tile arrives, and the attention output is then dominated by one value row
+    (the causal softmax of the LMDrive page §2.3 with the notes' Ch.04 cache,
+    evaluated by the oracle in fp64)."""
+    wl = _wl(d=shape["d"], H=shape["H"], Hkv=shape["Hkv"], f=1408, B=shape["B"], T=shape["T"],
+             prior=shape["prior"], seed=43)
+    print(f"case {wl} planted slots {shape['slots']}", flush=True)
+    w, x, kc, vc, pos, layer = _setup(wl)
+    kf = kc.float()
+    for slot, s in zip(shape["slots"], (40.0, 40.0, 4.0)):
+        kf[:, :, slot] *= s
+    kc.copy_(kf.to(kc.dtype))
+    kc0, vc0 = kc.clone(), vc.clone()
+    y = layer.prefill(x, pos, kc, vc)
+    if shape["rows"] is None:
+        _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc)
+        return
+    torch.cuda.synchronize()
+    rows = G.sample_rows(wl.batch, wl.seq, seed=shape["rows"])
+    yo, _, _ = G.oracle_prefill(wl, G.oracle_weights(w), x, pos, kc0, vc0, rows=rows)
+    G.assert_bf16_output(G.f64(y).reshape(-1, wl.d_model)[rows], yo.reshape(-1, wl.d_model)[rows], "y rows")
+
+
 @pytest.mark.parametrize("B,H,Hkv", [(5, 4, 2), (1, 4, 1), (40, 4, 4),
                                      # query heads per kv head 3, 5, 6, 7: every decode
                                      # attention width below 8 (5 and up: one workgroup per CU)
