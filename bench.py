@@ -13,6 +13,11 @@ Also reported on the same line:
                 timed live with HIP events on the library's stream during the
                 timed steps, against the 2.5 PFLOP/s dense bf16 MFMA peak;
                 layer_mfma_frac is the whole layer call's fraction;
+  layer.step_roofline, decode.step_roofline
+                every step of the per-step breakdown against its own
+                roofline (flops against the bf16 peak for the projections
+                and the prefill attention, HBM bytes against 8 TB/s for the
+                norms, the decode attention and the decode projections);
   decode        LLaMA-7B-shape decode step (32 sequences at position 4095):
                 algorithmic bytes / step time against 8 TB/s HBM, with the
                 oracle's rate on a sample of it (decode.cpu_baseline);
@@ -63,6 +68,48 @@ def decode_bytes(wl, B, pos):
     es = 2
     p_lin = d * (H + 2 * Hkv) * dh + H * dh * d + 3 * d * f
     return es * (p_lin + 2 * d) + es * B * 2 * Hkv * dh * pos + es * B * 2 * Hkv * dh + 2 * es * B * d
+
+
+def step_rooflines(wl, B, T, step_ms, pos=None):
+    """Each step of the per-step breakdown against its own roofline: the
+    projections and the prefill attention in algorithmic flops against the
+    bf16 peak, the RMSNorms and the decode attention in algorithmic HBM
+    bytes against 8 TB/s; weight-streaming (decode) projections in weight
+    bytes.  Times are the event-timed steps, each with its launch gap.
+    Prefill: T tokens at positions 0..T-1 per sequence; decode (pos given):
+    one token per sequence at position pos."""
+    d, H, Hkv, dh, f = wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff
+    M, es = B * T, 2
+    nqkv = (H + 2 * Hkv) * dh
+    if pos is None:
+        work = {
+            "rmsnorm_attn": ("GB/s", es * (2 * M * d + d)),
+            "qkv_rope_cache": ("TFLOP/s", 2 * M * nqkv * d),
+            "attention": ("TFLOP/s", 4 * dh * H * B * (T * (T + 1) // 2)),
+            "o_proj_residual": ("TFLOP/s", 2 * M * d * H * dh),
+            "rmsnorm_mlp": ("GB/s", 4 * M * d + es * (M * d + d)),
+            "gate_up_swiglu": ("TFLOP/s", 2 * M * 2 * f * d),
+            "down_residual": ("TFLOP/s", 2 * M * d * f),
+        }
+    else:
+        work = {
+            "rmsnorm_attn": ("GB/s", es * (2 * M * d + d)),
+            "qkv_rope_cache": ("GB/s", es * nqkv * d),
+            "attention": ("GB/s", es * B * 2 * Hkv * dh * (pos + 1)),
+            "o_proj_residual": ("GB/s", es * d * H * dh),
+            "rmsnorm_mlp": ("GB/s", 4 * M * d + es * (M * d + d)),
+            "gate_up_swiglu": ("GB/s", es * 2 * f * d),
+            "down_residual": ("GB/s", es * d * f),
+        }
+    out = {}
+    for k, (unit, amount) in work.items():
+        if k not in step_ms:
+            continue
+        t = step_ms[k] * 1e-3
+        rate = amount / t / (1e12 if unit == "TFLOP/s" else 1e9)
+        peak = PEAK_BF16_TFLOPS if unit == "TFLOP/s" else PEAK_HBM_GBPS
+        out[k] = {"unit": unit, "achieved": rate, "frac": rate / peak}
+    return out
 
 
 def source_sha(path):
@@ -190,7 +237,8 @@ def bench_decode(lib, synth, steps, warmup):
             "hbm_frac": nbytes / med / 1e6 / PEAK_HBM_GBPS, "tokens_per_s": B / med * 1e3,
             "cache_flush_between_steps": "512 MB read",
             "step_ms_by_kernel": breakdown,
-            "step_ms_by_kernel_note": "separate untimed pass with HIP events around every step"}
+            "step_ms_by_kernel_note": "separate untimed pass with HIP events around every step",
+            "step_roofline": step_rooflines(wl, B, 1, breakdown, pos=p)}
 
 
 def bench_decode_paged(lib, synth, steps, warmup, page=64):
@@ -555,7 +603,8 @@ def main():
         "layer": {"flops_per_step": flops, "tflops": flops / (ms_per_step * 1e-3) / 1e12,
                   "mfma_frac": flops / (ms_per_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                   "step_ms_by_kernel": step_avg,
-                  "step_ms_by_kernel_note": "separate untimed pass with HIP events around every step"},
+                  "step_ms_by_kernel_note": "separate untimed pass with HIP events around every step",
+                  "step_roofline": step_rooflines(wl, B, T, step_avg)},
     }
     if not args.no_decode:
         out["decode"] = bench_decode(lib, synth, args.decode_steps, 3)
