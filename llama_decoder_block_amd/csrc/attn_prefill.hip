@@ -69,7 +69,6 @@ __device__ __forceinline__ int kappa(int m) {  // swap bits 2 and 3
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // two bf16 (one 32-bit word) -> two fp16: exact for |v| in [2^-14, 65504]
 // (fp16 carries bf16's 8 significant bits with 3 to spare); below that fp16's
@@ -77,12 +76,6 @@ typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   typedef __fp16 h16x2 __attribute__((ext_vector_type(2)));
   const h16x2 h = __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16), __uint_as_float(w & 0xffff0000u));
-  return __builtin_bit_cast(uint32_t, h);
-}
-
-// two fp32 -> two fp16, round to nearest even
-__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
-  const f16x2 h = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
   return __builtin_bit_cast(uint32_t, h);
 }
 
@@ -287,8 +280,9 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
       }
       // Reference max m_run (log2 units; the scale is positive, so max and
       // scaling commute).  Output and sum carry the same factor
-      // 2^(15 - kLazy - m_run), which the final division cancels.  The rescale is skipped unless some query
-      // of the wave has a tile max more than kLazy above its reference m_run.
+      // 2^(15 - kLazy - m_run), which the final division cancels.  The
+      // rescale is skipped unless some query of the wave has a tile max more
+      // than kLazy above its reference m_run.
       const float m_tile = mt * scale_log2;
       if (__any(m_tile > m_run + kLazy)) {  // wave-uniform
         const float m_new = fmaxf(m_tile, m_run);
