@@ -192,7 +192,7 @@ def _f64(a):
 
 def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_heads,
                   eps=1e-6, rope_base=10000.0, bf16_points=False, rows=None,
-                  bidirectional=False, kv_exact=None):
+                  bidirectional=False, kv_exact=None, kv_store=None):
     """One pre-norm decoder layer forward over B sequences with a KV cache.
 
         X'  = x  + o_proj(CausalAttn(RoPE(q, k), v))      q,k,v = proj(RMSNorm1(x))
@@ -218,6 +218,10 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
                rounding (in the bf16 points mode they are computed from the
                rounded normalised activations; the cache holds their bf16
                rounding).  Token (b, t) is [b, :, t].
+    kv_store   optional function applied to the new tokens' keys and values
+               [B, Hkv, T, dh] (after the cache dtype's rounding) before they
+               are written to the cache: the int8 cache stores
+               dequantize(quantize(.)) of each row (kv_int8_store).
 
     Returns (y [B, T, d] (rows not asked for are NaN), k_cache', v_cache').
     """
@@ -244,6 +248,8 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
         kv_exact["k"], kv_exact["v"] = k.copy(), v.copy()
     k = r(k)
     v = r(v)
+    if kv_store is not None:
+        k, v = kv_store(k), kv_store(v)
     for b in range(B):
         kc[b][:, pos[b], :] = k[b]
         vc[b][:, pos[b], :] = v[b]
@@ -277,6 +283,70 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
         h_ = r(swiglu_hidden(xn2, W["w_gate"], W["w_up"]), "fp16")
         y[b, ts] = x1 + h_ @ W["w_down"].T
     return y, kc, vc
+
+
+# --------------------------------------------------------------------------
+# int8 KV cache  [Notes Ch.04 (KV-cache memory: bytes = 2 B T Hkv dh x the
+# element size, and quantising the cache as a lever beside GQA/MQA); "Llama
+# MLP deep dive" §6.4 (KV-cache quantisation named)].  The pages give no
+# scheme; the reading here: symmetric int8 codes with one fp32 scale per
+# cached row (one token's 128 dims of one kv head), taken from the row's bf16
+# values.  The code decision is made in fp32, the format the GPU decides it in:
+#   amax = max |x|;  s = fp32(amax / 127);  inv = fp32(127 / amax);
+#   c = rint(fp32(x * inv))  (round half to even), in [-127, 127];
+#   a row of zeros has s = 0 and codes 0.  The row stands for c * s.
+# --------------------------------------------------------------------------
+
+def kv_int8_quantize(rows):
+    """rows [..., dh] (values exact in fp32, e.g. bf16) -> (codes int8
+    [..., dh], scales float32 [...])."""
+    x = np.asarray(rows, dtype=np.float64).astype(np.float32)
+    amax = np.max(np.abs(x), axis=-1)
+    zero = amax == 0
+    safe = np.where(zero, np.float32(1), amax).astype(np.float32)
+    inv = (np.float32(127) / safe).astype(np.float32)
+    codes = np.rint((x * inv[..., None]).astype(np.float32))
+    codes = np.clip(codes, -127, 127)
+    codes = np.where(zero[..., None], 0, codes).astype(np.int8)
+    scales = np.where(zero, np.float32(0), (safe / np.float32(127)).astype(np.float32)).astype(np.float32)
+    return codes, scales
+
+
+def kv_int8_dequantize(codes, scales):
+    """codes int8 [..., dh], scales [...] -> the values they stand for (fp64)."""
+    return np.asarray(codes, dtype=np.float64) * np.asarray(scales, dtype=np.float64)[..., None]
+
+
+def kv_int8_store(rows):
+    """What the int8 cache holds for rows [..., dh]: dequantize(quantize(rows))."""
+    return kv_int8_dequantize(*kv_int8_quantize(rows))
+
+
+def decoder_layer_decode_int8(x, positions, weights, k_codes, k_scales, v_codes, v_scales, **kw):
+    """One decode step over an int8 cache: x [B, d], positions [B]; the cache
+    as codes [B, Hkv, S, dh] and scales [B, Hkv, S].  The new token's key and
+    value (bf16-rounded in the bf16 points mode, as the bf16 cache would hold
+    them) are quantized into slot positions[b]; attention reads every visible
+    slot as c * s.  Returns (y [B, d], k_codes', k_scales', v_codes',
+    v_scales')."""
+    x = _f64(x)
+    B, d = x.shape
+    pos = np.asarray(_f64(positions), dtype=np.int64).reshape(B)
+    kc = kv_int8_dequantize(k_codes, k_scales)
+    vc = kv_int8_dequantize(v_codes, v_scales)
+    new = {}
+
+    def store(a):  # called for k, then v
+        key = "k" if "k" not in new else "v"
+        new[key] = kv_int8_quantize(a)
+        return kv_int8_dequantize(*new[key])
+    y, _, _ = decoder_layer(x.reshape(B, 1, d), pos.reshape(B, 1), weights, kc, vc, kv_store=store, **kw)
+    kq, ks = np.array(k_codes, dtype=np.int8), np.array(k_scales, dtype=np.float32)
+    vq, vs = np.array(v_codes, dtype=np.int8), np.array(v_scales, dtype=np.float32)
+    for b in range(B):
+        kq[b, :, pos[b]], ks[b, :, pos[b]] = new["k"][0][b, :, 0], new["k"][1][b, :, 0]
+        vq[b, :, pos[b]], vs[b, :, pos[b]] = new["v"][0][b, :, 0], new["v"][1][b, :, 0]
+    return y.reshape(B, d), kq, ks, vq, vs
 
 
 # --------------------------------------------------------------------------

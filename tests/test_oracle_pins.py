@@ -599,3 +599,86 @@ def test_paged_layer_equals_contiguous_layer():
     yd, _, _ = O.decoder_layer_paged(xd[:, None], np.full((2, 1), prior + T), w, kp2, vp2, bt, ps, nblk * ps, **kw)
     ydc, _, _ = O.decoder_layer_decode(xd, np.full(2, prior + T), w, kc2, vc2, **kw)
     np.testing.assert_array_equal(yd[:, 0], ydc)
+
+
+# --------------------------------------------------------------------------
+# int8 KV cache (the reading: symmetric int8 codes, one fp32 scale per row;
+# Notes Ch.04 and "Llama MLP deep dive" §6.4 name cache quantisation, no scheme)
+# --------------------------------------------------------------------------
+
+def test_kv_int8_worked_example():
+    """[1, -2, 0.5, 0]: amax 2, 127/2 = 63.5 exactly, so 1 -> 63.5 -> 64 (half
+    to even), -2 -> -127, 0.5 -> 31.75 -> 32, 0 -> 0; scale fp32(2/127)."""
+    c, s = O.kv_int8_quantize(np.array([[1.0, -2.0, 0.5, 0.0], [0.0, 0.0, 0.0, 0.0]]))
+    assert c.dtype == np.int8 and s.dtype == np.float32
+    np.testing.assert_array_equal(c, [[64, -127, 32, 0], [0, 0, 0, 0]])
+    assert s[0] == np.float32(2.0) / np.float32(127.0) and s[1] == 0.0
+    # 2.5 * 127 / 5 = 63.5 again, now from a row whose amax is 5; 1.5 * 25.4 = 38.1
+    c, s = O.kv_int8_quantize(np.array([2.5, -5.0, 1.5, -0.0]))
+    np.testing.assert_array_equal(c, [64, -127, 38, 0])
+    # a tie that half-to-even and half-away-from-zero round apart: amax
+    # 127/32 makes 127/amax = 32 exactly, and 62.5/32 * 32 = 62.5 -> 62
+    c, s = O.kv_int8_quantize(np.array([62.5 / 32, -127 / 32, -61.5 / 32, 0.5 / 32]))
+    np.testing.assert_array_equal(c, [62, -127, -62, 0])
+    assert s == np.float32(1 / 32)
+
+
+def test_kv_int8_properties():
+    """On seeded bf16 rows: codes in [-127, 127], each row's largest magnitude
+    maps to +-127, every code is the nearest integer to x * 127/amax (error at
+    most half a step, up to fp32 rounding), negation flips the codes and keeps
+    the scale, and quantizing the dequantized row gives the same codes."""
+    rng = _rng(71)
+    x = O.bf16_round(rng.standard_normal((64, 128)) * rng.uniform(0.01, 100, (64, 1)))
+    c, s = O.kv_int8_quantize(x)
+    ci = c.astype(np.int64)
+    assert np.all(np.abs(ci) <= 127)
+    am = np.argmax(np.abs(x), axis=1)
+    np.testing.assert_array_equal(np.abs(ci[np.arange(64), am]), 127)
+    deq = O.kv_int8_dequantize(c, s)
+    step = s.astype(np.float64)[:, None]
+    # half a step, plus what the fp32 roundings of inv, s and x * inv add:
+    # |x| |1 - inv s| + s |x inv| 2^-24 <= 127 s (2^-23 + 2^-24 + 2^-24) < 4e-5 s
+    assert np.all(np.abs(x - deq) <= (0.5 + 4e-5) * step)
+    cn, sn = O.kv_int8_quantize(-x)
+    np.testing.assert_array_equal(cn.astype(np.int64), -ci)
+    np.testing.assert_array_equal(sn, s)
+    c2, s2 = O.kv_int8_quantize(deq)
+    np.testing.assert_array_equal(c2, c)
+    np.testing.assert_allclose(s2, s, rtol=1e-6)
+
+
+def test_kv_int8_decode_wiring():
+    """The int8 decode step: the new token's key and value rows are the
+    quantization of the rows the bf16 cache would hold (plain mode: the exact
+    ones), written at slot p, every other slot unchanged; the output is the
+    bf16-cache decode's up to the quantization error (a few 1e-3 here), and
+    attends to the quantized new row, not the exact one."""
+    x, w, kc, vc = _tiny(73, B=2, T=1, S=12)
+    rng = _rng(74)
+    kc[:, :, :9] = rng.standard_normal((2, 2, 9, 8))
+    vc[:, :, :9] = rng.standard_normal((2, 2, 9, 8))
+    kq, ks = O.kv_int8_quantize(kc)
+    vq, vs = O.kv_int8_quantize(vc)
+    kw = dict(n_heads=4, n_kv_heads=2)
+    pos = np.array([9, 5])
+    ex = {}
+    y8, kq2, ks2, vq2, vs2 = O.decoder_layer_decode_int8(x[:, 0], pos, w, kq, ks, vq, vs, kv_exact=ex, **kw)
+    for b in range(2):
+        cb, sb = O.kv_int8_quantize(ex["k"][b, :, 0])
+        np.testing.assert_array_equal(kq2[b, :, pos[b]], cb)
+        np.testing.assert_array_equal(ks2[b, :, pos[b]], sb)
+        cv, sv = O.kv_int8_quantize(ex["v"][b, :, 0])
+        np.testing.assert_array_equal(vq2[b, :, pos[b]], cv)
+        others = [j for j in range(12) if j != pos[b]]
+        np.testing.assert_array_equal(kq2[b][:, others], kq[b][:, others])
+        np.testing.assert_array_equal(vs2[b][:, others], vs[b][:, others])
+    # against the bf16-format decode over the dequantized prior cache
+    yd, _, _ = O.decoder_layer_decode(x[:, 0], pos, w, O.kv_int8_dequantize(kq, ks),
+                                      O.kv_int8_dequantize(vq, vs), **kw)
+    err = np.max(np.abs(y8 - yd)) / np.sqrt(np.mean(yd ** 2))
+    assert 1e-5 < err < 2e-2, err
+    # with the new rows stored exactly, the int8 step reproduces that decode
+    ye, _, _ = O.decoder_layer(x[:, :1], pos.reshape(2, 1), w, O.kv_int8_dequantize(kq, ks),
+                               O.kv_int8_dequantize(vq, vs), kv_store=O.kv_int8_store, **kw)
+    np.testing.assert_allclose(y8, ye.reshape(2, -1), rtol=0, atol=1e-12)
