@@ -179,6 +179,37 @@ int llama_layer_decode_paged(llama_layer* layer, const void* x, void* y, const i
                              void* k_pages, void* v_pages, const int32_t* block_table, int32_t blocks_per_seq,
                              int32_t page_size, int32_t n_pages, void* stream);
 
+/* int8 KV cache ("LLM mechanics lecture notes" Ch.04: the cache's memory,
+ * 2*B*T*Hkv*dh times the element size, is what decode streams every step,
+ * and quantising it is named as a lever beside GQA/MQA; "Llama MLP deep
+ * dive" page §6.4 names KV-cache quantisation).  The pages give no scheme;
+ * this one: each cached row (one token's 128 dims of one kv head) is stored
+ * as int8 codes and one fp32 scale, amax = max |x| over the row's bf16
+ * values, scale = amax/127, code = rint(x * (127/amax)) (fp32, correctly
+ * rounded divisions, round half to even; a row whose amax is below 2^-100,
+ * zeros among them: scale 0, codes 0); the
+ * row stands for code * scale.  Half the bytes of the bf16 cache, plus 4
+ * bytes per row.
+ * k_codes, v_codes  [B, Hkv, max_pos, 128] int8, 16-byte aligned.
+ * k_scale, v_scale  [B, Hkv, max_pos] float, 4-byte aligned.
+ * bf16 layers, contiguous caches only. */
+
+/* Quantize slots [0, n_slots) of B sequences of a contiguous bf16 cache
+ * [B, Hkv, max_pos, 128] (e.g. after a prefill) into the int8 cache, at the
+ * same slots.  Errors: NULL, INVALID (B < 1, n_slots outside [0, max_pos],
+ * misaligned pointers), UNSUPPORTED (fp32 layer), HIP. */
+int llama_layer_kv_quantize(llama_layer* layer, const void* k_cache, const void* v_cache, int32_t B,
+                            int32_t n_slots, void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                            void* stream);
+
+/* Decode over the int8 cache: as llama_layer_decode, with the new token's key
+ * and value quantized into slot positions[b] (codes and scale) and the
+ * attention reading every visible slot as code * scale.  Errors: as decode,
+ * plus NULL (a scale pointer), INVALID (misaligned scales), UNSUPPORTED (fp32
+ * layer). */
+int llama_layer_decode_int8(llama_layer* layer, const void* x, void* y, const int32_t* positions, int32_t B,
+                            void* k_codes, void* v_codes, float* k_scale, float* v_scale, void* stream);
+
 /* Allocation-free decode, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc).  The same computation, kernels and results as

@@ -54,12 +54,18 @@ __device__ __forceinline__ void softmax_merge(float& m1, float& l1, float* a1, f
   m1 = m;
 }
 
-template <int R, bool PAGED>
+// Q8: the int8 cache (codes [B, Hkv, max_pos, 128], one fp32 scale per row
+// in ksc / vsc): a row group's 16 lanes read its 128 codes with 8-byte loads
+// (a wavefront: 4 rows = 512 contiguous bytes per load) and the row's scale;
+// the score is the code dot product times the key row's scale, and a weight
+// multiplies the value codes after taking the value row's scale.
+template <int R, bool PAGED, bool Q8>
 __global__ __launch_bounds__(256) void attn_decode_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
-    const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ pos, float* __restrict__ part,
+    const bf16_t* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const int32_t* __restrict__ pos, float* __restrict__ part,
     bf16_t* __restrict__ o, int o_frag, int H, int Hkv, int max_pos, int span, KvPaging pg, int L, int n_split,
-    float scale_log2) {
+    float scale_log2, const float* __restrict__ ksc, const float* __restrict__ vsc) {
+  static_assert(!(Q8 && PAGED), "the int8 cache is contiguous");
   __shared__ float red_ml[4][R][2];
   __shared__ float red_o[4][R][DH];
 
@@ -97,8 +103,13 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 
   const size_t slice = PAGED ? 0 : (static_cast<size_t>(b) * Hkv + g) * max_pos * DH;
-  const bf16_t* K = k_cache + slice + static_cast<size_t>(j_begin) * DH + dc * 8;
-  const bf16_t* V = v_cache + slice + static_cast<size_t>(j_begin) * DH + dc * 8;
+  // (element offsets: 2-byte bf16 or 1-byte int8 elements)
+  constexpr int ES = Q8 ? 1 : 2;
+  const char* K = static_cast<const char*>(k_cache) + (slice + static_cast<size_t>(j_begin) * DH + dc * 8) * ES;
+  const char* V = static_cast<const char*>(v_cache) + (slice + static_cast<size_t>(j_begin) * DH + dc * 8) * ES;
+  // int8: the scales of this (sequence, kv head)'s slots from j_begin on
+  const float* KS = Q8 ? ksc + slice / DH + j_begin : nullptr;
+  const float* VS = Q8 ? vsc + slice / DH + j_begin : nullptr;
   // Paged: the 64 slots of one iteration, s0 .. s0 + 63 with s0 = j_begin +
   // j - sub (j_begin and L are multiples of 64), lie in one page.  Slot s0 + i
   // is row (page Hkv + g) page + s0 % page + i of the pool; as an offset from
@@ -121,14 +132,37 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   }
 
   // the 4 K and 4 V rows of this row group's next slots j, j + 16, ...
-  auto fetch = [&](int j, uint4 (&ku)[4], uint4 (&vu)[4]) {
+  // (int8: 8 codes per lane in .x / .y, and the rows' scales)
+  auto fetch = [&](int j, uint4 (&ku)[4], uint4 (&vu)[4], float (&kss)[4], float (&vss)[4]) {
     const long long base = PAGED ? page_shift(j) : 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bool ok = j + 16 * u < n;
       const long long r = base + j + 16 * u;
-      ku[u] = ok ? load16_nt(K + r * DH) : make_uint4(0, 0, 0, 0);
-      vu[u] = ok ? load16_nt(V + r * DH) : make_uint4(0, 0, 0, 0);
+      if constexpr (Q8) {
+        const uint2 k8 = ok ? load8_nt(K + r * DH) : make_uint2(0, 0);
+        const uint2 v8 = ok ? load8_nt(V + r * DH) : make_uint2(0, 0);
+        ku[u] = make_uint4(k8.x, k8.y, 0, 0);
+        vu[u] = make_uint4(v8.x, v8.y, 0, 0);
+        kss[u] = ok ? KS[r] : 0.f;
+        vss[u] = ok ? VS[r] : 0.f;
+      } else {
+        ku[u] = ok ? load16_nt(K + r * DH * 2) : make_uint4(0, 0, 0, 0);
+        vu[u] = ok ? load16_nt(V + r * DH * 2) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  // 8 values of a lane's row slice: bf16 pairs, or (int8) signed bytes
+  auto unpack8 = [&](const uint4& u, float (&f)[8]) {
+    if constexpr (Q8) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        f[e] = static_cast<float>(static_cast<int8_t>(u.x >> (8 * e)));
+        f[4 + e] = static_cast<float>(static_cast<int8_t>(u.y >> (8 * e)));
+      }
+    } else {
+      f[0] = lo_bf16(u.x); f[1] = hi_bf16(u.x); f[2] = lo_bf16(u.y); f[3] = hi_bf16(u.y);
+      f[4] = lo_bf16(u.z); f[5] = hi_bf16(u.z); f[6] = lo_bf16(u.w); f[7] = hi_bf16(u.w);
     }
   };
   // the rows of the next iteration are fetched before this one's arithmetic
@@ -136,22 +170,24 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   // with fewer, where up to four share a CU, it still measured 1% (R = 1, 2)
   // to 6% (R = 4) faster than fetching at the top of each iteration
   uint4 ku[4], vu[4];  // this iteration's rows
-  fetch(sub, ku, vu);
+  float kss[4], vss[4];  // (int8) their scales
+  fetch(sub, ku, vu, kss, vss);
   for (int j = sub; j < n; j += 64) {
     uint4 kn[4], vn[4];  // the next iteration's rows (prefetch)
-    fetch(j + 64, kn, vn);
+    float ksn[4], vsn[4];
+    fetch(j + 64, kn, vn, ksn, vsn);
     float sc[R][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       float kf[8];
-      kf[0] = lo_bf16(ku[u].x); kf[1] = hi_bf16(ku[u].x); kf[2] = lo_bf16(ku[u].y); kf[3] = hi_bf16(ku[u].y);
-      kf[4] = lo_bf16(ku[u].z); kf[5] = hi_bf16(ku[u].z); kf[6] = lo_bf16(ku[u].w); kf[7] = hi_bf16(ku[u].w);
+      unpack8(ku[u], kf);
 #pragma unroll
       for (int r = 0; r < R; ++r) {
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) d += qv[r][e] * kf[e];
         d = sum16_dpp(d);  // the 16 lanes of the row group
+        if constexpr (Q8) d *= kss[u];
         sc[r][u] = j + 16 * u < n ? d : -INFINITY;  // slots past the split are masked
       }
     }
@@ -170,17 +206,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       float vf[8];
-      vf[0] = lo_bf16(vu[u].x); vf[1] = hi_bf16(vu[u].x); vf[2] = lo_bf16(vu[u].y); vf[3] = hi_bf16(vu[u].y);
-      vf[4] = lo_bf16(vu[u].z); vf[5] = hi_bf16(vu[u].z); vf[6] = lo_bf16(vu[u].w); vf[7] = hi_bf16(vu[u].w);
+      unpack8(vu[u], vf);
 #pragma unroll
-      for (int r = 0; r < R; ++r)
+      for (int r = 0; r < R; ++r) {
+        const float wgt = Q8 ? sc[r][u] * vss[u] : sc[r][u];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[r][e] += sc[r][u] * vf[e];
+        for (int e = 0; e < 8; ++e) acc[r][e] += wgt * vf[e];
+      }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       ku[u] = kn[u];
       vu[u] = vn[u];
+      kss[u] = ksn[u];
+      vss[u] = vsn[u];
     }
   }
 
@@ -319,10 +358,10 @@ int decode_attn_max_splits(int max_pos, int B, int n_heads, int n_kv_heads) {
   return static_cast<int>(a < c ? a : c);
 }
 
-hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
+hipError_t launch_attn_decode(const bf16_t* q, const void* k_cache, const void* v_cache,
                               const int32_t* pos, bf16_t* o, int o_frag, float* part, int n_split,
                               int B, int n_heads, int n_kv_heads, int max_pos, int span, const KvPaging& pg,
-                              hipStream_t s) {
+                              hipStream_t s, const float* k_scale, const float* v_scale) {
   if (o_frag && B > kSkinnyMaxTokens) return hipErrorInvalidValue;
   if (pg.block_table && (pg.page % 64 || pg.page <= 0 || span > pg.blocks_per_seq * pg.page))
     return hipErrorInvalidValue;
@@ -333,15 +372,23 @@ hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16
   const dim3 grid(n_split, n_kv_heads * (n_rep / R), B);
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
   const bool paged = pg.block_table != nullptr;
+  const bool q8 = k_scale != nullptr;
+  if (q8 && (paged || !v_scale)) return hipErrorInvalidValue;
   switch (R) {
 #define LLAMA_DEC_CASE(RR)                                                                                      \
   case RR:                                                                                                      \
     if (paged)                                                                                                  \
-      hipLaunchKernelGGL((attn_decode_kernel<RR, true>), grid, dim3(256), 0, s, q, k_cache, v_cache, pos, part, \
-                         o, o_frag, n_heads, n_kv_heads, max_pos, span, pg, L, n_split, scale_log2);            \
+      hipLaunchKernelGGL((attn_decode_kernel<RR, true, false>), grid, dim3(256), 0, s, q, k_cache, v_cache, pos, \
+                         part, o, o_frag, n_heads, n_kv_heads, max_pos, span, pg, L, n_split, scale_log2,       \
+                         nullptr, nullptr);                                                                     \
+    else if (q8)                                                                                                \
+      hipLaunchKernelGGL((attn_decode_kernel<RR, false, true>), grid, dim3(256), 0, s, q, k_cache, v_cache, pos, \
+                         part, o, o_frag, n_heads, n_kv_heads, max_pos, span, pg, L, n_split, scale_log2,       \
+                         k_scale, v_scale);                                                                     \
     else                                                                                                        \
-      hipLaunchKernelGGL((attn_decode_kernel<RR, false>), grid, dim3(256), 0, s, q, k_cache, v_cache, pos,      \
-                         part, o, o_frag, n_heads, n_kv_heads, max_pos, span, pg, L, n_split, scale_log2);      \
+      hipLaunchKernelGGL((attn_decode_kernel<RR, false, false>), grid, dim3(256), 0, s, q, k_cache, v_cache,    \
+                         pos, part, o, o_frag, n_heads, n_kv_heads, max_pos, span, pg, L, n_split, scale_log2,  \
+                         nullptr, nullptr);                                                                     \
     break;
     LLAMA_DEC_CASE(1) LLAMA_DEC_CASE(2) LLAMA_DEC_CASE(3) LLAMA_DEC_CASE(4)
     LLAMA_DEC_CASE(5) LLAMA_DEC_CASE(6) LLAMA_DEC_CASE(7) LLAMA_DEC_CASE(8)

@@ -95,6 +95,11 @@ __device__ __forceinline__ uint4 load16_nt(const void* p) {
   const u32x4 v = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+__device__ __forceinline__ uint2 load8_nt(const void* p) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_nontemporal_load(static_cast<const u32x2*>(p));
+  return make_uint2(v[0], v[1]);
+}
 
 // Fragment order of a bf16 matrix [R, K] (K % 16 == 0): the operand layout of
 // v_mfma_f32_32x32x16_bf16.  The matrix is cut into 1 KB chunks of 32 rows x
@@ -186,6 +191,10 @@ struct QkvEpilogue {
   int T, n_heads, n_kv_heads, max_pos;
   int span;                // positions >= span write no slot
   KvPaging pg;
+  // stage = 1: the new keys and values go to k_cache / v_cache as staging
+  // buffers [M, Hkv, 128] (row = token * Hkv + kv head) instead of cache
+  // slots, for the int8 cache's quantizing append (pos, span still gate them)
+  int stage;
 };
 
 hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,
@@ -259,10 +268,28 @@ hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf1
 // decode_attn_max_splits bounds the splits of every span <= max_pos.
 int decode_attn_splits(int span, int B, int n_heads, int n_kv_heads);
 int decode_attn_max_splits(int max_pos, int B, int n_heads, int n_kv_heads);
-hipError_t launch_attn_decode(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
+// int8 cache (k_scale non-null, contiguous only): k_cache / v_cache hold
+// int8 codes [B, Hkv, max_pos, 128] and k_scale / v_scale one fp32 scale per
+// row [B, Hkv, max_pos]; a row stands for code * scale.
+hipError_t launch_attn_decode(const bf16_t* q, const void* k_cache, const void* v_cache,
                               const int32_t* pos, bf16_t* o, int o_frag, float* part, int n_split,
                               int B, int n_heads, int n_kv_heads, int max_pos, int span, const KvPaging& pg,
-                              hipStream_t s);
+                              hipStream_t s, const float* k_scale = nullptr, const float* v_scale = nullptr);
+
+// int8 KV cache rows (one token's 128 dims of one kv head): amax = max |x|,
+// scale = amax / 127, code = rint(x * (127 / amax)) (fp32, round half to
+// even; a row with amax below 2^-100: scale 0, codes 0).
+// Append: the staged bf16 rows of B sequences (one token each, row b * Hkv +
+// g) into slot pos[b] of the int8 cache (positions outside [0, span) write
+// nothing).
+hipError_t launch_kv_int8_append(const bf16_t* k_stage, const bf16_t* v_stage, const int32_t* pos, int B,
+                                 int n_kv_heads, int max_pos, int span, int8_t* k_codes, int8_t* v_codes,
+                                 float* k_scale, float* v_scale, hipStream_t s);
+// Convert slots [0, n_slots) of a contiguous bf16 cache [B, Hkv, max_pos, 128]
+// into the int8 cache (same slot indices).
+hipError_t launch_kv_int8_convert(const bf16_t* k_cache, const bf16_t* v_cache, int B, int n_kv_heads,
+                                  int max_pos, int n_slots, int8_t* k_codes, int8_t* v_codes, float* k_scale,
+                                  float* v_scale, hipStream_t s);
 
 // fp32 path (any shape).
 struct F32Layer {

@@ -338,7 +338,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
           dst = q.q + static_cast<size_t>(row) * (q.n_heads * 128) + hh * 128;
         } else {
           if (p < 0 || p >= q.span) continue;
-          const long long kr = kv_row(q.pg, row / q.T, hh, q.n_kv_heads, q.max_pos, p);
+          const long long kr = q.stage ? static_cast<long long>(row) * q.n_kv_heads + hh
+                                       : kv_row(q.pg, row / q.T, hh, q.n_kv_heads, q.max_pos, p);
           if (kr < 0) continue;  // no valid page for this slot
           dst = (kind == 1 ? q.k_cache : q.v_cache) + kr * 128;
         }

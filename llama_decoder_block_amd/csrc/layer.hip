@@ -97,6 +97,7 @@ struct llama_layer {
   float* gu = nullptr;    // fp32 path: [max_tokens, 2f]
   float* part = nullptr;  // split-K partials
   int part_seqs = 0;      // sequences the partial buffer holds at once
+  void* kv_stage = nullptr;  // bf16 layers: [2, rows, Hkv, 128] new keys / values for the int8 cache's append
   SkinnyScratch sk{};     // split column groups of the weight-streaming GEMMs
   int* check_flag = nullptr;  // LLAMA_LAYER_CHECK=1 at create: position validation result
   // per-step event timing (measurement aid)
@@ -123,6 +124,7 @@ struct CallScratch {
   float* part;     // decode attention split partials
   int part_seqs;   // sequences whose partials fit at once
   SkinnyScratch sk;
+  void* kv_stage;  // [2, rows, Hkv, 128] bf16 (the int8 cache's append), or null
 };
 
 // The call's cache: contiguous [B, Hkv, max_pos, 128] K and V (pg null), or
@@ -132,10 +134,14 @@ struct KvArgs {
   void* v;
   KvPaging pg;
   int span;
+  // int8 cache (contiguous, decode): k and v hold int8 codes [B, Hkv, max_pos,
+  // 128] and these one fp32 scale per row [B, Hkv, max_pos]; null for bf16/fp32
+  float* k_scale = nullptr;
+  float* v_scale = nullptr;
 };
 
 CallScratch handle_scratch(llama_layer* L) {
-  return CallScratch{L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->part_seqs, L->sk};
+  return CallScratch{L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->part_seqs, L->sk, L->kv_stage};
 }
 
 }  // namespace
@@ -167,7 +173,8 @@ void release(llama_layer* L) {
     for (auto& row : L->ev)
       for (auto& e : row) (void)hipEventDestroy(e);
   void* bufs[] = {L->wqkv, L->wo, L->wgu, L->wd, L->g1, L->g2, L->rope_cos, L->rope_sin,
-                  L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->sk.part, L->sk.cnt, L->check_flag};
+                  L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->sk.part, L->sk.cnt, L->check_flag,
+                  L->kv_stage};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
 }
@@ -336,6 +343,7 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
     ALLOC_OR_FAIL(L->check_flag, sizeof(int));
   if (cfg->dtype == LLAMA_BF16) {
     ALLOC_OR_FAIL(L->q, mt * nq * es);
+    ALLOC_OR_FAIL(L->kv_stage, 2 * mt * nkv * es);
     const int pf = part_floats(*cfg, &L->part_seqs);
     ALLOC_OR_FAIL(L->part, static_cast<size_t>(pf) * sizeof(float));
     ALLOC_OR_FAIL(L->sk.part, skinny_scratch_floats() * sizeof(float));
@@ -520,6 +528,16 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
   ep.max_pos = c.max_pos;
   ep.span = kv.span;
   ep.pg = kv.pg;
+  // int8 cache: the projection stages the new rows in bf16, the append
+  // quantizes them into their slots
+  const bool q8 = kv.k_scale != nullptr;
+  bf16_t* k_stage = static_cast<bf16_t*>(S.kv_stage);
+  bf16_t* v_stage = q8 ? k_stage + static_cast<size_t>(M) * Hkv * 128 : nullptr;
+  if (q8) {
+    ep.stage = 1;
+    ep.k_cache = k_stage;
+    ep.v_cache = v_stage;
+  }
 
   hipEvent_t* ev = nullptr;
   if (L->prof_on) {
@@ -537,22 +555,29 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
   HIP_OR_RETURN(skinny ? launch_skinny_qkv(xn, wqkv, M, nqkv, d, ep, S.sk, s)
                        : launch_gemm_qkv(xn, wqkv, M, nqkv, d, ep, s),
                 "qkv projection");
+  if (q8)
+    HIP_OR_RETURN(launch_kv_int8_append(k_stage, v_stage, pos, B, Hkv, c.max_pos, kv.span, static_cast<int8_t*>(kc),
+                                        static_cast<int8_t*>(vc), kv.k_scale, kv.v_scale, s),
+                  "int8 cache append");
   HIP_OR_RETURN(mark(2), "event record");
   if (T == 1) {
     // sequences in chunks of part_seqs (one chunk for <= 64 tokens, whose o is
     // in fragment order): contiguous caches or block-table rows move with b0
     const bool paged = kv.pg.block_table != nullptr;
-    const size_t kv_seq = paged ? 0 : static_cast<size_t>(Hkv) * c.max_pos * 128;
+    const size_t kv_seq = paged ? 0 : static_cast<size_t>(Hkv) * c.max_pos * 128;  // elements per sequence
+    const size_t kv_es = q8 ? 1 : 2;
     for (int b0 = 0; b0 < B; b0 += S.part_seqs) {
       const int nb = B - b0 < S.part_seqs ? B - b0 : S.part_seqs;
       const int ns = decode_attn_splits(kv.span, nb, H, Hkv);
       KvPaging pgc = kv.pg;
       if (paged) pgc.block_table += static_cast<size_t>(b0) * pgc.blocks_per_seq;
+      const size_t sc0 = q8 ? static_cast<size_t>(b0) * Hkv * c.max_pos : 0;  // scale rows before sequence b0
       HIP_OR_RETURN(launch_attn_decode(q + static_cast<size_t>(b0) * H * 128,
-                                       static_cast<const bf16_t*>(kc) + b0 * kv_seq,
-                                       static_cast<const bf16_t*>(vc) + b0 * kv_seq, pos + b0,
+                                       static_cast<const char*>(kc) + b0 * kv_seq * kv_es,
+                                       static_cast<const char*>(vc) + b0 * kv_seq * kv_es, pos + b0,
                                        o + static_cast<size_t>(b0) * H * 128, skinny, S.part, ns, nb, H, Hkv,
-                                       c.max_pos, kv.span, pgc, s),
+                                       c.max_pos, kv.span, pgc, s, q8 ? kv.k_scale + sc0 : nullptr,
+                                       q8 ? kv.v_scale + sc0 : nullptr),
                     "decode attention");
     }
   } else {
@@ -663,6 +688,41 @@ int llama_layer_decode(llama_layer* L, const void* x, void* y, const int32_t* po
                        void* k_cache, void* v_cache, void* stream) {
   g_last_error.clear();
   return checked_call(L, x, y, positions, B, 1, contiguous_kv(L, k_cache, v_cache), stream);
+}
+
+int llama_layer_kv_quantize(llama_layer* L, const void* k_cache, const void* v_cache, int32_t B, int32_t n_slots,
+                            void* k_codes, void* v_codes, float* k_scale, float* v_scale, void* stream) {
+  g_last_error.clear();
+  if (!L || !k_cache || !v_cache || !k_codes || !v_codes || !k_scale || !v_scale)
+    return fail(LLAMA_ERR_NULL, "layer, caches, codes and scales must be non-null");
+  if (L->cfg.dtype != LLAMA_BF16) return fail(LLAMA_ERR_UNSUPPORTED, "the int8 cache serves bf16 layers");
+  if (B < 1 || n_slots < 0 || n_slots > L->cfg.max_pos)
+    return fail(LLAMA_ERR_INVALID, "B must be >= 1 and n_slots in [0, max_pos] (got %d, %d)", B, n_slots);
+  if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_codes) || !aligned16(v_codes) ||
+      ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3u))
+    return fail(LLAMA_ERR_INVALID, "caches and codes must be 16-byte aligned, scales 4-byte aligned");
+  int cur = 0;
+  HIP_OR_RETURN(hipGetDevice(&cur), "hipGetDevice");
+  if (cur != L->device) HIP_OR_RETURN(hipSetDevice(L->device), "hipSetDevice");
+  const hipError_t e = launch_kv_int8_convert(static_cast<const bf16_t*>(k_cache), static_cast<const bf16_t*>(v_cache),
+                                              B, L->cfg.n_kv_heads, L->cfg.max_pos, n_slots,
+                                              static_cast<int8_t*>(k_codes), static_cast<int8_t*>(v_codes), k_scale,
+                                              v_scale, static_cast<hipStream_t>(stream));
+  if (cur != L->device) (void)hipSetDevice(cur);
+  return e != hipSuccess ? hip_fail(e, "int8 cache conversion") : LLAMA_OK;
+}
+
+int llama_layer_decode_int8(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
+                            void* k_codes, void* v_codes, float* k_scale, float* v_scale, void* stream) {
+  g_last_error.clear();
+  if (!L || !k_scale || !v_scale) return fail(LLAMA_ERR_NULL, "layer and scales must be non-null");
+  if (L->cfg.dtype != LLAMA_BF16) return fail(LLAMA_ERR_UNSUPPORTED, "the int8 cache serves bf16 layers");
+  if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3u)
+    return fail(LLAMA_ERR_INVALID, "scales must be 4-byte aligned");
+  KvArgs kv = contiguous_kv(L, k_codes, v_codes);
+  kv.k_scale = k_scale;
+  kv.v_scale = v_scale;
+  return checked_call(L, x, y, positions, B, 1, kv, stream);
 }
 
 int llama_layer_prefill_paged(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B, int32_t T,

@@ -160,7 +160,8 @@ __global__ __launch_bounds__(NW * 64) void skinny_kernel(const bf16_t* __restric
           dst = q.q + static_cast<size_t>(tok) * (q.n_heads * 128) + hh * 128;
         } else {
           if (p < 0 || p >= q.span) continue;
-          const long long kr = kv_row(q.pg, tok / q.T, hh, q.n_kv_heads, q.max_pos, p);
+          const long long kr = q.stage ? static_cast<long long>(tok) * q.n_kv_heads + hh
+                                       : kv_row(q.pg, tok / q.T, hh, q.n_kv_heads, q.max_pos, p);
           if (kr < 0) continue;  // no valid page for this slot
           dst = (kind == 1 ? q.k_cache : q.v_cache) + kr * 128;
         }

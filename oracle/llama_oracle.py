@@ -294,7 +294,8 @@ def decoder_layer(x, positions, weights, k_cache, v_cache, *, n_heads, n_kv_head
 # values.  The code decision is made in fp32, the format the GPU decides it in:
 #   amax = max |x|;  s = fp32(amax / 127);  inv = fp32(127 / amax);
 #   c = rint(fp32(x * inv))  (round half to even), in [-127, 127];
-#   a row of zeros has s = 0 and codes 0.  The row stands for c * s.
+#   a row whose amax is below 2^-100 (zeros among them) has s = 0 and codes
+#   0, which keeps 127 / amax finite.  The row stands for c * s.
 # --------------------------------------------------------------------------
 
 def kv_int8_quantize(rows):
@@ -302,7 +303,7 @@ def kv_int8_quantize(rows):
     [..., dh], scales float32 [...])."""
     x = np.asarray(rows, dtype=np.float64).astype(np.float32)
     amax = np.max(np.abs(x), axis=-1)
-    zero = amax == 0
+    zero = amax < np.float32(2.0 ** -100)
     safe = np.where(zero, np.float32(1), amax).astype(np.float32)
     inv = (np.float32(127) / safe).astype(np.float32)
     codes = np.rint((x * inv[..., None]).astype(np.float32))

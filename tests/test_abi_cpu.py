@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "llama_layer.h")
 MODEL_HEADER = os.path.join(ROOT, "include", "llama_model.h")
 
 
-def _declared_functions(header=HEADER, pattern=r"llama_layer_[a-z_]+"):
+def _declared_functions(header=HEADER, pattern=r"llama_layer_[a-z0-9_]+"):
     text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(" + pattern + r")\s*\(", text)))
@@ -34,7 +34,7 @@ def test_header_declares_the_abi():
 def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", lib.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    exported = set(re.findall(r"\bT (llama_[a-z_]+)\b", out))
+    exported = set(re.findall(r"\bT (llama_[a-z0-9_]+)\b", out))
     for name in _declared_functions() + _model_functions():
         assert name in exported, name
         assert hasattr(lib.LIB, name)
@@ -134,6 +134,15 @@ def test_calls_reject_null_handle():
     assert lib.LIB.llama_layer_prefill_paged(None, p, p, p, 1, 1, p, p, p, 1, 64, 1, None) == lib.LLAMA_ERR_NULL
     assert lib.LIB.llama_layer_decode_paged(None, p, p, p, 1, p, p, p, 1, 64, 1, None) == lib.LLAMA_ERR_NULL
     lib.LIB.llama_layer_destroy(None)  # no-op
+
+
+def test_int8_cache_calls_reject_bad_arguments():
+    """The int8 cache's calls check their pointers before any HIP call."""
+    p = ctypes.c_void_p(4096)
+    assert lib.LIB.llama_layer_decode_int8(None, p, p, p, 1, p, p, p, p, None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_kv_quantize(None, p, p, 1, 1, p, p, p, p, None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_kv_quantize(p, p, p, 1, 1, p, p, None, p, None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_decode_int8(p, p, p, p, 1, p, p, None, p, None) == lib.LLAMA_ERR_NULL
 
 
 def test_binding_refuses_host_tensors():

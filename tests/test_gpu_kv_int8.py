@@ -1,0 +1,126 @@
+"""GPU parity of the int8 KV cache (symmetric int8 codes, one fp32 scale per
+cached row) against the oracle's quantizer and its int8 decode step: the
+conversion of a bf16 cache bit for bit, and decode steps over the int8 cache
+at the raw 0.02 x RMS gate.  Every call goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import llama_oracle as O
+from tests import gpu_helpers as G
+
+pytestmark = pytest.mark.gpu
+
+import llama_decoder_block_amd as lib  # noqa: E402  (fails loudly if the library is not built)
+
+DEV = "cuda"
+
+
+def _wl(d=512, H=4, Hkv=2, f=1408, B=3, prior=300, steps=0, seed=51):
+    """max_pos = prior + 1 + steps: room for the appended slots"""
+    return synth.Workload("int8", "bf16", d, H, Hkv, 128, f, B, 1, prior=prior, decode_steps=steps, seed=seed)
+
+
+def _int8_cache(wl):
+    B, Hkv, S = wl.batch, wl.n_kv_heads, wl.max_pos
+    kq = torch.full((B, Hkv, S, 128), 85, dtype=torch.int8, device=DEV)  # sentinels: slots not written keep them
+    vq = torch.full((B, Hkv, S, 128), -86, dtype=torch.int8, device=DEV)
+    ks = torch.full((B, Hkv, S), 7.25, dtype=torch.float32, device=DEV)
+    vs = torch.full((B, Hkv, S), -3.5, dtype=torch.float32, device=DEV)
+    return kq, vq, ks, vs
+
+
+def test_convert_matches_the_oracle_bit_for_bit():
+    """llama_layer_kv_quantize on a bf16 cache with N(0,1) rows, rows scaled
+    by 1e-30 and 1e30, a zero row and a row below 2^-100: codes and scales
+    equal the oracle's (the same fp32 decision on the same bf16 values);
+    slots past n_slots keep their contents."""
+    wl = _wl(prior=300)
+    print(f"case {wl}", flush=True)
+    w = synth.make_weights(wl, DEV)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, 64), w)
+    kc, vc = synth.make_cache(wl, DEV)
+    kf = kc.float()
+    kf[0, 0, 3] = 0.0
+    kf[0, 1, 4] *= 1e-30
+    kf[1, 0, 5] *= 1e30
+    kf[2, 1, 6] = 2.0 ** -110
+    kc.copy_(kf.to(kc.dtype))
+    kq, vq, ks, vs = _int8_cache(wl)
+    n = 257
+    layer.kv_quantize(kc, vc, n, kq, vq, ks, vs)
+    torch.cuda.synchronize()
+    for name, cache, q, s in (("K", kc, kq, ks), ("V", vc, vq, vs)):
+        co, so = O.kv_int8_quantize(G.f64(cache)[:, :, :n])
+        np.testing.assert_array_equal(q[:, :, :n].cpu().numpy(), co, err_msg=f"{name} codes")
+        np.testing.assert_array_equal(s[:, :, :n].cpu().numpy(), so, err_msg=f"{name} scales")
+    assert torch.all(kq[:, :, n:] == 85) and torch.all(vq[:, :, n:] == -86)
+    assert torch.all(ks[:, :, n:] == 7.25) and torch.all(vs[:, :, n:] == -3.5)
+    assert torch.all(kq[0, 0, 3] == 0) and ks[0, 0, 3] == 0 and ks[2, 1, 6] == 0
+    layer.close()
+
+
+@pytest.mark.parametrize("shape", [
+    # 2 query heads per kv head, three sequences at different lengths, one split
+    dict(d=512, H=4, Hkv=2, B=3, prior=300, pos=(300, 150, 77), steps=3),
+    # 4 query heads per kv head over 4096 slots: several splits and their merge
+    dict(d=2048, H=16, Hkv=4, B=2, prior=4095, pos=(4095, 3000), steps=2),
+])
+def test_decode_steps_over_the_int8_cache(shape):
+    """A random bf16 cache converted to int8, then decode steps that append
+    quantized rows and attend over code * scale: y against the oracle's int8
+    step (bf16 rounding points, the oracle continuing from its own int8
+    cache) at the raw 0.02 x RMS gate; the appended rows within one code step
+    of the oracle's int8 rows, their codes equal to the oracle's but where
+    the two sides' bf16 values differ (then one apart, for at most 5%);
+    every other slot untouched."""
+    wl = _wl(d=shape["d"], H=shape["H"], Hkv=shape["Hkv"], B=shape["B"], prior=shape["prior"], steps=shape["steps"])
+    print(f"case {shape}", flush=True)
+    w = synth.make_weights(wl, DEV)
+    w64 = G.oracle_weights(w)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, 64), w)
+    kc, vc = synth.make_cache(wl, DEV)
+    kq, vq, ks, vs = _int8_cache(wl)
+    layer.kv_quantize(kc, vc, wl.max_pos, kq, vq, ks, vs)
+    torch.cuda.synchronize()
+    okq, oks = O.kv_int8_quantize(G.f64(kc))
+    ovq, ovs = O.kv_int8_quantize(G.f64(vc))
+    kw = dict(n_heads=wl.n_heads, n_kv_heads=wl.n_kv_heads, eps=wl.rms_eps, rope_base=wl.rope_base,
+              bf16_points=True)
+    for step in range(shape["steps"]):
+        p = np.array(shape["pos"]) + step  # below max_pos = prior + 1 + steps
+        x = synth.make_x(wl, (wl.batch,), tensor_id=synth.TID_DECODE_BASE + step, device=DEV)
+        pos = torch.tensor(p, dtype=torch.int32, device=DEV)
+        before = (kq.clone(), vq.clone(), ks.clone(), vs.clone())
+        y = layer.decode_int8(x, pos, kq, vq, ks, vs)
+        torch.cuda.synchronize()
+        ex = {}
+        yo, okq, oks, ovq, ovs = O.decoder_layer_decode_int8(G.f64(x), p, w64, okq, oks, ovq, ovs, kv_exact=ex, **kw)
+        G.assert_bf16_output(G.f64(y), yo, f"decode step {step} y")
+        for name, q, s, oq, os_, kx, prev in (("K", kq, ks, okq, oks, ex["k"], before[0]),
+                                             ("V", vq, vs, ovq, ovs, ex["v"], before[1])):
+            qn, sn = q.cpu().numpy(), s.cpu().numpy()
+            got = np.stack([O.kv_int8_dequantize(qn[b, :, p[b]], sn[b, :, p[b]]) for b in range(wl.batch)])
+            want = np.stack([O.kv_int8_dequantize(oq[b, :, p[b]], os_[b, :, p[b]]) for b in range(wl.batch)])
+            step_ = np.maximum(np.stack([sn[b, :, p[b]] for b in range(wl.batch)]),
+                               np.stack([os_[b, :, p[b]] for b in range(wl.batch)]))[..., None]
+            ref = kx[:, :, 0]  # [B, Hkv, dh], exact (before any rounding)
+            print(f"  {name} appended: max|err|/rms against the exact values = "
+                  f"{np.max(np.abs(got - ref)) / G.rms(ref):.5f} (the int8 format's own error included); "
+                  f"against the oracle's int8 row: {np.max(np.abs(got - want) / step_):.3f} steps")
+            # the two sides round the same bf16 values but where those differ: one code step at most
+            assert np.all(np.abs(got - want) <= 1.01 * step_)
+            gc = np.stack([qn[b, :, p[b]] for b in range(wl.batch)]).astype(np.int64)
+            oc = np.stack([oq[b, :, p[b]] for b in range(wl.batch)]).astype(np.int64)
+            diff = np.abs(gc - oc)
+            print(f"  {name} appended codes: {int((diff > 0).sum())}/{diff.size} differ from the oracle's, max {diff.max()}")
+            assert diff.max() <= 1 and (diff > 0).mean() <= 0.05
+            # every other slot is untouched
+            mask = np.ones(qn.shape[:3], dtype=bool)
+            for b in range(wl.batch):
+                mask[b, :, p[b]] = False
+            np.testing.assert_array_equal(qn[mask], prev.cpu().numpy()[mask])
+        # the oracle carries its own cache on: the two sides' appended rows may
+        # differ by a step where their bf16 keys differ (counted above)
+    layer.close()

@@ -621,6 +621,10 @@ def test_kv_int8_worked_example():
     c, s = O.kv_int8_quantize(np.array([62.5 / 32, -127 / 32, -61.5 / 32, 0.5 / 32]))
     np.testing.assert_array_equal(c, [62, -127, -62, 0])
     assert s == np.float32(1 / 32)
+    # rows below 2^-100 are stored as zeros; just above, quantized as usual
+    c, s = O.kv_int8_quantize(np.array([[2.0 ** -101, -(2.0 ** -102)], [2.0 ** -99, -(2.0 ** -100)]]))
+    np.testing.assert_array_equal(c, [[0, 0], [127, -64]])
+    assert s[0] == 0 and s[1] == np.float32(2.0 ** -99) / np.float32(127)
 
 
 def test_kv_int8_properties():
