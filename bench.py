@@ -23,6 +23,8 @@ Also reported on the same line:
                 oracle's rate on a sample of it (decode.cpu_baseline);
   decode_paged  the same step over a paged KV cache (pages of 64 slots in
                 shuffled order);
+  decode_int8   the same step over the int8 KV cache (codes and one fp32
+                scale per row; its own algorithmic bytes);
   other_configs the 7B shape with bidirectional attention, the 13B-shape
                 prefill, the 70B-shape GQA prefill and its 64 decode steps,
                 and greedy generation with a 32-layer 7B-shape stack;
@@ -287,6 +289,65 @@ def bench_decode_paged(lib, synth, steps, warmup, page=64):
     return {"workload": "llama7b_decode, paged KV cache", "page_slots": page, "pages": B * nb, "batch": B,
             "position": p, "ms_per_step_median": med, "bytes_per_step": nbytes, "GBps": nbytes / med / 1e6,
             "hbm_frac": nbytes / med / 1e6 / PEAK_HBM_GBPS, "tokens_per_s": B / med * 1e3}
+
+
+def decode_int8_bytes(wl, B, pos):
+    """As decode_bytes with the int8 cache: the prior K/V as int8 codes plus
+    a 4-byte scale per row, the appended rows likewise."""
+    d, H, Hkv, dh, f = wl.d_model, wl.n_heads, wl.n_kv_heads, wl.head_dim, wl.d_ff
+    es = 2
+    p_lin = d * (H + 2 * Hkv) * dh + H * dh * d + 3 * d * f
+    rows = B * 2 * Hkv * (pos + 1)
+    return es * (p_lin + 2 * d) + rows * (dh + 4) + 2 * es * B * d
+
+
+def bench_decode_int8(lib, synth, steps, warmup):
+    """The 7B decode workload over the int8 cache: the same random bf16 cache
+    converted by llama_layer_kv_quantize, then the step timed like the
+    contiguous decode (median of event-timed steps, caches evicted by a
+    512 MB read before each)."""
+    import torch
+    wl = synth.WORKLOADS["llama7b_decode"]
+    B, p = wl.batch, wl.prior
+    w = synth.make_weights(wl, "cuda")
+    x = synth.make_x(wl, (B,), device="cuda")
+    pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
+    kc, vc = synth.make_cache(wl, "cuda")
+    kq = torch.empty(kc.shape, dtype=torch.int8, device="cuda")
+    vq = torch.empty_like(kq)
+    ks = torch.empty(kc.shape[:3], dtype=torch.float32, device="cuda")
+    vs = torch.empty_like(ks)
+    y = torch.empty_like(x)
+    layer = lib.LlamaLayer(layer_config(lib, wl, B), w)
+    layer.kv_quantize(kc, vc, wl.max_pos, kq, vq, ks, vs)
+    del kc, vc
+    flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+    ramp_clocks(lambda: layer.decode_int8(x, pos, kq, vq, ks, vs, y=y))
+    for _ in range(warmup):
+        layer.decode_int8(x, pos, kq, vq, ks, vs, y=y)
+    times = []
+    for _ in range(steps):
+        flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        layer.decode_int8(x, pos, kq, vq, ks, vs, y=y)  # a repeated decode at one position is idempotent
+        e1.record(stream)
+        times.append((e0, e1))
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in times)
+    med = ms[len(ms) // 2]
+    nbytes = decode_int8_bytes(wl, B, p)
+
+    def step():
+        flush.sum()
+        layer.decode_int8(x, pos, kq, vq, ks, vs, y=y)
+    breakdown = per_step_breakdown(lib, layer, step, max(5, steps // 2))
+    layer.close()
+    return {"workload": "llama7b_decode, int8 KV cache (codes + one fp32 scale per row)", "batch": B,
+            "position": p, "ms_per_step_median": med, "bytes_per_step": nbytes, "GBps": nbytes / med / 1e6,
+            "hbm_frac": nbytes / med / 1e6 / PEAK_HBM_GBPS, "tokens_per_s": B / med * 1e3,
+            "step_ms_by_kernel": breakdown}
 
 
 def measure_ceilings(lib, runs=5):
@@ -610,6 +671,7 @@ def main():
         out["decode"] = bench_decode(lib, synth, args.decode_steps, 3)
         if not args.headline_only:
             out["decode_paged"] = bench_decode_paged(lib, synth, args.decode_steps, 3)
+            out["decode_int8"] = bench_decode_int8(lib, synth, args.decode_steps, 3)
     # fractions of what this GPU sustains (the roofline above uses the published peaks)
     ceil = measure_ceilings(lib)
     ceil["prefill_layer_frac_of_mfma_loop"] = out["layer"]["tflops"] / ceil["mfma_loop_tflops"]

@@ -33,6 +33,9 @@ Two modes:
               format of these internal operands).  Scores, softmax weights,
               the residual stream X' and the returned y are never rounded.
 
+It also holds the paged cache (gather / scatter around the same layer) and
+the int8 cache (the row quantizer, and a decode step over int8 rows).
+
 Parity status: every function below is pinned by a CPU test against what the
 pages or the mathematics fix (worked examples, invariants, library routines
 on tiny inputs); see tests/test_oracle_pins.py.

@@ -41,3 +41,11 @@ def test_decode_step_bytes():
     assert round(by["gate_up_swiglu"]) == 2 * 2 * f * d
     assert round(by["down_residual"]) == 2 * d * f
     assert round(by["attention"]) == 2 * 32 * 2 * 32 * 128 * 4096  # prior slots and the appended one
+
+
+def test_int8_decode_bytes():
+    """The int8 cache's step moves each cached row as 128 one-byte codes and a
+    4-byte scale instead of 128 bf16 values: 124 bytes less per row."""
+    wd = synth.WORKLOADS["llama7b_decode"]
+    rows = 32 * 2 * 32 * 4096  # sequences x (K, V) x kv heads x (4095 prior slots + the appended one)
+    assert bench.decode_int8_bytes(wd, 32, 4095) == bench.decode_bytes(wd, 32, 4095) - rows * (2 * 128 - 128 - 4)
