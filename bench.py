@@ -605,7 +605,9 @@ def main():
     ap.add_argument("--cpu-budget-s", type=float, default=30.0)
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other configs (13B prefill, 70B GQA prefill + 64 decode steps, the "
-                         "bidirectional variant, the generation stack, the paged decode)")
+                         "bidirectional variant, the generation stack, the paged and int8 decode)")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="keep the paged and int8 decode, skip the other configs")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for HBM byte counters)")
     args = ap.parse_args()
@@ -679,7 +681,7 @@ def main():
     if "decode" in out:
         ceil["decode_frac_of_stream_read"] = out["decode"]["GBps"] / ceil["stream_read_GBps"]
     out["ceilings"] = ceil
-    if not args.headline_only:
+    if not args.headline_only and not args.no_other_configs:
         out["other_configs"] = bench_other_configs(lib, synth, max(3, args.steps // 4), 2)
         out["other_configs"]["llama7b_generate"] = bench_generate(lib, synth)
     if not args.no_cpu_baseline:

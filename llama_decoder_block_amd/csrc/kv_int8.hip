@@ -13,79 +13,112 @@
 //   (zeros among them) has scale 0 and codes 0, so 127 / amax stays finite.
 // The row stands for code * scale.
 //
-// gfx950 design: one wavefront per row, lane i holding dims 2i and 2i + 1
-// (one 32-bit word of the bf16 row: 256 B per wavefront load, 128 B of codes
-// per store); the row's amax is a wavefront max.  The work is tiny (a decode
-// step appends B * Hkv rows of K and of V), so the kernel is one launch with
-// four rows per 256-thread workgroup.
+// gfx950 design: 16 lanes per row, lane l of its row group holding dims
+// 8l .. 8l + 7 (one 16-byte bf16 load, one 8-byte code store), so a
+// wavefront quantizes 4 rows per instruction; the row's amax is a 16-lane
+// max by DPP lane moves.  The append (B * Hkv rows of K and of V per decode
+// step) takes 16 rows per 256-thread workgroup; the conversion of a whole
+// cache strides a fixed grid over the rows, with 4 row groups (16 rows) of
+// loads in flight per wavefront.
 #include "common.h"
 
 #include <math.h>
+
+#include <algorithm>
 
 namespace llama {
 namespace {
 
 constexpr int DH = 128;
 
-__device__ __forceinline__ int8_t code_of(float x, float inv) {
-  const float c = rintf(x * inv);
-  return static_cast<int8_t>(fminf(fmaxf(c, -127.f), 127.f));
+__device__ __forceinline__ float max16_dpp(float v) {  // max over the 16 lanes of a row (the moves of sum16_dpp)
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+  v = fmaxf(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+  return v;
 }
 
-// quantize one row (the calling wavefront's): src 128 bf16, dst 128 int8 + a scale
-__device__ __forceinline__ void quantize_row(const bf16_t* __restrict__ src, int8_t* __restrict__ dst,
-                                             float* __restrict__ scale, int lane) {
-  const uint32_t w = reinterpret_cast<const uint32_t*>(src)[lane];
-  const float a = lo_bf16(w), b = hi_bf16(w);
-  float m = fmaxf(fabsf(a), fabsf(b));
+__device__ __forceinline__ uint32_t code_of(float x, float inv) {
+  const float c = fminf(fmaxf(rintf(x * inv), -127.f), 127.f);
+  return static_cast<uint32_t>(static_cast<uint8_t>(static_cast<int8_t>(c)));
+}
+
+// quantize one row from its 16 lanes: u holds this lane's 8 bf16 dims; the
+// lane stores its 8 codes at dst (8 bytes) and the row's first lane the scale
+__device__ __forceinline__ void quantize8(const uint4& u, int8_t* __restrict__ dst, float* __restrict__ scale,
+                                          bool first) {
+  const float x[8] = {lo_bf16(u.x), hi_bf16(u.x), lo_bf16(u.y), hi_bf16(u.y),
+                      lo_bf16(u.z), hi_bf16(u.z), lo_bf16(u.w), hi_bf16(u.w)};
+  float m = 0.f;
 #pragma unroll
-  for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
-  int8_t ca = 0, cb = 0;
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(x[e]));
+  m = max16_dpp(m);
+  uint32_t lo = 0, hi = 0;
   float sc = 0.f;
-  if (m >= 0x1p-100f) {  // uniform over the wavefront (smaller rows are stored as zeros)
+  if (m >= 0x1p-100f) {  // uniform over the row (smaller rows are stored as zeros)
     const float inv = __fdiv_rn(127.f, m);
     sc = __fdiv_rn(m, 127.f);
-    ca = code_of(a, inv);
-    cb = code_of(b, inv);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo |= code_of(x[e], inv) << (8 * e);
+      hi |= code_of(x[4 + e], inv) << (8 * e);
+    }
   }
-  reinterpret_cast<uint16_t*>(dst)[lane] =
-      static_cast<uint16_t>(static_cast<uint8_t>(ca) | (static_cast<uint16_t>(static_cast<uint8_t>(cb)) << 8));
-  if (lane == 0) *scale = sc;
+  *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+  if (first) *scale = sc;
 }
 
 // rows r = (kv 0 / 1) * B * Hkv + b * Hkv + g: the staged row of sequence b,
-// kv head g goes to slot pos[b]
+// kv head g goes to slot pos[b]; 16 lanes per row
 __global__ __launch_bounds__(256) void kv_int8_append_kernel(
     const bf16_t* __restrict__ ks, const bf16_t* __restrict__ vs, const int32_t* __restrict__ pos, int B,
     int Hkv, int max_pos, int span, int8_t* __restrict__ kq, int8_t* __restrict__ vq,
     float* __restrict__ ksc, float* __restrict__ vsc) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int dc = threadIdx.x & 15;
+  const int r = blockIdx.x * 16 + (threadIdx.x >> 4);
   const int rows = B * Hkv;
-  if (r >= 2 * rows) return;
+  if (r >= 2 * rows) return;  // whole row groups leave together
   const bool is_v = r >= rows;
   const int bg = is_v ? r - rows : r;
-  const int b = bg / Hkv;
-  const int p = pos[b];
+  const int p = pos[bg / Hkv];
   if (p < 0 || p >= span) return;
   const size_t slot = static_cast<size_t>(bg) * max_pos + p;
-  quantize_row((is_v ? vs : ks) + static_cast<size_t>(bg) * DH, (is_v ? vq : kq) + slot * DH,
-               (is_v ? vsc : ksc) + slot, lane);
+  const uint4 u = *reinterpret_cast<const uint4*>((is_v ? vs : ks) + static_cast<size_t>(bg) * DH + dc * 8);
+  quantize8(u, (is_v ? vq : kq) + slot * DH + dc * 8, (is_v ? vsc : ksc) + slot, dc == 0);
 }
 
-// rows r = (kv 0 / 1) * B * Hkv * n_slots + (b * Hkv + g) * n_slots + j
+// rows r = (kv 0 / 1) * B * Hkv * n_slots + (b * Hkv + g) * n_slots + j; a
+// grid of at most kConvertBlocks workgroups strides over them: a row group
+// (16 lanes) takes one row per pass, and issues kConvertPasses passes' loads
+// before quantizing any
+constexpr int kConvertPasses = 4;
+constexpr int kConvertBlocks = 4096;
 __global__ __launch_bounds__(256) void kv_int8_convert_kernel(
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc, int B, int Hkv, int max_pos, int n_slots,
     int8_t* __restrict__ kq, int8_t* __restrict__ vq, float* __restrict__ ksc, float* __restrict__ vsc) {
-  const int lane = threadIdx.x & 63;
-  const long long r = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int dc = threadIdx.x & 15;
   const long long rows = static_cast<long long>(B) * Hkv * n_slots;
-  if (r >= 2 * rows) return;
-  const bool is_v = r >= rows;
-  const long long i = is_v ? r - rows : r;
-  const long long bg = i / n_slots, j = i % n_slots;
-  const size_t slot = static_cast<size_t>(bg) * max_pos + static_cast<size_t>(j);
-  quantize_row((is_v ? vc : kc) + slot * DH, (is_v ? vq : kq) + slot * DH, (is_v ? vsc : ksc) + slot, lane);
+  const long long groups = static_cast<long long>(gridDim.x) * 16;  // row groups in the grid
+  const long long g0 = static_cast<long long>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  for (long long base = 0; base < 2 * rows; base += groups * kConvertPasses) {
+    uint4 u[kConvertPasses];
+    size_t slot[kConvertPasses];
+    bool is_v[kConvertPasses];
+#pragma unroll
+    for (int k = 0; k < kConvertPasses; ++k) {  // loads first
+      const long long r0 = base + g0 + k * groups;
+      const long long r = r0 < 2 * rows ? r0 : 2 * rows - 1;  // past the end: reload the last row, store nothing
+      is_v[k] = r >= rows;
+      const long long i = is_v[k] ? r - rows : r;
+      slot[k] = static_cast<size_t>(i / n_slots) * max_pos + static_cast<size_t>(i % n_slots);
+      u[k] = *reinterpret_cast<const uint4*>((is_v[k] ? vc : kc) + slot[k] * DH + dc * 8);
+    }
+#pragma unroll
+    for (int k = 0; k < kConvertPasses; ++k)
+      if (base + g0 + k * groups < 2 * rows)  // uniform over the row group
+        quantize8(u[k], (is_v[k] ? vq : kq) + slot[k] * DH + dc * 8, (is_v[k] ? vsc : ksc) + slot[k], dc == 0);
+  }
 }
 
 }  // namespace
@@ -95,8 +128,8 @@ hipError_t launch_kv_int8_append(const bf16_t* k_stage, const bf16_t* v_stage, c
                                  float* k_scale, float* v_scale, hipStream_t s) {
   if (B <= 0) return hipSuccess;
   const long long rows = 2LL * B * n_kv_heads;
-  hipLaunchKernelGGL(kv_int8_append_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, k_stage,
-                     v_stage, pos, B, n_kv_heads, max_pos, span, k_codes, v_codes, k_scale, v_scale);
+  hipLaunchKernelGGL(kv_int8_append_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s,
+                     k_stage, v_stage, pos, B, n_kv_heads, max_pos, span, k_codes, v_codes, k_scale, v_scale);
   return hipGetLastError();
 }
 
@@ -105,8 +138,9 @@ hipError_t launch_kv_int8_convert(const bf16_t* k_cache, const bf16_t* v_cache, 
                                   float* v_scale, hipStream_t s) {
   if (B <= 0 || n_slots <= 0) return hipSuccess;
   const long long rows = 2LL * B * n_kv_heads * n_slots;
-  if ((rows + 3) / 4 > 0x7fffffffLL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(kv_int8_convert_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, k_cache,
+  const long long blocks = std::min<long long>((rows + 16 * kConvertPasses - 1) / (16 * kConvertPasses),
+                                               kConvertBlocks);
+  hipLaunchKernelGGL(kv_int8_convert_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, k_cache,
                      v_cache, B, n_kv_heads, max_pos, n_slots, k_codes, v_codes, k_scale, v_scale);
   return hipGetLastError();
 }
