@@ -66,6 +66,10 @@ def test_convert_matches_the_oracle_bit_for_bit():
     dict(d=512, H=4, Hkv=2, B=3, prior=300, pos=(300, 150, 77), steps=3),
     # 4 query heads per kv head over 4096 slots: several splits and their merge
     dict(d=2048, H=16, Hkv=4, B=2, prior=4095, pos=(4095, 3000), steps=2),
+    # 80 sequences: more tokens than the weight-streaming GEMMs take, so the
+    # tiled QKV GEMM's epilogue stages the rows (and the attention runs in
+    # chunks of sequences)
+    dict(d=512, H=4, Hkv=2, B=80, prior=200, pos=tuple(range(120, 200)), steps=1),
 ])
 def test_decode_steps_over_the_int8_cache(shape):
     """A random bf16 cache converted to int8, then decode steps that append
@@ -79,7 +83,7 @@ def test_decode_steps_over_the_int8_cache(shape):
     print(f"case {shape}", flush=True)
     w = synth.make_weights(wl, DEV)
     w64 = G.oracle_weights(w)
-    layer = lib.LlamaLayer(G.layer_config(lib, wl, 64), w)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, max(64, wl.batch)), w)
     kc, vc = synth.make_cache(wl, DEV)
     kq, vq, ks, vs = _int8_cache(wl)
     layer.kv_quantize(kc, vc, wl.max_pos, kq, vq, ks, vs)
