@@ -34,7 +34,8 @@ Two modes:
               the residual stream X' and the returned y are never rounded.
 
 It also holds the paged cache (gather / scatter around the same layer) and
-the int8 cache (the row quantizer, and a decode step over int8 rows).
+the int8 cache (the row quantizer, and a layer call -- a prefill chunk or a
+decode step -- over int8 rows).
 
 Parity status: every function below is pinned by a CPU test against what the
 pages or the mathematics fix (worked examples, invariants, library routines
@@ -326,30 +327,44 @@ def kv_int8_store(rows):
     return kv_int8_dequantize(*kv_int8_quantize(rows))
 
 
-def decoder_layer_decode_int8(x, positions, weights, k_codes, k_scales, v_codes, v_scales, **kw):
-    """One decode step over an int8 cache: x [B, d], positions [B]; the cache
-    as codes [B, Hkv, S, dh] and scales [B, Hkv, S].  The new token's key and
-    value (bf16-rounded in the bf16 points mode, as the bf16 cache would hold
-    them) are quantized into slot positions[b]; attention reads every visible
-    slot as c * s.  Returns (y [B, d], k_codes', k_scales', v_codes',
-    v_scales')."""
+def decoder_layer_int8(x, positions, weights, k_codes, k_scales, v_codes, v_scales, **kw):
+    """One layer call over an int8 cache: x [B, T, d] at positions [B, T]; the
+    cache as codes [B, Hkv, S, dh] and scales [B, Hkv, S].  Each new token's
+    key and value rows (bf16-rounded in the bf16 points mode, as the bf16
+    cache would hold them) are quantized, row by row, into slot positions[b, t]
+    before any query reads the cache; attention reads every visible slot,
+    the new ones included, as c * s.  Other keywords as for decoder_layer
+    (rows, bidirectional, kv_exact ...).  Returns (y [B, T, d], k_codes',
+    k_scales', v_codes', v_scales')."""
     x = _f64(x)
-    B, d = x.shape
-    pos = np.asarray(_f64(positions), dtype=np.int64).reshape(B)
+    B, T, d = x.shape
+    pos = np.asarray(_f64(positions), dtype=np.int64).reshape(B, T)
     kc = kv_int8_dequantize(k_codes, k_scales)
     vc = kv_int8_dequantize(v_codes, v_scales)
     new = {}
 
-    def store(a):  # called for k, then v
+    def store(a):  # called for k, then v: a [B, Hkv, T, dh]
         key = "k" if "k" not in new else "v"
         new[key] = kv_int8_quantize(a)
         return kv_int8_dequantize(*new[key])
-    y, _, _ = decoder_layer(x.reshape(B, 1, d), pos.reshape(B, 1), weights, kc, vc, kv_store=store, **kw)
+    y, _, _ = decoder_layer(x, pos, weights, kc, vc, kv_store=store, **kw)
     kq, ks = np.array(k_codes, dtype=np.int8), np.array(k_scales, dtype=np.float32)
     vq, vs = np.array(v_codes, dtype=np.int8), np.array(v_scales, dtype=np.float32)
     for b in range(B):
-        kq[b, :, pos[b]], ks[b, :, pos[b]] = new["k"][0][b, :, 0], new["k"][1][b, :, 0]
-        vq[b, :, pos[b]], vs[b, :, pos[b]] = new["v"][0][b, :, 0], new["v"][1][b, :, 0]
+        kq[b][:, pos[b]], ks[b][:, pos[b]] = new["k"][0][b], new["k"][1][b]
+        vq[b][:, pos[b]], vs[b][:, pos[b]] = new["v"][0][b], new["v"][1][b]
+    return y, kq, ks, vq, vs
+
+
+def decoder_layer_decode_int8(x, positions, weights, k_codes, k_scales, v_codes, v_scales, **kw):
+    """One decode step over an int8 cache: x [B, d], positions [B] (the
+    one-token case of decoder_layer_int8).  Returns (y [B, d], k_codes',
+    k_scales', v_codes', v_scales')."""
+    x = _f64(x)
+    B, d = x.shape
+    pos = np.asarray(_f64(positions), dtype=np.int64).reshape(B, 1)
+    y, kq, ks, vq, vs = decoder_layer_int8(x.reshape(B, 1, d), pos, weights, k_codes, k_scales, v_codes,
+                                           v_scales, **kw)
     return y.reshape(B, d), kq, ks, vq, vs
 
 

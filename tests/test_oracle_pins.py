@@ -686,3 +686,36 @@ def test_kv_int8_decode_wiring():
     ye, _, _ = O.decoder_layer(x[:, :1], pos.reshape(2, 1), w, O.kv_int8_dequantize(kq, ks),
                                O.kv_int8_dequantize(vq, vs), kv_store=O.kv_int8_store, **kw)
     np.testing.assert_allclose(y8, ye.reshape(2, -1), rtol=0, atol=1e-12)
+def test_kv_int8_prefill_is_a_run_of_decode_steps():
+    """A causal chunk over the int8 cache equals the same tokens fed one decode
+    step at a time: every new row is quantized on its own (per token and kv
+    head, not over the chunk), lands in its own slot, and every query reads the
+    chunk's earlier rows as c * s, not exactly.  Both rounding modes; the two
+    sequences start at different positions over different prior lengths; and
+    the rows= subset gives the same rows."""
+    T = 5
+    x, w, kc, vc = _tiny(75, B=2, T=T, S=16)
+    rng = _rng(76)
+    kc[:, :, :9] = rng.standard_normal((2, 2, 9, 8))
+    vc[:, :, :9] = rng.standard_normal((2, 2, 9, 8)) * 3
+    kq, ks = O.kv_int8_quantize(kc)
+    vq, vs = O.kv_int8_quantize(vc)
+    pos = np.array([[9, 10, 11, 12, 13], [4, 5, 6, 7, 8]])
+    for bf in (False, True):
+        kw = dict(n_heads=4, n_kv_heads=2, bf16_points=bf)
+        y, kq2, ks2, vq2, vs2 = O.decoder_layer_int8(x, pos, w, kq, ks, vq, vs, **kw)
+        st = (kq, ks, vq, vs)
+        ys = []
+        for t in range(T):
+            yt, *st = O.decoder_layer_decode_int8(x[:, t], pos[:, t], w, *st, **kw)
+            ys.append(yt)
+        np.testing.assert_allclose(y, np.stack(ys, axis=1), rtol=0, atol=1e-12)
+        for a, b_ in zip((kq2, ks2, vq2, vs2), st):
+            np.testing.assert_array_equal(a, b_)
+        # a chunk quantized as a whole (one amax per chunk) would differ
+        assert not np.array_equal(ks2[0, 0, 9:14], np.full(5, ks2[0, 0, 9]))
+        yr, *_ = O.decoder_layer_int8(x, pos, w, kq, ks, vq, vs, rows=[1, 7], **kw)
+        np.testing.assert_allclose(yr.reshape(10, -1)[[1, 7]], y.reshape(10, -1)[[1, 7]], rtol=0, atol=1e-12)
+        assert np.all(np.isnan(yr.reshape(10, -1)[[0, 2, 9]]))
+
+
