@@ -202,6 +202,17 @@ int llama_layer_kv_quantize(llama_layer* layer, const void* k_cache, const void*
                             int32_t n_slots, void* k_codes, void* v_codes, float* k_scale, float* v_scale,
                             void* stream);
 
+/* Prefill (a chunk of T tokens per sequence) over the int8 cache: as
+ * llama_layer_prefill, with every new token's key and value rows quantized,
+ * row by row, into slot positions[b*T + t] before the attention, which reads
+ * every visible slot (the chunk's own rows included) as code * scale; the
+ * bidirectional flag applies as for prefill.  A chunk of T tokens over an
+ * empty cache is a whole prompt.  Errors: as prefill, plus NULL (a scale
+ * pointer), INVALID (misaligned scales), UNSUPPORTED (fp32 layer). */
+int llama_layer_prefill_int8(llama_layer* layer, const void* x, void* y, const int32_t* positions, int32_t B,
+                             int32_t T, void* k_codes, void* v_codes, float* k_scale, float* v_scale,
+                             void* stream);
+
 /* Decode over the int8 cache: as llama_layer_decode, with the new token's key
  * and value quantized into slot positions[b] (codes and scale) and the
  * attention reading every visible slot as code * scale.  Errors: as decode,

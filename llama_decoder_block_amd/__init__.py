@@ -34,7 +34,7 @@ LLAMA_BF16 = 1
 
 EXPORTED = ("llama_layer_create", "llama_layer_prefill", "llama_layer_decode", "llama_layer_decode_noalloc",
             "llama_layer_prefill_paged", "llama_layer_decode_paged",
-            "llama_layer_kv_quantize", "llama_layer_decode_int8",
+            "llama_layer_kv_quantize", "llama_layer_prefill_int8", "llama_layer_decode_int8",
             "llama_layer_destroy", "llama_layer_strerror", "llama_layer_last_error",
             "llama_layer_profile", "llama_layer_profile_read", "llama_layer_step_name",
             "llama_layer_ceiling_mfma", "llama_layer_ceiling_read")
@@ -103,6 +103,8 @@ def _load():
     lib.llama_layer_decode_noalloc.restype = ctypes.c_int
     lib.llama_layer_kv_quantize.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.llama_layer_kv_quantize.restype = ctypes.c_int
+    lib.llama_layer_prefill_int8.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
+    lib.llama_layer_prefill_int8.restype = ctypes.c_int
     lib.llama_layer_decode_int8.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]
     lib.llama_layer_decode_int8.restype = ctypes.c_int
     lib.llama_layer_destroy.argtypes = [vp]
@@ -246,6 +248,15 @@ def llama_layer_kv_quantize(handle, k_cache, v_cache, B, n_slots, k_codes, v_cod
                                        _ptr(v_scale, "v_scale", torch.float32), _stream_ptr(stream)))
 
 
+def llama_layer_prefill_int8(handle, x, y, positions, B, T, k_codes, v_codes, k_scale, v_scale, stream=None):
+    import torch
+    _check(LIB.llama_layer_prefill_int8(handle, _ptr(x, "x"), _ptr(y, "y"),
+                                        _ptr(positions, "positions", torch.int32), int(B), int(T),
+                                        _ptr(k_codes, "k_codes", torch.int8), _ptr(v_codes, "v_codes", torch.int8),
+                                        _ptr(k_scale, "k_scale", torch.float32),
+                                        _ptr(v_scale, "v_scale", torch.float32), _stream_ptr(stream)))
+
+
 def llama_layer_decode_int8(handle, x, y, positions, B, k_codes, v_codes, k_scale, v_scale, stream=None):
     import torch
     _check(LIB.llama_layer_decode_int8(handle, _ptr(x, "x"), _ptr(y, "y"),
@@ -318,6 +329,14 @@ class LlamaLayer:
         """Quantize slots [0, n_slots) of the bf16 caches into the int8 cache (codes, scales)."""
         llama_layer_kv_quantize(self.handle, k_cache, v_cache, int(k_cache.shape[0]), n_slots, k_codes, v_codes,
                                 k_scale, v_scale, stream)
+
+    def prefill_int8(self, x, positions, k_codes, v_codes, k_scale, v_scale, y=None, stream=None):
+        """As prefill, over the int8 cache (codes and scales updated in place)."""
+        import torch
+        B, T = int(x.shape[0]), int(x.shape[1])
+        y = torch.empty_like(x) if y is None else y
+        llama_layer_prefill_int8(self.handle, x, y, positions, B, T, k_codes, v_codes, k_scale, v_scale, stream)
+        return y
 
     def decode_int8(self, x, positions, k_codes, v_codes, k_scale, v_scale, y=None, stream=None):
         """As decode, over the int8 cache: codes [B, Hkv, max_pos, 128] int8,

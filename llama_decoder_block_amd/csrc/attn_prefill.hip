@@ -89,6 +89,26 @@ __device__ __forceinline__ void split_f16(float p0, float p1, uint32_t& hi, uint
   lo = l;
 }
 
+// p0, p1 -> bf16 pairs hi = p rounded to nearest even, lo = bf16(p - hi)
+// (the difference is exact in fp32): about 16 significant bits of p, and
+// fp32's range
+__device__ __forceinline__ void split_bf16(float p0, float p1, uint32_t& hi, uint32_t& lo) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){p0, p1}, b16x2));
+  const float l0 = p0 - __uint_as_float(hi << 16), l1 = p1 - __uint_as_float(hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){l0, l1}, b16x2));
+}
+
+// an int8 code as a float (exact), from byte i of w
+__device__ __forceinline__ float code_f(uint32_t w, int i) {
+  return static_cast<float>(static_cast<int>(static_cast<int8_t>(w >> (8 * i))));
+}
+// two exact floats -> their bf16 bits packed (the low halves are zero)
+__device__ __forceinline__ uint32_t pack_bf16_exact(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
 // lazy rescaling: the reference max a wave's weights are taken against moves
 // only when some query's tile max exceeds it by more than kLazy (log2 units);
 // weights are 2^(s - ref + 15 - kLazy) <= 2^15, within fp16's range
@@ -98,14 +118,25 @@ constexpr float kLazy = 8.f;
 // (NGRP = 2 halves the longest serial chains when the grid holds at most two
 // workgroups per CU; with more, two independent 4-wavefront workgroups per CU
 // overlap better)
-template <int NGRP, bool PAGED>
+//
+// Q8: the int8 cache (contiguous).  A row stands for code * scale; the codes
+// are staged as bf16 (exact), so S^T = K_code Q^T is exact up to fp32
+// accumulation and each score is then multiplied by its row's K scale (times
+// the softmax scale); the weight of slot j enters the P.V product as
+// p_j * s_v(j) (bf16 hi + lo, fp32's range) against the V codes, while the row
+// sum adds p_j.  The tile's 64 K and 64 V scales are staged in LDS.
+template <int NGRP, bool PAGED, bool Q8>
 __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k_cache,
-    const bf16_t* __restrict__ v_cache, const int32_t* __restrict__ pos, bf16_t* __restrict__ o,
+    const bf16_t* __restrict__ q, const void* __restrict__ k_cache,
+    const void* __restrict__ v_cache, const int32_t* __restrict__ pos, bf16_t* __restrict__ o,
     int o_frag, int n_seq, int T, int H, int Hkv, int max_pos, int span, KvPaging pg, int bidir,
-    float scale_log2) {
+    float scale_log2, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
+  static_assert(!(Q8 && PAGED), "the int8 cache is contiguous");
+  constexpr uint32_t ES = Q8 ? 1u : 2u;  // bytes per cached element
   __shared__ __attribute__((aligned(16))) bf16_t Ks[NGRP][2][BKV * KSTR];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[NGRP][2][DH * VSTR];
+  // Q8: [0, 64) the tile's K scales times the softmax scale, [64, 128) its V scales
+  __shared__ __attribute__((aligned(16))) float Sc[NGRP][2][Q8 ? 2 * BKV : 4];
 
   // 1-D grid, heaviest query tiles of every (sequence, head) first
   const int n_qt = (T + BQ - 1) / BQ;
@@ -142,54 +173,107 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
   // group for its own tiles: every thread loads 4 K and 4 V chunks of 16 bytes.
   // (paged: one page per tile at most, since pages hold a multiple of 64
   // slots; a tile whose page id is out of range reads zeros)
-  const size_t slice = PAGED ? 0 : (static_cast<size_t>(b) * Hkv + g) * max_pos * DH;
-  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(k_cache + slice, static_cast<uint32_t>(max_pos) * DH * 2u);
-  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(v_cache + slice, static_cast<uint32_t>(max_pos) * DH * 2u);
+  const size_t srow = PAGED ? 0 : (static_cast<size_t>(b) * Hkv + g) * max_pos;  // the slice's first row
+  const char* const kbase = static_cast<const char*>(k_cache);
+  const char* const vbase = static_cast<const char*>(v_cache);
+  const __amdgpu_buffer_rsrc_t k_rs = make_rsrc(kbase + srow * DH * ES, static_cast<uint32_t>(max_pos) * DH * ES);
+  const __amdgpu_buffer_rsrc_t v_rs = make_rsrc(vbase + srow * DH * ES, static_cast<uint32_t>(max_pos) * DH * ES);
+  // Q8 scales: wave 0 of a group stages the tile's K scales, wave 1 its V scales
+  // (16 lanes, 16 bytes each)
+  const __amdgpu_buffer_rsrc_t sc_rs =
+      make_rsrc(Q8 ? (wave == 0 ? k_scale : v_scale) + srow : nullptr, Q8 ? static_cast<uint32_t>(max_pos) * 4u : 0u);
+  const bool sc_lane = Q8 && wave < 2 && lane < 16;
   // V: thread (vkg, vdg) loads slots 4 vkg .. 4 vkg + 3 at dims 8 vdg .. 8 vdg + 7
   // and writes them transposed as 8 rows (dims) of 4 slots, 8 bytes per row.
   // K: thread (kr, kc) loads 16-byte chunk kc of rows kr + 16 i, i < 4.
   // Every wave stages both, so the fp16 conversion work is spread evenly.
+  // Q8: K thread (kr8, kc8) loads the 16 codes (bytes) kc8 of rows kr8 and
+  // kr8 + 32; V thread (vkg, vdg) loads 8 codes per slot, 4 slots.
   const int vkg = tid & 15, vdg = tid >> 4;
   const int kr = tid >> 4, kc = tid & 15;
-  uint4 kreg[4], vreg[4];
+  const int kr8 = tid >> 3, kc8 = tid & 7;
+  uint4 kreg[Q8 ? 2 : 4], vreg[Q8 ? 2 : 4];  // Q8: vreg holds the 4 slots' 8-byte code runs
+  uint4 sreg = make_uint4(0, 0, 0, 0);
   auto gload = [&](int j0) {
-    __amdgpu_buffer_rsrc_t krs = k_rs, vrs = v_rs;
-    uint32_t so = static_cast<uint32_t>(j0) * DH * 2u;
-    if constexpr (PAGED) {  // the tile's page (uniform)
-      const int bi = j0 / pg.page;
-      const int blk = __builtin_amdgcn_readfirstlane(pg.block_table[static_cast<size_t>(b) * pg.blocks_per_seq + bi]);
-      const bool ok = blk >= 0 && blk < pg.n_pages;
-      const size_t base = ok ? (static_cast<size_t>(blk) * Hkv + g) * pg.page * DH : 0;
-      const uint32_t bytes = ok ? static_cast<uint32_t>(pg.page) * DH * 2u : 0u;
-      krs = make_rsrc(k_cache + base, bytes);
-      vrs = make_rsrc(v_cache + base, bytes);
-      so = static_cast<uint32_t>(j0 % pg.page) * DH * 2u;
+    if constexpr (Q8) {
+      const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j0) * DH);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) kreg[i] = buf_load16(k_rs, static_cast<uint32_t>(kr8 * DH + kc8 * 16), so + 32 * i * DH);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const uint2 a = buf_load8(v_rs, static_cast<uint32_t>((4 * vkg + 2 * i) * DH + vdg * 8), so);
+        const uint2 c = buf_load8(v_rs, static_cast<uint32_t>((4 * vkg + 2 * i + 1) * DH + vdg * 8), so);
+        vreg[i] = make_uint4(a.x, a.y, c.x, c.y);
+      }
+      if (sc_lane) sreg = buf_load16(sc_rs, static_cast<uint32_t>(lane) * 16u, static_cast<uint32_t>(j0) * 4u);
+    } else {
+      __amdgpu_buffer_rsrc_t krs = k_rs, vrs = v_rs;
+      uint32_t so = static_cast<uint32_t>(j0) * DH * 2u;
+      if constexpr (PAGED) {  // the tile's page (uniform)
+        const int bi = j0 / pg.page;
+        const int blk = __builtin_amdgcn_readfirstlane(pg.block_table[static_cast<size_t>(b) * pg.blocks_per_seq + bi]);
+        const bool ok = blk >= 0 && blk < pg.n_pages;
+        const size_t base = ok ? (static_cast<size_t>(blk) * Hkv + g) * pg.page * DH : 0;
+        const uint32_t bytes = ok ? static_cast<uint32_t>(pg.page) * DH * 2u : 0u;
+        krs = make_rsrc(kbase + base * 2, bytes);
+        vrs = make_rsrc(vbase + base * 2, bytes);
+        so = static_cast<uint32_t>(j0 % pg.page) * DH * 2u;
+      }
+      so = __builtin_amdgcn_readfirstlane(so);  // tile offset, uniform
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(vrs, (4 * vkg * DH + vdg * 8) * 2u, so + i * DH * 2u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(krs, (kr * DH + kc * 8) * 2u, so + 16 * i * DH * 2u);
     }
-    so = __builtin_amdgcn_readfirstlane(so);  // tile offset, uniform
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vreg[i] = buf_load16(vrs, (4 * vkg * DH + vdg * 8) * 2u, so + i * DH * 2u);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) kreg[i] = buf_load16(krs, (kr * DH + kc * 8) * 2u, so + 16 * i * DH * 2u);
   };
   auto lstore = [&](int st) {
-    // V goes to LDS as fp16 (the P.V product runs in fp16 so that P keeps
-    // 11 significant bits in one operand)
-    uint32_t w[16];  // w[4 * slot + dim/2]
-    {
-      const uint32_t* wb = reinterpret_cast<const uint32_t*>(vreg);
+    if constexpr (Q8) {  // codes -> bf16 (exact); V transposed as below
 #pragma unroll
-      for (int i = 0; i < 16; ++i) w[i] = bf16x2_to_f16x2(wb[i]);
+      for (int i = 0; i < 2; ++i) {
+        const uint32_t c[4] = {kreg[i].x, kreg[i].y, kreg[i].z, kreg[i].w};
+        uint32_t w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = pack_bf16_exact(code_f(c[e >> 1], 2 * (e & 1)), code_f(c[e >> 1], 2 * (e & 1) + 1));
+        bf16_t* dst = &Ks[grp][st][(kr8 + 32 * i) * KSTR + kc8 * 16];
+        *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<uint4*>(dst + 8) = make_uint4(w[4], w[5], w[6], w[7]);
+      }
+      // vreg[i] = slots 4 vkg + 2 i (x, y) and 4 vkg + 2 i + 1 (z, w), dims 8 vdg ..
+      const uint32_t vw[4][2] = {{vreg[0].x, vreg[0].y}, {vreg[0].z, vreg[0].w},
+                                 {vreg[1].x, vreg[1].y}, {vreg[1].z, vreg[1].w}};
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        uint2 o;
+        o.x = pack_bf16_exact(code_f(vw[0][d >> 2], d & 3), code_f(vw[1][d >> 2], d & 3));
+        o.y = pack_bf16_exact(code_f(vw[2][d >> 2], d & 3), code_f(vw[3][d >> 2], d & 3));
+        *reinterpret_cast<uint2*>(&Vt[grp][st][(vdg * 8 + d) * VSTR + 4 * vkg]) = o;
+      }
+      if (sc_lane) {
+        float4 f = make_float4(__uint_as_float(sreg.x), __uint_as_float(sreg.y), __uint_as_float(sreg.z),
+                               __uint_as_float(sreg.w));
+        if (wave == 0) f = make_float4(f.x * scale_log2, f.y * scale_log2, f.z * scale_log2, f.w * scale_log2);
+        *reinterpret_cast<float4*>(&Sc[grp][st][wave * BKV + 4 * lane]) = f;
+      }
+    } else {
+      // V goes to LDS as fp16 (the P.V product runs in fp16 so that P keeps
+      // 11 significant bits in one operand)
+      uint32_t w[16];  // w[4 * slot + dim/2]
+      {
+        const uint32_t* wb = reinterpret_cast<const uint32_t*>(vreg);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w[i] = bf16x2_to_f16x2(wb[i]);
+      }
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
+        uint2 o;
+        o.x = __builtin_amdgcn_perm(w[4 * 1 + (d >> 1)], w[4 * 0 + (d >> 1)], sel);
+        o.y = __builtin_amdgcn_perm(w[4 * 3 + (d >> 1)], w[4 * 2 + (d >> 1)], sel);
+        *reinterpret_cast<uint2*>(&Vt[grp][st][(vdg * 8 + d) * VSTR + 4 * vkg]) = o;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&Ks[grp][st][(kr + 16 * i) * KSTR + kc * 8]) = kreg[i];
     }
-#pragma unroll
-    for (int d = 0; d < 8; ++d) {
-      const uint32_t sel = (d & 1) ? 0x07060302u : 0x05040100u;
-      uint2 o;
-      o.x = __builtin_amdgcn_perm(w[4 * 1 + (d >> 1)], w[4 * 0 + (d >> 1)], sel);
-      o.y = __builtin_amdgcn_perm(w[4 * 3 + (d >> 1)], w[4 * 2 + (d >> 1)], sel);
-      *reinterpret_cast<uint2*>(&Vt[grp][st][(vdg * 8 + d) * VSTR + 4 * vkg]) = o;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&Ks[grp][st][(kr + 16 * i) * KSTR + kc * 8]) = kreg[i];
   };
 
   // the group's first K/V tile, in flight while the positions are read (a
@@ -237,6 +321,7 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
   __syncthreads();
 
   const int k_row0 = kappa(lq) * KSTR + hl * 8;
+  const float sl = Q8 ? 1.f : scale_log2;  // Q8 scores already carry the softmax scale
   const int v_row0 = lq * VSTR + hl * 8;
 
   // the trip count is the same for both groups (they share the barrier)
@@ -263,6 +348,18 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
       }
       // mask and tile max.  Register r of block kb is slot
       // j0 + 32 kb + 16 (r/8) + 8 hl + r%8.
+      if constexpr (Q8) {  // scores times the rows' K scales (which carry the softmax scale)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const float* c = &Sc[grp][st][32 * kb + 16 * hh + 8 * hl];
+            const float4 c0 = *reinterpret_cast<const float4*>(c), c1 = *reinterpret_cast<const float4*>(c + 4);
+            const float cs[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sacc[kb][8 * hh + e] *= cs[e];
+          }
+      }
       float mt = -INFINITY;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -283,7 +380,7 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
       // 2^(15 - kLazy - m_run), which the final division cancels.  The
       // rescale is skipped unless some query of the wave has a tile max more
       // than kLazy above its reference m_run.
-      const float m_tile = mt * scale_log2;
+      const float m_tile = mt * sl;
       if (__any(m_tile > m_run + kLazy)) {  // wave-uniform
         const float m_new = fmaxf(m_tile, m_run);
         const float alpha = m_new == m_run ? 1.f : fast_exp2(m_run - m_new);  // 0 from -inf
@@ -300,16 +397,31 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
       // lo = fp16(p - hi), so hi + lo keeps about 22 bits of p (fp16
       // alone keeps 11, which flips the bf16 rounding of the attention output
       // far more often than fp32 weights would).  The row sum adds p in fp32.
+      // (Q8: the weights enter P.V times the rows' V scales, as bf16 hi + lo.)
       float lsum = 0.f;
-      uint32_t ph[2][2][4], pl[2][2][4];  // [kb][half][packed fp16 pair]
+      uint32_t ph[2][2][4], pl[2][2][4];  // [kb][half][packed fp16 (Q8: bf16) pair]
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(fmaf(sacc[kb][r], scale_log2, -m_sh));
-          const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], scale_log2, -m_sh));
-          split_f16(p0, p1, ph[kb][r >> 3][(r & 7) >> 1], pl[kb][r >> 3][(r & 7) >> 1]);
-          lsum += p0 + p1;
+        for (int hh = 0; hh < 2; ++hh) {
+          float vs[8];
+          if constexpr (Q8) {
+            const float* c = &Sc[grp][st][BKV + 32 * kb + 16 * hh + 8 * hl];
+            const float4 c0 = *reinterpret_cast<const float4*>(c), c1 = *reinterpret_cast<const float4*>(c + 4);
+            vs[0] = c0.x; vs[1] = c0.y; vs[2] = c0.z; vs[3] = c0.w;
+            vs[4] = c1.x; vs[5] = c1.y; vs[6] = c1.z; vs[7] = c1.w;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const int r = 8 * hh + e;
+            const float p0 = fast_exp2(fmaf(sacc[kb][r], sl, -m_sh));
+            const float p1 = fast_exp2(fmaf(sacc[kb][r + 1], sl, -m_sh));
+            if constexpr (Q8)
+              split_bf16(p0 * vs[e], p1 * vs[e + 1], ph[kb][hh][e >> 1], pl[kb][hh][e >> 1]);
+            else
+              split_f16(p0, p1, ph[kb][hh][e >> 1], pl[kb][hh][e >> 1]);
+            lsum += p0 + p1;
+          }
         }
       l_run += lsum;
       // O^T += V^T (P_hi + P_lo)^T over 4 blocks of 16 slots
@@ -317,17 +429,30 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const f16x8 bh = __builtin_bit_cast(f16x8, make_uint4(ph[kb][half][0], ph[kb][half][1], ph[kb][half][2], ph[kb][half][3]));
-          const f16x8 bl = __builtin_bit_cast(f16x8, make_uint4(pl[kb][half][0], pl[kb][half][1], pl[kb][half][2], pl[kb][half][3]));
+          const uint4 uh = make_uint4(ph[kb][half][0], ph[kb][half][1], ph[kb][half][2], ph[kb][half][3]);
+          const uint4 ul = make_uint4(pl[kb][half][0], pl[kb][half][1], pl[kb][half][2], pl[kb][half][3]);
           const int kcol = (kb * 2 + half) * 16;
-          f16x8 a[4];
+          if constexpr (Q8) {
+            bf16x8 a[4];
 #pragma unroll
-          for (int fd = 0; fd < 4; ++fd) {
-            a[fd] = *reinterpret_cast<const f16x8*>(&Vt[grp][st][v_row0 + fd * 32 * VSTR + kcol]);
-            oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[fd], bh, oacc[fd], 0, 0, 0);
+            for (int fd = 0; fd < 4; ++fd) {
+              a[fd] = *reinterpret_cast<const bf16x8*>(&Vt[grp][st][v_row0 + fd * 32 * VSTR + kcol]);
+              oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fd], as_bf16x8(uh), oacc[fd], 0, 0, 0);
+            }
+#pragma unroll
+            for (int fd = 0; fd < 4; ++fd)
+              oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fd], as_bf16x8(ul), oacc[fd], 0, 0, 0);
+          } else {
+            const f16x8 bh = __builtin_bit_cast(f16x8, uh), bl = __builtin_bit_cast(f16x8, ul);
+            f16x8 a[4];
+#pragma unroll
+            for (int fd = 0; fd < 4; ++fd) {
+              a[fd] = *reinterpret_cast<const f16x8*>(&Vt[grp][st][v_row0 + fd * 32 * VSTR + kcol]);
+              oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[fd], bh, oacc[fd], 0, 0, 0);
+            }
+#pragma unroll
+            for (int fd = 0; fd < 4; ++fd) oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[fd], bl, oacc[fd], 0, 0, 0);
           }
-#pragma unroll
-          for (int fd = 0; fd < 4; ++fd) oacc[fd] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[fd], bl, oacc[fd], 0, 0, 0);
         }
     };
     if (it < ntiles && j0 <= wmax) {  // wave-uniform: skip tiles wholly above this wave's diagonal
@@ -389,12 +514,14 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
 
 }  // namespace
 
-hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
+hipError_t launch_attn_prefill(const bf16_t* q, const void* k_cache, const void* v_cache,
                                const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
                                int n_kv_heads, int max_pos, int span, const KvPaging& pg, int bidir,
-                               hipStream_t s) {
+                               hipStream_t s, const float* k_scale, const float* v_scale) {
   if (pg.block_table && (pg.page % BKV || pg.page <= 0 || span > pg.blocks_per_seq * pg.page))
     return hipErrorInvalidValue;
+  const bool q8 = k_scale != nullptr;
+  if (q8 && (pg.block_table || !v_scale)) return hipErrorInvalidValue;
   if (o_frag && B * T > kSkinnyMaxTokens) return hipErrorInvalidValue;
   const int n_wg = (T + BQ - 1) / BQ * n_heads * B;
   const dim3 grid(static_cast<unsigned>(n_wg));
@@ -402,14 +529,16 @@ hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf1
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return hipErrorInvalidDevice;
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
-#define LLAMA_ATTN_LAUNCH(NG, PG)                                                                          \
-  hipLaunchKernelGGL((attn_prefill_kernel<NG, PG>), grid, dim3(256 * NG), 0, s, q, k_cache, v_cache, pos, o, \
-                     o_frag, B, T, n_heads, n_kv_heads, max_pos, span, pg, bidir, scale_log2)
+#define LLAMA_ATTN_LAUNCH(NG, PG, Q8)                                                                          \
+  hipLaunchKernelGGL((attn_prefill_kernel<NG, PG, Q8>), grid, dim3(256 * NG), 0, s, q, k_cache, v_cache, pos, o, \
+                     o_frag, B, T, n_heads, n_kv_heads, max_pos, span, pg, bidir, scale_log2, k_scale, v_scale)
   const bool two = n_wg <= 2 * n_cu;  // few workgroups: halve each query tile's chain
   if (pg.block_table) {
-    if (two) LLAMA_ATTN_LAUNCH(2, true); else LLAMA_ATTN_LAUNCH(1, true);
+    if (two) LLAMA_ATTN_LAUNCH(2, true, false); else LLAMA_ATTN_LAUNCH(1, true, false);
+  } else if (q8) {
+    if (two) LLAMA_ATTN_LAUNCH(2, false, true); else LLAMA_ATTN_LAUNCH(1, false, true);
   } else {
-    if (two) LLAMA_ATTN_LAUNCH(2, false); else LLAMA_ATTN_LAUNCH(1, false);
+    if (two) LLAMA_ATTN_LAUNCH(2, false, false); else LLAMA_ATTN_LAUNCH(1, false, false);
   }
 #undef LLAMA_ATTN_LAUNCH
   return hipGetLastError();

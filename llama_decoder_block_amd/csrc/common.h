@@ -70,6 +70,8 @@ __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w 
 
 // Raw buffer resource over [base, base + bytes): loads at or past the end
 // return zeros (hardware range check), which is how tiles handle ragged edges.
+// The check covers the whole offset, the VGPR and the SGPR (soffset) parts
+// (measured on gfx950: a load past the end through either returns zero).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), 0x00020000);
@@ -80,6 +82,12 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+__device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+  return make_uint2(v[0], v[1]);
 }
 
 // Streaming loads of data that one call reads exactly once (the decode
@@ -255,10 +263,12 @@ hipError_t launch_skinny_f32out(const bf16_t* A, const bf16_t* W, int M, int N, 
 // instead of row-major.
 // max_pos: the contiguous caches' slots per (sequence, kv head); span: the
 // slots a query may see (max_pos, or the paged capacity); pg: paging.
-hipError_t launch_attn_prefill(const bf16_t* q, const bf16_t* k_cache, const bf16_t* v_cache,
+// int8 cache (k_scale non-null, contiguous only): k_cache / v_cache hold
+// int8 codes and k_scale / v_scale one fp32 scale per row, as for decode.
+hipError_t launch_attn_prefill(const bf16_t* q, const void* k_cache, const void* v_cache,
                                const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
                                int n_kv_heads, int max_pos, int span, const KvPaging& pg, int bidir,
-                               hipStream_t s);
+                               hipStream_t s, const float* k_scale = nullptr, const float* v_scale = nullptr);
 
 // Decode attention (bf16, dh = 128) for one query per sequence, split over
 // the cache when the grid would otherwise be small, followed by the merge of
@@ -279,11 +289,11 @@ hipError_t launch_attn_decode(const bf16_t* q, const void* k_cache, const void* 
 // int8 KV cache rows (one token's 128 dims of one kv head): amax = max |x|,
 // scale = amax / 127, code = rint(x * (127 / amax)) (fp32, round half to
 // even; a row with amax below 2^-100: scale 0, codes 0).
-// Append: the staged bf16 rows of B sequences (one token each, row b * Hkv +
-// g) into slot pos[b] of the int8 cache (positions outside [0, span) write
-// nothing).
+// Append: the staged bf16 rows of B sequences of T tokens (token m = b * T +
+// t, kv head g at staging row m * Hkv + g) into slot pos[m] of sequence b's
+// int8 cache (positions outside [0, span) write nothing).
 hipError_t launch_kv_int8_append(const bf16_t* k_stage, const bf16_t* v_stage, const int32_t* pos, int B,
-                                 int n_kv_heads, int max_pos, int span, int8_t* k_codes, int8_t* v_codes,
+                                 int T, int n_kv_heads, int max_pos, int span, int8_t* k_codes, int8_t* v_codes,
                                  float* k_scale, float* v_scale, hipStream_t s);
 // Convert slots [0, n_slots) of a contiguous bf16 cache [B, Hkv, max_pos, 128]
 // into the int8 cache (same slot indices).

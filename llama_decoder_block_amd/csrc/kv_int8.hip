@@ -16,8 +16,8 @@
 // gfx950 design: 16 lanes per row, lane l of its row group holding dims
 // 8l .. 8l + 7 (one 16-byte bf16 load, one 8-byte code store), so a
 // wavefront quantizes 4 rows per instruction; the row's amax is a 16-lane
-// max by DPP lane moves.  The append (B * Hkv rows of K and of V per decode
-// step) takes 16 rows per 256-thread workgroup; the conversion of a whole
+// max by DPP lane moves.  The append (B * T * Hkv rows of K and of V per layer
+// call) takes 16 rows per 256-thread workgroup; the conversion of a whole
 // cache strides a fixed grid over the rows, with 4 row groups (16 rows) of
 // loads in flight per wavefront.
 #include "common.h"
@@ -69,22 +69,24 @@ __device__ __forceinline__ void quantize8(const uint4& u, int8_t* __restrict__ d
   if (first) *scale = sc;
 }
 
-// rows r = (kv 0 / 1) * B * Hkv + b * Hkv + g: the staged row of sequence b,
-// kv head g goes to slot pos[b]; 16 lanes per row
+// rows r = (kv 0 / 1) * M * Hkv + m * Hkv + g (M = B * T tokens): the staged
+// row of token m = b * T + t, kv head g goes to slot pos[m] of sequence b;
+// 16 lanes per row
 __global__ __launch_bounds__(256) void kv_int8_append_kernel(
-    const bf16_t* __restrict__ ks, const bf16_t* __restrict__ vs, const int32_t* __restrict__ pos, int B,
-    int Hkv, int max_pos, int span, int8_t* __restrict__ kq, int8_t* __restrict__ vq,
+    const bf16_t* __restrict__ ks, const bf16_t* __restrict__ vs, const int32_t* __restrict__ pos, int M,
+    int T, int Hkv, int max_pos, int span, int8_t* __restrict__ kq, int8_t* __restrict__ vq,
     float* __restrict__ ksc, float* __restrict__ vsc) {
   const int dc = threadIdx.x & 15;
   const int r = blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int rows = B * Hkv;
+  const int rows = M * Hkv;
   if (r >= 2 * rows) return;  // whole row groups leave together
   const bool is_v = r >= rows;
-  const int bg = is_v ? r - rows : r;
-  const int p = pos[bg / Hkv];
+  const int mg = is_v ? r - rows : r;  // staging row m * Hkv + g
+  const int m = mg / Hkv, g = mg - m * Hkv;
+  const int p = pos[m];
   if (p < 0 || p >= span) return;
-  const size_t slot = static_cast<size_t>(bg) * max_pos + p;
-  const uint4 u = *reinterpret_cast<const uint4*>((is_v ? vs : ks) + static_cast<size_t>(bg) * DH + dc * 8);
+  const size_t slot = (static_cast<size_t>(m / T) * Hkv + g) * max_pos + p;
+  const uint4 u = *reinterpret_cast<const uint4*>((is_v ? vs : ks) + static_cast<size_t>(mg) * DH + dc * 8);
   quantize8(u, (is_v ? vq : kq) + slot * DH + dc * 8, (is_v ? vsc : ksc) + slot, dc == 0);
 }
 
@@ -124,12 +126,14 @@ __global__ __launch_bounds__(256) void kv_int8_convert_kernel(
 }  // namespace
 
 hipError_t launch_kv_int8_append(const bf16_t* k_stage, const bf16_t* v_stage, const int32_t* pos, int B,
-                                 int n_kv_heads, int max_pos, int span, int8_t* k_codes, int8_t* v_codes,
+                                 int T, int n_kv_heads, int max_pos, int span, int8_t* k_codes, int8_t* v_codes,
                                  float* k_scale, float* v_scale, hipStream_t s) {
-  if (B <= 0) return hipSuccess;
-  const long long rows = 2LL * B * n_kv_heads;
+  if (B <= 0 || T <= 0) return hipSuccess;
+  const long long rows = 2LL * B * T * n_kv_heads;
+  if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kv_int8_append_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s,
-                     k_stage, v_stage, pos, B, n_kv_heads, max_pos, span, k_codes, v_codes, k_scale, v_scale);
+                     k_stage, v_stage, pos, B * T, T, n_kv_heads, max_pos, span, k_codes, v_codes, k_scale,
+                     v_scale);
   return hipGetLastError();
 }
 

@@ -134,8 +134,8 @@ struct KvArgs {
   void* v;
   KvPaging pg;
   int span;
-  // int8 cache (contiguous, decode): k and v hold int8 codes [B, Hkv, max_pos,
-  // 128] and these one fp32 scale per row [B, Hkv, max_pos]; null for bf16/fp32
+  // int8 cache (contiguous): k and v hold int8 codes [B, Hkv, max_pos, 128]
+  // and these one fp32 scale per row [B, Hkv, max_pos]; null for bf16/fp32
   float* k_scale = nullptr;
   float* v_scale = nullptr;
 };
@@ -556,7 +556,7 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
                        : launch_gemm_qkv(xn, wqkv, M, nqkv, d, ep, s),
                 "qkv projection");
   if (q8)
-    HIP_OR_RETURN(launch_kv_int8_append(k_stage, v_stage, pos, B, Hkv, c.max_pos, kv.span, static_cast<int8_t*>(kc),
+    HIP_OR_RETURN(launch_kv_int8_append(k_stage, v_stage, pos, B, T, Hkv, c.max_pos, kv.span, static_cast<int8_t*>(kc),
                                         static_cast<int8_t*>(vc), kv.k_scale, kv.v_scale, s),
                   "int8 cache append");
   HIP_OR_RETURN(mark(2), "event record");
@@ -581,8 +581,8 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
                     "decode attention");
     }
   } else {
-    HIP_OR_RETURN(launch_attn_prefill(q, static_cast<const bf16_t*>(kc), static_cast<const bf16_t*>(vc), pos,
-                                      o, skinny, B, T, H, Hkv, c.max_pos, kv.span, kv.pg, c.bidirectional, s),
+    HIP_OR_RETURN(launch_attn_prefill(q, kc, vc, pos, o, skinny, B, T, H, Hkv, c.max_pos, kv.span, kv.pg,
+                                      c.bidirectional, s, kv.k_scale, kv.v_scale),
                   "prefill attention");
   }
   HIP_OR_RETURN(mark(3), "event record");
@@ -712,9 +712,8 @@ int llama_layer_kv_quantize(llama_layer* L, const void* k_cache, const void* v_c
   return e != hipSuccess ? hip_fail(e, "int8 cache conversion") : LLAMA_OK;
 }
 
-int llama_layer_decode_int8(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
-                            void* k_codes, void* v_codes, float* k_scale, float* v_scale, void* stream) {
-  g_last_error.clear();
+static int int8_call(llama_layer* L, const void* x, void* y, const int32_t* positions, int B, int T, void* k_codes,
+                     void* v_codes, float* k_scale, float* v_scale, void* stream) {
   if (!L || !k_scale || !v_scale) return fail(LLAMA_ERR_NULL, "layer and scales must be non-null");
   if (L->cfg.dtype != LLAMA_BF16) return fail(LLAMA_ERR_UNSUPPORTED, "the int8 cache serves bf16 layers");
   if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3u)
@@ -722,7 +721,19 @@ int llama_layer_decode_int8(llama_layer* L, const void* x, void* y, const int32_
   KvArgs kv = contiguous_kv(L, k_codes, v_codes);
   kv.k_scale = k_scale;
   kv.v_scale = v_scale;
-  return checked_call(L, x, y, positions, B, 1, kv, stream);
+  return checked_call(L, x, y, positions, B, T, kv, stream);
+}
+
+int llama_layer_prefill_int8(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B, int32_t T,
+                             void* k_codes, void* v_codes, float* k_scale, float* v_scale, void* stream) {
+  g_last_error.clear();
+  return int8_call(L, x, y, positions, B, T, k_codes, v_codes, k_scale, v_scale, stream);
+}
+
+int llama_layer_decode_int8(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
+                            void* k_codes, void* v_codes, float* k_scale, float* v_scale, void* stream) {
+  g_last_error.clear();
+  return int8_call(L, x, y, positions, B, 1, k_codes, v_codes, k_scale, v_scale, stream);
 }
 
 int llama_layer_prefill_paged(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B, int32_t T,

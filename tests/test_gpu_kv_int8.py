@@ -128,3 +128,81 @@ def test_decode_steps_over_the_int8_cache(shape):
         # the oracle carries its own cache on: the two sides' appended rows may
         # differ by a step where their bf16 keys differ (counted above)
     layer.close()
+
+
+def _check_appended(name, q, s, oq, os_, slots, prev_q, prev_s):
+    """The rows written at slots[b] (a list per sequence) of the int8 cache
+    (codes q [B, Hkv, S, dh], scales s) against the oracle's (oq, os_): within
+    one code step, codes equal but where the two sides' bf16 values differ (then
+    one apart, for at most 5%); every other slot unchanged from prev_q / prev_s."""
+    qn, sn = q.cpu().numpy(), s.cpu().numpy()
+    gd, od, stp, gc, oc = [], [], [], [], []
+    for b, sl in enumerate(slots):
+        gd.append(O.kv_int8_dequantize(qn[b][:, sl], sn[b][:, sl]).ravel())
+        od.append(O.kv_int8_dequantize(oq[b][:, sl], os_[b][:, sl]).ravel())
+        stp.append(np.repeat(np.maximum(sn[b][:, sl], os_[b][:, sl]).ravel(), qn.shape[-1]))
+        gc.append(qn[b][:, sl].astype(np.int64).ravel())
+        oc.append(oq[b][:, sl].astype(np.int64).ravel())
+    gd, od, stp, gc, oc = (np.concatenate(a) for a in (gd, od, stp, gc, oc))
+    diff = np.abs(gc - oc)
+    print(f"  {name} appended: {np.max(np.abs(gd - od) / np.maximum(stp, 1e-30)):.3f} steps from the oracle's "
+          f"int8 rows; codes {int((diff > 0).sum())}/{diff.size} differ, max {diff.max()}", flush=True)
+    assert np.all(np.abs(gd - od) <= 1.01 * stp)
+    assert diff.max() <= 1 and (diff > 0).mean() <= 0.05
+    mask = np.ones(qn.shape[:3], dtype=bool)
+    for b, sl in enumerate(slots):
+        mask[b][:, sl] = False
+    np.testing.assert_array_equal(qn[mask], prev_q.cpu().numpy()[mask])
+    np.testing.assert_array_equal(sn[mask], prev_s.cpu().numpy()[mask])
+
+
+@pytest.mark.parametrize("shape", [
+    # two sequences, one continuing its converted cache at 120, one a fresh
+    # prompt at 0 (ragged query tiles; few workgroups: the eight-wavefront
+    # attention kernel)
+    dict(d=512, H=4, Hkv=2, f=1408, B=2, T=150, prior=120, starts=(120, 0)),
+    # 544 query tiles: the four-wavefront kernel in several rounds, GQA 4:1,
+    # a ragged last tile; sampled rows
+    dict(d=2048, H=16, Hkv=4, f=5632, B=2, T=2100, prior=64, starts=(64, 64), sampled=True),
+    # 15 tokens: the weight-streaming GEMMs stage the rows
+    dict(d=256, H=2, Hkv=2, f=384, B=3, T=5, prior=40, starts=(40, 7, 0)),
+    # the bidirectional variant
+    dict(d=512, H=4, Hkv=2, f=1408, B=2, T=100, prior=50, starts=(50, 20), bidirectional=True),
+])
+def test_prefill_over_the_int8_cache(shape):
+    """A chunk of T tokens per sequence over a converted int8 cache: the new
+    rows are quantized into their slots and every query reads code * scale
+    (its own chunk's rows included).  y against the oracle's int8 layer call
+    at the raw 0.02 x RMS gate; the appended rows as in the decode test; every
+    other slot untouched."""
+    bidir = shape.get("bidirectional", False)
+    wl = synth.Workload("int8p", "bf16", shape["d"], shape["H"], shape["Hkv"], 128, shape["f"], shape["B"],
+                        shape["T"], prior=shape["prior"], seed=53)
+    print(f"case {shape}", flush=True)
+    B, T = wl.batch, wl.seq
+    w = synth.make_weights(wl, DEV, random_gains=True)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, B * T, bidirectional=bidir), w)
+    kc, vc = synth.make_cache(wl, DEV)
+    kq, vq, ks, vs = _int8_cache(wl)
+    layer.kv_quantize(kc, vc, wl.max_pos, kq, vq, ks, vs)
+    torch.cuda.synchronize()
+    before = (kq.clone(), ks.clone(), vq.clone(), vs.clone())
+    x = synth.make_x(wl, (B, T), device=DEV)
+    p = np.stack([np.arange(s0, s0 + T) for s0 in shape["starts"]])  # below max_pos = prior + T
+    pos = torch.tensor(p, dtype=torch.int32, device=DEV)
+    y = layer.prefill_int8(x, pos, kq, vq, ks, vs)
+    torch.cuda.synchronize()
+    rows = G.sample_rows(B, T, seed=54) if shape.get("sampled") else None
+    okq, oks = O.kv_int8_quantize(G.f64(kc))
+    ovq, ovs = O.kv_int8_quantize(G.f64(vc))
+    yo, okq, oks, ovq, ovs = O.decoder_layer_int8(
+        G.f64(x), p, G.oracle_weights(w), okq, oks, ovq, ovs, rows=rows, n_heads=wl.n_heads,
+        n_kv_heads=wl.n_kv_heads, eps=wl.rms_eps, rope_base=wl.rope_base, bf16_points=True, bidirectional=bidir)
+    yg = G.f64(y).reshape(B * T, -1)
+    yo = yo.reshape(B * T, -1)
+    sel = rows if rows is not None else slice(None)
+    G.assert_bf16_output(yg[sel], yo[sel], "y")
+    slots = [list(p[b]) for b in range(B)]
+    _check_appended("K", kq, ks, okq, oks, slots, before[0], before[1])
+    _check_appended("V", vq, vs, ovq, ovs, slots, before[2], before[3])
+    layer.close()
