@@ -25,6 +25,9 @@ Also reported on the same line:
                 shuffled order);
   decode_int8   the same step over the int8 KV cache (codes and one fp32
                 scale per row; its own algorithmic bytes);
+  prefill_int8  the headline prefill writing and reading the int8 KV cache
+                (the chunk's rows quantized into their slots; attention over
+                code * scale);
   other_configs the 7B shape with bidirectional attention, the 13B-shape
                 prefill, the 70B-shape GQA prefill and its 64 decode steps,
                 and greedy generation with a 32-layer 7B-shape stack;
@@ -195,6 +198,43 @@ def bench_prefill(lib, synth, steps, warmup):
     host = {"w": w, "x": x, "pos": pos, "kc": kc, "vc": vc}
     layer.close()
     return wl, (t1 - t0), gu_ms, avg, host
+
+
+def bench_prefill_int8(lib, synth, steps, warmup):
+    """The headline prefill (a 2048-token prompt into an empty cache) over the
+    int8 KV cache: wall time of back-to-back calls, like the headline."""
+    import torch
+    wl = synth.WORKLOADS["llama7b_prefill"]
+    B, T = wl.batch, wl.seq
+    w = synth.make_weights(wl, "cuda")
+    x = synth.make_x(wl, (B, T), device="cuda")
+    pos = synth.prefill_positions(B, T, device="cuda")
+    shape = (B, wl.n_kv_heads, wl.max_pos, wl.head_dim)
+    kq = torch.zeros(shape, dtype=torch.int8, device="cuda")
+    vq = torch.zeros_like(kq)
+    ks = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
+    vs = torch.zeros_like(ks)
+    y = torch.empty_like(x)
+    layer = lib.LlamaLayer(layer_config(lib, wl, B * T), w)
+
+    def call():
+        layer.prefill_int8(x, pos, kq, vq, ks, vs, y=y)
+    ramp_clocks(call)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / steps * 1e3
+    breakdown = per_step_breakdown(lib, layer, call, max(5, steps // 2))
+    layer.close()
+    flops = prefill_flops(wl, T, B)
+    return {"workload": "llama7b_prefill, int8 KV cache (codes + one fp32 scale per row)", "batch": B,
+            "seq_len": T, "ms_per_step": ms, "tokens_per_s": B * T / ms * 1e3,
+            "tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+            "step_ms_by_kernel": breakdown}
 
 
 def bench_decode(lib, synth, steps, warmup):
@@ -669,6 +709,8 @@ def main():
                   "step_ms_by_kernel_note": "separate untimed pass with HIP events around every step",
                   "step_roofline": step_rooflines(wl, B, T, step_avg)},
     }
+    if not args.headline_only:
+        out["prefill_int8"] = bench_prefill_int8(lib, synth, args.steps, args.warmup)
     if not args.no_decode:
         out["decode"] = bench_decode(lib, synth, args.decode_steps, 3)
         if not args.headline_only:
