@@ -33,9 +33,9 @@ Two modes:
               format of these internal operands).  Scores, softmax weights,
               the residual stream X' and the returned y are never rounded.
 
-It also holds the paged cache (gather / scatter around the same layer) and
-the int8 cache (the row quantizer, and a layer call -- a prefill chunk or a
-decode step -- over int8 rows).
+It also holds the paged cache (gather / scatter around the same layer), the
+int8 cache (the row quantizer, and a layer call -- a prefill chunk or a
+decode step -- over int8 rows), and the two combined (int8 page pools).
 
 Parity status: every function below is pinned by a CPU test against what the
 pages or the mathematics fix (worked examples, invariants, library routines
@@ -416,6 +416,35 @@ def decoder_layer_paged(x, positions, weights, k_pool, v_pool, block_table, page
     slots = [list(pos[b]) for b in range(pos.shape[0])]
     return (y, scatter_pages(kc, k_pool, block_table, page_size, slots),
             scatter_pages(vc, v_pool, block_table, page_size, slots))
+
+
+def decoder_layer_paged_int8(x, positions, weights, k_pool, k_scale_pool, v_pool, v_scale_pool, block_table,
+                             page_size, capacity, **kw):
+    """The int8 layer call over paged pools: codes [n_pages, Hkv, page, dh]
+    and scales [n_pages, Hkv, page], slot p of sequence b in page
+    block_table[b, p // page] at row p % page.  Gathers codes and scales into
+    the contiguous int8 cache, runs decoder_layer_int8 there and writes the new
+    tokens' slots back.  Returns (y, k_pool', k_scale_pool', v_pool',
+    v_scale_pool')."""
+    x = _f64(x)
+    pos = np.asarray(_f64(positions), dtype=np.int64).reshape(x.shape[0], x.shape[1])
+
+    def gather(pool, scale_pool):
+        c = gather_pages(pool, block_table, page_size, capacity).astype(np.int8)
+        s = gather_pages(np.asarray(scale_pool)[..., None], block_table, page_size, capacity)[..., 0]
+        return c, s.astype(np.float32)
+    kq, ks = gather(k_pool, k_scale_pool)
+    vq, vs = gather(v_pool, v_scale_pool)
+    y, kq, ks, vq, vs = decoder_layer_int8(x, pos, weights, kq, ks, vq, vs, **kw)
+    slots = [list(pos[b]) for b in range(pos.shape[0])]
+
+    def scatter(c, s, pool, scale_pool):
+        cp = scatter_pages(c, pool, block_table, page_size, slots).astype(np.int8)
+        sp = scatter_pages(s[..., None], np.asarray(scale_pool)[..., None], block_table, page_size, slots)[..., 0]
+        return cp, sp.astype(np.float32)
+    kp, ksp = scatter(kq, ks, k_pool, k_scale_pool)
+    vp, vsp = scatter(vq, vs, v_pool, v_scale_pool)
+    return y, kp, ksp, vp, vsp
 
 
 def decoder_layer_decode(x, positions, weights, k_cache, v_cache, **kw):

@@ -719,3 +719,43 @@ def test_kv_int8_prefill_is_a_run_of_decode_steps():
         assert np.all(np.isnan(yr.reshape(10, -1)[[0, 2, 9]]))
 
 
+
+
+def test_paged_int8_layer_equals_contiguous_int8_layer():
+    """int8 page pools (codes and per-row scales) on a shuffled table with
+    spare pages: a prefill over prior rows and then a decode step equal the
+    contiguous int8 layer on the gathered cache; a new slot's code row and
+    scale land in page table[b, p // page] at row p % page; unmapped pages
+    are untouched."""
+    H, Hkv, T, prior, ps, nblk = 4, 2, 5, 6, 4, 4
+    x, w, _, _ = _tiny(77, B=2, T=T, H=H, Hkv=Hkv)
+    dh = 32 // H
+    rng = _rng(78)
+    n_pages = 2 * nblk + 3
+    bt = rng.permutation(n_pages)[:2 * nblk].reshape(2, nblk)
+    kq, ks = O.kv_int8_quantize(rng.standard_normal((n_pages, Hkv, ps, dh)))
+    vq, vs = O.kv_int8_quantize(rng.standard_normal((n_pages, Hkv, ps, dh)) * 2)
+    pos = np.array([np.arange(prior, prior + T), np.arange(prior - 3, prior - 3 + T)])
+    cap = nblk * ps
+    kw = dict(n_heads=H, n_kv_heads=Hkv, bf16_points=True)
+    y, kq2, ks2, vq2, vs2 = O.decoder_layer_paged_int8(x, pos, w, kq, ks, vq, vs, bt, ps, cap, **kw)
+
+    def g(c, s):
+        return (O.gather_pages(c, bt, ps, cap).astype(np.int8),
+                O.gather_pages(s[..., None], bt, ps, cap)[..., 0].astype(np.float32))
+    yc, kqc, ksc, vqc, vsc = O.decoder_layer_int8(x, pos, w, *g(kq, ks), *g(vq, vs), **kw)
+    np.testing.assert_array_equal(y, yc)
+    for (c2, s2), (cc, sc) in zip((g(kq2, ks2), g(vq2, vs2)), ((kqc, ksc), (vqc, vsc))):
+        np.testing.assert_array_equal(c2, cc)
+        np.testing.assert_array_equal(s2, sc)
+    p = pos[1, 2]
+    np.testing.assert_array_equal(kq2[bt[1, p // ps], :, p % ps], kqc[1, :, p])
+    assert np.array_equal(ks2[bt[1, p // ps], :, p % ps], ksc[1, :, p])
+    spare = sorted(set(range(n_pages)) - set(bt.ravel().tolist()))
+    np.testing.assert_array_equal(kq2[spare], kq[spare])
+    np.testing.assert_array_equal(vs2[spare], vs[spare])
+    xd = _rng(79).standard_normal((2, 1, 32))
+    pd = np.array([[prior + T], [prior + 4]])
+    yd, *_ = O.decoder_layer_paged_int8(xd, pd, w, kq2, ks2, vq2, vs2, bt, ps, cap, **kw)
+    ydc, *_ = O.decoder_layer_int8(xd, pd, w, kqc, ksc, vqc, vsc, **kw)
+    np.testing.assert_array_equal(yd, ydc)
