@@ -192,7 +192,7 @@ int llama_layer_decode_paged(llama_layer* layer, const void* x, void* y, const i
  * bytes per row.
  * k_codes, v_codes  [B, Hkv, max_pos, 128] int8, 16-byte aligned.
  * k_scale, v_scale  [B, Hkv, max_pos] float, 4-byte aligned.
- * bf16 layers, contiguous caches only. */
+ * bf16 layers; contiguous caches here, page pools below. */
 
 /* Quantize slots [0, n_slots) of B sequences of a contiguous bf16 cache
  * [B, Hkv, max_pos, 128] (e.g. after a prefill) into the int8 cache, at the
@@ -220,6 +220,24 @@ int llama_layer_prefill_int8(llama_layer* layer, const void* x, void* y, const i
  * layer). */
 int llama_layer_decode_int8(llama_layer* layer, const void* x, void* y, const int32_t* positions, int32_t B,
                             void* k_codes, void* v_codes, float* k_scale, float* v_scale, void* stream);
+
+/* The int8 cache in page pools: as llama_layer_prefill_paged /
+ * llama_layer_decode_paged (same block table, page size and capacity rules),
+ * with int8 code pools k_pages, v_pages [n_pages, Hkv, page_size, 128]
+ * (16-byte aligned) and fp32 scale pools k_scale_pages, v_scale_pages
+ * [n_pages, Hkv, page_size] (4-byte aligned): slot p of sequence b is code
+ * row p % page_size and scale p % page_size of page block_table[b][p /
+ * page_size].  The rows are quantized and read as for the contiguous int8
+ * cache; the output equals the contiguous int8 call's on the cache the pages
+ * stand for.  Errors: as the paged calls, plus those of the int8 calls. */
+int llama_layer_prefill_paged_int8(llama_layer* layer, const void* x, void* y, const int32_t* positions,
+                                   int32_t B, int32_t T, void* k_pages, void* v_pages, float* k_scale_pages,
+                                   float* v_scale_pages, const int32_t* block_table, int32_t blocks_per_seq,
+                                   int32_t page_size, int32_t n_pages, void* stream);
+int llama_layer_decode_paged_int8(llama_layer* layer, const void* x, void* y, const int32_t* positions,
+                                  int32_t B, void* k_pages, void* v_pages, float* k_scale_pages,
+                                  float* v_scale_pages, const int32_t* block_table, int32_t blocks_per_seq,
+                                  int32_t page_size, int32_t n_pages, void* stream);
 
 /* Allocation-free decode, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid

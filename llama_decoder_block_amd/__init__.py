@@ -35,6 +35,7 @@ LLAMA_BF16 = 1
 EXPORTED = ("llama_layer_create", "llama_layer_prefill", "llama_layer_decode", "llama_layer_decode_noalloc",
             "llama_layer_prefill_paged", "llama_layer_decode_paged",
             "llama_layer_kv_quantize", "llama_layer_prefill_int8", "llama_layer_decode_int8",
+            "llama_layer_prefill_paged_int8", "llama_layer_decode_paged_int8",
             "llama_layer_destroy", "llama_layer_strerror", "llama_layer_last_error",
             "llama_layer_profile", "llama_layer_profile_read", "llama_layer_step_name",
             "llama_layer_ceiling_mfma", "llama_layer_ceiling_read")
@@ -106,6 +107,10 @@ def _load():
     lib.llama_layer_prefill_int8.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp]
     lib.llama_layer_prefill_int8.restype = ctypes.c_int
     lib.llama_layer_decode_int8.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]
+    lib.llama_layer_prefill_paged_int8.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.llama_layer_prefill_paged_int8.restype = ctypes.c_int
+    lib.llama_layer_decode_paged_int8.argtypes = [vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.llama_layer_decode_paged_int8.restype = ctypes.c_int
     lib.llama_layer_decode_int8.restype = ctypes.c_int
     lib.llama_layer_destroy.argtypes = [vp]
     lib.llama_layer_destroy.restype = None
@@ -257,6 +262,30 @@ def llama_layer_prefill_int8(handle, x, y, positions, B, T, k_codes, v_codes, k_
                                         _ptr(v_scale, "v_scale", torch.float32), _stream_ptr(stream)))
 
 
+def llama_layer_prefill_paged_int8(handle, x, y, positions, B, T, k_pages, v_pages, k_scale_pages, v_scale_pages,
+                                   block_table, page_size, stream=None):
+    """Prefill over int8 page pools: codes [n_pages, Hkv, page_size, 128] int8,
+    scales [n_pages, Hkv, page_size] float32; block_table [B, blocks_per_seq]."""
+    import torch
+    _check(LIB.llama_layer_prefill_paged_int8(
+        handle, _ptr(x, "x"), _ptr(y, "y"), _ptr(positions, "positions", torch.int32), int(B), int(T),
+        _ptr(k_pages, "k_pages", torch.int8), _ptr(v_pages, "v_pages", torch.int8),
+        _ptr(k_scale_pages, "k_scale_pages", torch.float32), _ptr(v_scale_pages, "v_scale_pages", torch.float32),
+        _ptr(block_table, "block_table", torch.int32), int(block_table.shape[-1]), int(page_size),
+        int(k_pages.shape[0]), _stream_ptr(stream)))
+
+
+def llama_layer_decode_paged_int8(handle, x, y, positions, B, k_pages, v_pages, k_scale_pages, v_scale_pages,
+                                  block_table, page_size, stream=None):
+    import torch
+    _check(LIB.llama_layer_decode_paged_int8(
+        handle, _ptr(x, "x"), _ptr(y, "y"), _ptr(positions, "positions", torch.int32), int(B),
+        _ptr(k_pages, "k_pages", torch.int8), _ptr(v_pages, "v_pages", torch.int8),
+        _ptr(k_scale_pages, "k_scale_pages", torch.float32), _ptr(v_scale_pages, "v_scale_pages", torch.float32),
+        _ptr(block_table, "block_table", torch.int32), int(block_table.shape[-1]), int(page_size),
+        int(k_pages.shape[0]), _stream_ptr(stream)))
+
+
 def llama_layer_decode_int8(handle, x, y, positions, B, k_codes, v_codes, k_scale, v_scale, stream=None):
     import torch
     _check(LIB.llama_layer_decode_int8(handle, _ptr(x, "x"), _ptr(y, "y"),
@@ -362,6 +391,25 @@ class LlamaLayer:
         y = torch.empty_like(x) if y is None else y
         llama_layer_decode_paged(self.handle, x, y, positions, int(x.shape[0]), k_pages, v_pages, block_table,
                                  int(k_pages.shape[2]), stream)
+        return y
+
+    def prefill_paged_int8(self, x, positions, k_pages, v_pages, k_scale_pages, v_scale_pages, block_table, y=None,
+                           stream=None):
+        """As prefill_paged, over int8 pools (codes [n_pages, Hkv, page, 128]
+        int8, scales [n_pages, Hkv, page] float32), updated in place."""
+        import torch
+        B, T = int(x.shape[0]), int(x.shape[1])
+        y = torch.empty_like(x) if y is None else y
+        llama_layer_prefill_paged_int8(self.handle, x, y, positions, B, T, k_pages, v_pages, k_scale_pages,
+                                       v_scale_pages, block_table, int(k_pages.shape[2]), stream)
+        return y
+
+    def decode_paged_int8(self, x, positions, k_pages, v_pages, k_scale_pages, v_scale_pages, block_table, y=None,
+                          stream=None):
+        import torch
+        y = torch.empty_like(x) if y is None else y
+        llama_layer_decode_paged_int8(self.handle, x, y, positions, int(x.shape[0]), k_pages, v_pages,
+                                      k_scale_pages, v_scale_pages, block_table, int(k_pages.shape[2]), stream)
         return y
 
     def decode_noalloc(self, x, positions, k_cache, v_cache, y, stream=None):

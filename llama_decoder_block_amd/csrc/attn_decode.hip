@@ -55,8 +55,10 @@ __device__ __forceinline__ void softmax_merge(float& m1, float& l1, float* a1, f
 }
 
 // Q8: the int8 cache (codes [B, Hkv, max_pos, 128], one fp32 scale per row
-// in ksc / vsc): a row group's 16 lanes read its 128 codes with 8-byte loads
-// (a wavefront: 4 rows = 512 contiguous bytes per load) and the row's scale;
+// in ksc / vsc [B, Hkv, max_pos]; paged: code pools [n_pages, Hkv, page, 128]
+// and scale pools [n_pages, Hkv, page], a slot's scale at its code row's
+// index): a row group's 16 lanes read its 128 codes with 8-byte loads (a
+// wavefront: 4 rows = 512 contiguous bytes per load) and the row's scale;
 // the score is the code dot product times the key row's scale, and a weight
 // multiplies the value codes after taking the value row's scale.
 template <int R, bool PAGED, bool Q8>
@@ -65,7 +67,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     const void* __restrict__ v_cache, const int32_t* __restrict__ pos, float* __restrict__ part,
     bf16_t* __restrict__ o, int o_frag, int H, int Hkv, int max_pos, int span, KvPaging pg, int L, int n_split,
     float scale_log2, const float* __restrict__ ksc, const float* __restrict__ vsc) {
-  static_assert(!(Q8 && PAGED), "the int8 cache is contiguous");
   __shared__ float red_ml[4][R][2];
   __shared__ float red_o[4][R][DH];
 
@@ -108,6 +109,7 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   const char* K = static_cast<const char*>(k_cache) + (slice + static_cast<size_t>(j_begin) * DH + dc * 8) * ES;
   const char* V = static_cast<const char*>(v_cache) + (slice + static_cast<size_t>(j_begin) * DH + dc * 8) * ES;
   // int8: the scales of this (sequence, kv head)'s slots from j_begin on
+  // (paged: indexed by the same pool rows as the codes)
   const float* KS = Q8 ? ksc + slice / DH + j_begin : nullptr;
   const float* VS = Q8 ? vsc + slice / DH + j_begin : nullptr;
   // Paged: the 64 slots of one iteration, s0 .. s0 + 63 with s0 = j_begin +
@@ -373,11 +375,15 @@ hipError_t launch_attn_decode(const bf16_t* q, const void* k_cache, const void* 
   const float scale_log2 = static_cast<float>(1.4426950408889634 / sqrt(static_cast<double>(DH)));
   const bool paged = pg.block_table != nullptr;
   const bool q8 = k_scale != nullptr;
-  if (q8 && (paged || !v_scale)) return hipErrorInvalidValue;
+  if (q8 && !v_scale) return hipErrorInvalidValue;
   switch (R) {
 #define LLAMA_DEC_CASE(RR)                                                                                      \
   case RR:                                                                                                      \
-    if (paged)                                                                                                  \
+    if (paged && q8)                                                                                            \
+      hipLaunchKernelGGL((attn_decode_kernel<RR, true, true>), grid, dim3(256), 0, s, q, k_cache, v_cache, pos,  \
+                         part, o, o_frag, n_heads, n_kv_heads, max_pos, span, pg, L, n_split, scale_log2,       \
+                         k_scale, v_scale);                                                                     \
+    else if (paged)                                                                                             \
       hipLaunchKernelGGL((attn_decode_kernel<RR, true, false>), grid, dim3(256), 0, s, q, k_cache, v_cache, pos, \
                          part, o, o_frag, n_heads, n_kv_heads, max_pos, span, pg, L, n_split, scale_log2,       \
                          nullptr, nullptr);                                                                     \

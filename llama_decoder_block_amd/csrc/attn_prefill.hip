@@ -119,7 +119,8 @@ constexpr float kLazy = 8.f;
 // workgroups per CU; with more, two independent 4-wavefront workgroups per CU
 // overlap better)
 //
-// Q8: the int8 cache (contiguous).  A row stands for code * scale; the codes
+// Q8: the int8 cache (contiguous, or paged: code pools [n_pages, Hkv, page,
+// 128] with scale pools [n_pages, Hkv, page]).  A row stands for code * scale; the codes
 // are staged as bf16 (exact), so S^T = K_code Q^T is exact up to fp32
 // accumulation and each score is then multiplied by its row's K scale (times
 // the softmax scale); the weight of slot j enters the P.V product as
@@ -131,7 +132,6 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
     const void* __restrict__ v_cache, const int32_t* __restrict__ pos, bf16_t* __restrict__ o,
     int o_frag, int n_seq, int T, int H, int Hkv, int max_pos, int span, KvPaging pg, int bidir,
     float scale_log2, const float* __restrict__ k_scale, const float* __restrict__ v_scale) {
-  static_assert(!(Q8 && PAGED), "the int8 cache is contiguous");
   constexpr uint32_t ES = Q8 ? 1u : 2u;  // bytes per cached element
   __shared__ __attribute__((aligned(16))) bf16_t Ks[NGRP][2][BKV * KSTR];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[NGRP][2][DH * VSTR];
@@ -196,16 +196,30 @@ __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
   uint4 sreg = make_uint4(0, 0, 0, 0);
   auto gload = [&](int j0) {
     if constexpr (Q8) {
-      const uint32_t so = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(j0) * DH);
+      __amdgpu_buffer_rsrc_t krs = k_rs, vrs = v_rs, srs = sc_rs;
+      uint32_t row0 = static_cast<uint32_t>(j0);  // the tile's first row in the resources
+      if constexpr (PAGED) {  // the tile's page (uniform); its scales sit at its code rows' indices
+        const int bi = j0 / pg.page;
+        const int blk = __builtin_amdgcn_readfirstlane(pg.block_table[static_cast<size_t>(b) * pg.blocks_per_seq + bi]);
+        const bool ok = blk >= 0 && blk < pg.n_pages;
+        const size_t prow = ok ? (static_cast<size_t>(blk) * Hkv + g) * pg.page : 0;
+        const uint32_t nrow = ok ? static_cast<uint32_t>(pg.page) : 0u;
+        krs = make_rsrc(kbase + prow * DH, nrow * DH);
+        vrs = make_rsrc(vbase + prow * DH, nrow * DH);
+        srs = make_rsrc((wave == 0 ? k_scale : v_scale) + prow, nrow * 4u);
+        row0 = static_cast<uint32_t>(j0 % pg.page);
+      }
+      row0 = __builtin_amdgcn_readfirstlane(row0);
+      const uint32_t so = row0 * DH;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) kreg[i] = buf_load16(k_rs, static_cast<uint32_t>(kr8 * DH + kc8 * 16), so + 32 * i * DH);
+      for (int i = 0; i < 2; ++i) kreg[i] = buf_load16(krs, static_cast<uint32_t>(kr8 * DH + kc8 * 16), so + 32 * i * DH);
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        const uint2 a = buf_load8(v_rs, static_cast<uint32_t>((4 * vkg + 2 * i) * DH + vdg * 8), so);
-        const uint2 c = buf_load8(v_rs, static_cast<uint32_t>((4 * vkg + 2 * i + 1) * DH + vdg * 8), so);
+        const uint2 a = buf_load8(vrs, static_cast<uint32_t>((4 * vkg + 2 * i) * DH + vdg * 8), so);
+        const uint2 c = buf_load8(vrs, static_cast<uint32_t>((4 * vkg + 2 * i + 1) * DH + vdg * 8), so);
         vreg[i] = make_uint4(a.x, a.y, c.x, c.y);
       }
-      if (sc_lane) sreg = buf_load16(sc_rs, static_cast<uint32_t>(lane) * 16u, static_cast<uint32_t>(j0) * 4u);
+      if (sc_lane) sreg = buf_load16(srs, static_cast<uint32_t>(lane) * 16u, row0 * 4u);
     } else {
       __amdgpu_buffer_rsrc_t krs = k_rs, vrs = v_rs;
       uint32_t so = static_cast<uint32_t>(j0) * DH * 2u;
@@ -521,7 +535,7 @@ hipError_t launch_attn_prefill(const bf16_t* q, const void* k_cache, const void*
   if (pg.block_table && (pg.page % BKV || pg.page <= 0 || span > pg.blocks_per_seq * pg.page))
     return hipErrorInvalidValue;
   const bool q8 = k_scale != nullptr;
-  if (q8 && (pg.block_table || !v_scale)) return hipErrorInvalidValue;
+  if (q8 && !v_scale) return hipErrorInvalidValue;
   if (o_frag && B * T > kSkinnyMaxTokens) return hipErrorInvalidValue;
   const int n_wg = (T + BQ - 1) / BQ * n_heads * B;
   const dim3 grid(static_cast<unsigned>(n_wg));
@@ -533,7 +547,9 @@ hipError_t launch_attn_prefill(const bf16_t* q, const void* k_cache, const void*
   hipLaunchKernelGGL((attn_prefill_kernel<NG, PG, Q8>), grid, dim3(256 * NG), 0, s, q, k_cache, v_cache, pos, o, \
                      o_frag, B, T, n_heads, n_kv_heads, max_pos, span, pg, bidir, scale_log2, k_scale, v_scale)
   const bool two = n_wg <= 2 * n_cu;  // few workgroups: halve each query tile's chain
-  if (pg.block_table) {
+  if (pg.block_table && q8) {
+    if (two) LLAMA_ATTN_LAUNCH(2, true, true); else LLAMA_ATTN_LAUNCH(1, true, true);
+  } else if (pg.block_table) {
     if (two) LLAMA_ATTN_LAUNCH(2, true, false); else LLAMA_ATTN_LAUNCH(1, true, false);
   } else if (q8) {
     if (two) LLAMA_ATTN_LAUNCH(2, false, true); else LLAMA_ATTN_LAUNCH(1, false, true);

@@ -263,7 +263,7 @@ hipError_t launch_skinny_f32out(const bf16_t* A, const bf16_t* W, int M, int N, 
 // instead of row-major.
 // max_pos: the contiguous caches' slots per (sequence, kv head); span: the
 // slots a query may see (max_pos, or the paged capacity); pg: paging.
-// int8 cache (k_scale non-null, contiguous only): k_cache / v_cache hold
+// int8 cache (k_scale non-null; contiguous or paged): k_cache / v_cache hold
 // int8 codes and k_scale / v_scale one fp32 scale per row, as for decode.
 hipError_t launch_attn_prefill(const bf16_t* q, const void* k_cache, const void* v_cache,
                                const int32_t* pos, bf16_t* o, int o_frag, int B, int T, int n_heads,
@@ -278,9 +278,10 @@ hipError_t launch_attn_prefill(const bf16_t* q, const void* k_cache, const void*
 // decode_attn_max_splits bounds the splits of every span <= max_pos.
 int decode_attn_splits(int span, int B, int n_heads, int n_kv_heads);
 int decode_attn_max_splits(int max_pos, int B, int n_heads, int n_kv_heads);
-// int8 cache (k_scale non-null, contiguous only): k_cache / v_cache hold
-// int8 codes [B, Hkv, max_pos, 128] and k_scale / v_scale one fp32 scale per
-// row [B, Hkv, max_pos]; a row stands for code * scale.
+// int8 cache (k_scale non-null): k_cache / v_cache hold int8 codes [B, Hkv,
+// max_pos, 128] and k_scale / v_scale one fp32 scale per row [B, Hkv,
+// max_pos] (paged: pools [n_pages, Hkv, page, 128] and [n_pages, Hkv, page]);
+// a row stands for code * scale.
 hipError_t launch_attn_decode(const bf16_t* q, const void* k_cache, const void* v_cache,
                               const int32_t* pos, bf16_t* o, int o_frag, float* part, int n_split,
                               int B, int n_heads, int n_kv_heads, int max_pos, int span, const KvPaging& pg,
@@ -291,10 +292,11 @@ hipError_t launch_attn_decode(const bf16_t* q, const void* k_cache, const void* 
 // even; a row with amax below 2^-100: scale 0, codes 0).
 // Append: the staged bf16 rows of B sequences of T tokens (token m = b * T +
 // t, kv head g at staging row m * Hkv + g) into slot pos[m] of sequence b's
-// int8 cache (positions outside [0, span) write nothing).
+// int8 cache (positions outside [0, span) write nothing); with pg, into the
+// page pools (codes [n_pages, Hkv, page, 128], scales [n_pages, Hkv, page]).
 hipError_t launch_kv_int8_append(const bf16_t* k_stage, const bf16_t* v_stage, const int32_t* pos, int B,
-                                 int T, int n_kv_heads, int max_pos, int span, int8_t* k_codes, int8_t* v_codes,
-                                 float* k_scale, float* v_scale, hipStream_t s);
+                                 int T, int n_kv_heads, int max_pos, int span, const KvPaging& pg,
+                                 int8_t* k_codes, int8_t* v_codes, float* k_scale, float* v_scale, hipStream_t s);
 // Convert slots [0, n_slots) of a contiguous bf16 cache [B, Hkv, max_pos, 128]
 // into the int8 cache (same slot indices).
 hipError_t launch_kv_int8_convert(const bf16_t* k_cache, const bf16_t* v_cache, int B, int n_kv_heads,

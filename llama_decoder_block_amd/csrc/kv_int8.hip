@@ -70,11 +70,13 @@ __device__ __forceinline__ void quantize8(const uint4& u, int8_t* __restrict__ d
 }
 
 // rows r = (kv 0 / 1) * M * Hkv + m * Hkv + g (M = B * T tokens): the staged
-// row of token m = b * T + t, kv head g goes to slot pos[m] of sequence b;
+// row of token m = b * T + t, kv head g goes to slot pos[m] of sequence b
+// (paged: row (page Hkv + g) page_size + pos % page_size of the pools, the
+// page from the block table; a page id outside [0, n_pages) writes nothing);
 // 16 lanes per row
 __global__ __launch_bounds__(256) void kv_int8_append_kernel(
     const bf16_t* __restrict__ ks, const bf16_t* __restrict__ vs, const int32_t* __restrict__ pos, int M,
-    int T, int Hkv, int max_pos, int span, int8_t* __restrict__ kq, int8_t* __restrict__ vq,
+    int T, int Hkv, int max_pos, int span, KvPaging pg, int8_t* __restrict__ kq, int8_t* __restrict__ vq,
     float* __restrict__ ksc, float* __restrict__ vsc) {
   const int dc = threadIdx.x & 15;
   const int r = blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -85,7 +87,14 @@ __global__ __launch_bounds__(256) void kv_int8_append_kernel(
   const int m = mg / Hkv, g = mg - m * Hkv;
   const int p = pos[m];
   if (p < 0 || p >= span) return;
-  const size_t slot = (static_cast<size_t>(m / T) * Hkv + g) * max_pos + p;
+  size_t slot;
+  if (pg.block_table) {
+    const int blk = pg.block_table[static_cast<size_t>(m / T) * pg.blocks_per_seq + p / pg.page];
+    if (blk < 0 || blk >= pg.n_pages) return;
+    slot = (static_cast<size_t>(blk) * Hkv + g) * pg.page + p % pg.page;
+  } else {
+    slot = (static_cast<size_t>(m / T) * Hkv + g) * max_pos + p;
+  }
   const uint4 u = *reinterpret_cast<const uint4*>((is_v ? vs : ks) + static_cast<size_t>(mg) * DH + dc * 8);
   quantize8(u, (is_v ? vq : kq) + slot * DH + dc * 8, (is_v ? vsc : ksc) + slot, dc == 0);
 }
@@ -126,13 +135,14 @@ __global__ __launch_bounds__(256) void kv_int8_convert_kernel(
 }  // namespace
 
 hipError_t launch_kv_int8_append(const bf16_t* k_stage, const bf16_t* v_stage, const int32_t* pos, int B,
-                                 int T, int n_kv_heads, int max_pos, int span, int8_t* k_codes, int8_t* v_codes,
-                                 float* k_scale, float* v_scale, hipStream_t s) {
+                                 int T, int n_kv_heads, int max_pos, int span, const KvPaging& pg,
+                                 int8_t* k_codes, int8_t* v_codes, float* k_scale, float* v_scale, hipStream_t s) {
   if (B <= 0 || T <= 0) return hipSuccess;
+  if (pg.block_table && (pg.page <= 0 || span > pg.blocks_per_seq * pg.page)) return hipErrorInvalidValue;
   const long long rows = 2LL * B * T * n_kv_heads;
   if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
   hipLaunchKernelGGL(kv_int8_append_kernel, dim3(static_cast<unsigned>((rows + 15) / 16)), dim3(256), 0, s,
-                     k_stage, v_stage, pos, B * T, T, n_kv_heads, max_pos, span, k_codes, v_codes, k_scale,
+                     k_stage, v_stage, pos, B * T, T, n_kv_heads, max_pos, span, pg, k_codes, v_codes, k_scale,
                      v_scale);
   return hipGetLastError();
 }

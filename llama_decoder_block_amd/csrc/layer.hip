@@ -134,8 +134,9 @@ struct KvArgs {
   void* v;
   KvPaging pg;
   int span;
-  // int8 cache (contiguous): k and v hold int8 codes [B, Hkv, max_pos, 128]
-  // and these one fp32 scale per row [B, Hkv, max_pos]; null for bf16/fp32
+  // int8 cache: k and v hold int8 codes [B, Hkv, max_pos, 128] and these one
+  // fp32 scale per row [B, Hkv, max_pos] (paged: code pools [n_pages, Hkv,
+  // page, 128] and scale pools [n_pages, Hkv, page]); null for bf16/fp32
   float* k_scale = nullptr;
   float* v_scale = nullptr;
 };
@@ -556,7 +557,7 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
                        : launch_gemm_qkv(xn, wqkv, M, nqkv, d, ep, s),
                 "qkv projection");
   if (q8)
-    HIP_OR_RETURN(launch_kv_int8_append(k_stage, v_stage, pos, B, T, Hkv, c.max_pos, kv.span, static_cast<int8_t*>(kc),
+    HIP_OR_RETURN(launch_kv_int8_append(k_stage, v_stage, pos, B, T, Hkv, c.max_pos, kv.span, kv.pg, static_cast<int8_t*>(kc),
                                         static_cast<int8_t*>(vc), kv.k_scale, kv.v_scale, s),
                   "int8 cache append");
   HIP_OR_RETURN(mark(2), "event record");
@@ -571,7 +572,7 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
       const int ns = decode_attn_splits(kv.span, nb, H, Hkv);
       KvPaging pgc = kv.pg;
       if (paged) pgc.block_table += static_cast<size_t>(b0) * pgc.blocks_per_seq;
-      const size_t sc0 = q8 ? static_cast<size_t>(b0) * Hkv * c.max_pos : 0;  // scale rows before sequence b0
+      const size_t sc0 = q8 && !paged ? static_cast<size_t>(b0) * Hkv * c.max_pos : 0;  // scale rows before sequence b0
       HIP_OR_RETURN(launch_attn_decode(q + static_cast<size_t>(b0) * H * 128,
                                        static_cast<const char*>(kc) + b0 * kv_seq * kv_es,
                                        static_cast<const char*>(vc) + b0 * kv_seq * kv_es, pos + b0,
@@ -712,13 +713,18 @@ int llama_layer_kv_quantize(llama_layer* L, const void* k_cache, const void* v_c
   return e != hipSuccess ? hip_fail(e, "int8 cache conversion") : LLAMA_OK;
 }
 
-static int int8_call(llama_layer* L, const void* x, void* y, const int32_t* positions, int B, int T, void* k_codes,
-                     void* v_codes, float* k_scale, float* v_scale, void* stream) {
+// The int8 calls' own argument checks, made before anything reads the handle.
+static int int8_args(const llama_layer* L, const float* k_scale, const float* v_scale) {
   if (!L || !k_scale || !v_scale) return fail(LLAMA_ERR_NULL, "layer and scales must be non-null");
   if (L->cfg.dtype != LLAMA_BF16) return fail(LLAMA_ERR_UNSUPPORTED, "the int8 cache serves bf16 layers");
   if ((reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) & 3u)
     return fail(LLAMA_ERR_INVALID, "scales must be 4-byte aligned");
-  KvArgs kv = contiguous_kv(L, k_codes, v_codes);
+  return LLAMA_OK;
+}
+
+// kv: the call's codes (contiguous or paged); the scales are added here
+static int int8_call(llama_layer* L, const void* x, void* y, const int32_t* positions, int B, int T, KvArgs kv,
+                     float* k_scale, float* v_scale, void* stream) {
   kv.k_scale = k_scale;
   kv.v_scale = v_scale;
   return checked_call(L, x, y, positions, B, T, kv, stream);
@@ -727,13 +733,41 @@ static int int8_call(llama_layer* L, const void* x, void* y, const int32_t* posi
 int llama_layer_prefill_int8(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B, int32_t T,
                              void* k_codes, void* v_codes, float* k_scale, float* v_scale, void* stream) {
   g_last_error.clear();
-  return int8_call(L, x, y, positions, B, T, k_codes, v_codes, k_scale, v_scale, stream);
+  const int st = int8_args(L, k_scale, v_scale);
+  return st != LLAMA_OK ? st
+                        : int8_call(L, x, y, positions, B, T, contiguous_kv(L, k_codes, v_codes), k_scale, v_scale,
+                                    stream);
 }
 
 int llama_layer_decode_int8(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
                             void* k_codes, void* v_codes, float* k_scale, float* v_scale, void* stream) {
   g_last_error.clear();
-  return int8_call(L, x, y, positions, B, 1, k_codes, v_codes, k_scale, v_scale, stream);
+  const int st = int8_args(L, k_scale, v_scale);
+  return st != LLAMA_OK ? st
+                        : int8_call(L, x, y, positions, B, 1, contiguous_kv(L, k_codes, v_codes), k_scale, v_scale,
+                                    stream);
+}
+
+int llama_layer_prefill_paged_int8(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
+                                   int32_t T, void* k_pages, void* v_pages, float* k_scale_pages,
+                                   float* v_scale_pages, const int32_t* block_table, int32_t blocks_per_seq,
+                                   int32_t page_size, int32_t n_pages, void* stream) {
+  g_last_error.clear();
+  KvArgs kv{};
+  int st = int8_args(L, k_scale_pages, v_scale_pages);
+  if (st == LLAMA_OK) st = paged_kv(L, k_pages, v_pages, block_table, blocks_per_seq, page_size, n_pages, &kv);
+  return st != LLAMA_OK ? st : int8_call(L, x, y, positions, B, T, kv, k_scale_pages, v_scale_pages, stream);
+}
+
+int llama_layer_decode_paged_int8(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B,
+                                  void* k_pages, void* v_pages, float* k_scale_pages, float* v_scale_pages,
+                                  const int32_t* block_table, int32_t blocks_per_seq, int32_t page_size,
+                                  int32_t n_pages, void* stream) {
+  g_last_error.clear();
+  KvArgs kv{};
+  int st = int8_args(L, k_scale_pages, v_scale_pages);
+  if (st == LLAMA_OK) st = paged_kv(L, k_pages, v_pages, block_table, blocks_per_seq, page_size, n_pages, &kv);
+  return st != LLAMA_OK ? st : int8_call(L, x, y, positions, B, 1, kv, k_scale_pages, v_scale_pages, stream);
 }
 
 int llama_layer_prefill_paged(llama_layer* L, const void* x, void* y, const int32_t* positions, int32_t B, int32_t T,

@@ -145,6 +145,12 @@ def test_int8_cache_calls_reject_bad_arguments():
     assert lib.LIB.llama_layer_decode_int8(p, p, p, p, 1, p, p, None, p, None) == lib.LLAMA_ERR_NULL
     assert lib.LIB.llama_layer_prefill_int8(None, p, p, p, 1, 4, p, p, p, p, None) == lib.LLAMA_ERR_NULL
     assert lib.LIB.llama_layer_prefill_int8(p, p, p, p, 1, 4, p, p, p, None, None) == lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_prefill_paged_int8(None, p, p, p, 1, 4, p, p, p, p, p, 1, 64, 1, None) == \
+        lib.LLAMA_ERR_NULL
+    assert lib.LIB.llama_layer_decode_paged_int8(None, p, p, p, 1, p, p, p, p, p, 1, 64, 1, None) == lib.LLAMA_ERR_NULL
+    # a scale pointer is checked before the handle is read (p is no handle)
+    assert lib.LIB.llama_layer_decode_paged_int8(p, p, p, p, 1, p, p, None, p, p, 1, 64, 1, None) == \
+        lib.LLAMA_ERR_NULL
 
 
 def test_binding_refuses_host_tensors():

@@ -177,3 +177,75 @@ def test_paged_llama70b_prefill_and_64_decode_steps_are_bit_identical():
         assert _same(a, b) == 0, f"decode step {s}"
     assert _same(from_pages(kp, bt, 64), kc) == 0 and _same(from_pages(vp, bt, 64), vc) == 0
     print("  prefill and 64 decode steps bit-identical", flush=True)
+
+
+@pytest.mark.parametrize("shape", [
+    dict(d=512, H=4, Hkv=2, f=1408, B=2, T=300, prior=212, page=64),    # tiled GEMMs, 8-wave attention
+    dict(d=256, H=2, Hkv=2, f=384, B=3, T=5, prior=123, page=128),      # weight-streaming GEMMs, pages of 128
+    dict(d=1024, H=8, Hkv=2, f=1408, B=8, T=300, prior=212, page=64),   # 4-wave attention kernel, rounds
+])
+def test_paged_int8_prefill_then_decode(shape):
+    """int8 page pools (codes and per-row scales, shuffled table, spare pages):
+    a prefill over converted prior rows, then a decode step at ragged
+    positions, bit-identical to the contiguous int8 calls on the cache the
+    pages stand for, unmapped pages untouched, and y against the oracle's
+    paged int8 call at the 0.02 x RMS gate."""
+    page = shape["page"]
+    wl = synth.Workload("paged8", "bf16", shape["d"], shape["H"], shape["Hkv"], 128, shape["f"], shape["B"],
+                        shape["T"], prior=shape["prior"], decode_steps=1, seed=43)
+    cap = -(-wl.max_pos // page) * page
+    print(f"case {shape} capacity {cap}", flush=True)
+    B, T = wl.batch, wl.seq
+    w = synth.make_weights(wl, DEV, random_gains=True)
+    x = synth.make_x(wl, (B, T), device=DEV)
+    kc, vc = synth.make_cache(wl, DEV)
+    kc = torch.nn.functional.pad(kc, (0, 0, 0, cap - wl.max_pos)).contiguous()
+    vc = torch.nn.functional.pad(vc, (0, 0, 0, cap - wl.max_pos)).contiguous()
+    cfg = G.layer_config(lib, wl, B * T, max_pos=cap)
+    layer = lib.LlamaLayer(cfg, w)
+    kq = torch.empty(kc.shape, dtype=torch.int8, device=DEV)
+    vq = torch.empty_like(kq)
+    ks = torch.empty(kc.shape[:3], dtype=torch.float32, device=DEV)
+    vs = torch.empty_like(ks)
+    layer.kv_quantize(kc, vc, cap, kq, vq, ks, vs)
+    torch.cuda.synchronize()
+
+    def pages(t):  # scales [B, Hkv, cap] ride as rows of one element
+        pool, bt = to_pages(t if t.dim() == 4 else t.unsqueeze(-1), page, seed=1)
+        return (pool if t.dim() == 4 else pool.squeeze(-1).contiguous()), bt
+    (kp, bt), (vp, _), (ksp, _), (vsp, _) = pages(kq), pages(vq), pages(ks), pages(vs)
+    pools0 = [t.clone() for t in (kp, ksp, vp, vsp)]
+    pos = synth.prefill_positions(B, T, start=wl.prior, device=DEV)
+    y = layer.prefill_paged_int8(x, pos, kp, vp, ksp, vsp, bt)
+    c = [t.clone() for t in (kq, vq, ks, vs)]
+    yc = layer.prefill_int8(x, pos, *c)
+    torch.cuda.synchronize()
+
+    def gathered():
+        return (from_pages(kp, bt, page), from_pages(vp, bt, page), from_pages(ksp.unsqueeze(-1), bt, page)[..., 0],
+                from_pages(vsp.unsqueeze(-1), bt, page)[..., 0])
+    assert _same(y, yc) == 0
+    for a, b_ in zip(gathered(), c):
+        assert torch.equal(a, b_)
+    spare = sorted(set(range(kp.shape[0])) - set(bt.view(-1).tolist()))
+    for t, t0 in zip((kp, ksp, vp, vsp), pools0):
+        assert torch.equal(t[spare], t0[spare])  # unmapped pages untouched
+    w64 = G.oracle_weights(w)
+    btn = bt.cpu().numpy()
+    kw = dict(n_heads=wl.n_heads, n_kv_heads=wl.n_kv_heads, eps=wl.rms_eps, rope_base=wl.rope_base, bf16_points=True)
+    yo, *opools = O.decoder_layer_paged_int8(G.f64(x), G.f64(pos), w64, pools0[0].cpu().numpy(),
+                                             pools0[1].cpu().numpy(), pools0[2].cpu().numpy(),
+                                             pools0[3].cpu().numpy(), btn, page, cap, **kw)
+    G.assert_bf16_output(G.f64(y), yo, "paged int8 prefill y")
+    # one decode step at ragged positions
+    xd = synth.make_x(wl, (B,), tensor_id=synth.TID_DECODE_BASE, device=DEV)
+    pd = torch.tensor([wl.prior + T - (37 * b) % 50 for b in range(B)], dtype=torch.int32, device=DEV)
+    yd = layer.decode_paged_int8(xd, pd, kp, vp, ksp, vsp, bt)
+    ydc = layer.decode_int8(xd, pd, *c)
+    torch.cuda.synchronize()
+    assert _same(yd, ydc) == 0
+    for a, b_ in zip(gathered(), c):
+        assert torch.equal(a, b_)
+    ydo, *_ = O.decoder_layer_paged_int8(G.f64(xd)[:, None], G.f64(pd)[:, None], w64, *opools, btn, page, cap, **kw)
+    G.assert_bf16_output(G.f64(yd), ydo[:, 0], "paged int8 decode y")
+    layer.close()
