@@ -25,6 +25,8 @@ Also reported on the same line:
                 shuffled order);
   decode_int8   the same step over the int8 KV cache (codes and one fp32
                 scale per row; its own algorithmic bytes);
+  decode_paged_int8
+                the same over int8 page pools;
   prefill_int8  the headline prefill writing and reading the int8 KV cache
                 (the chunk's rows quantized into their slots; attention over
                 code * scale);
@@ -283,52 +285,71 @@ def bench_decode(lib, synth, steps, warmup):
             "step_roofline": step_rooflines(wl, B, 1, breakdown, pos=p)}
 
 
-def bench_decode_paged(lib, synth, steps, warmup, page=64):
+def bench_decode_paged(lib, synth, steps, warmup, page=64, int8=False):
     """The 7B decode workload over a paged cache: the same K/V scattered into
     pages of `page` slots in shuffled order (a block table per sequence),
     timed like the contiguous decode (median of event-timed steps, caches
-    evicted by a 512 MB read before each)."""
+    evicted by a 512 MB read before each).  int8: the cache converted by
+    llama_layer_kv_quantize first, then its codes and scales paged alike."""
     import torch
     wl = synth.WORKLOADS["llama7b_decode"]
-    B, p = wl.batch, wl.prior
+    B, p, Hkv = wl.batch, wl.prior, wl.n_kv_heads
     w = synth.make_weights(wl, "cuda")
     x = synth.make_x(wl, (B,), device="cuda")
     pos = torch.full((B,), p, dtype=torch.int32, device="cuda")
     kc, vc = synth.make_cache(wl, "cuda")
+    layer = lib.LlamaLayer(layer_config(lib, wl, B), w)
+    if int8:
+        kq = torch.empty(kc.shape, dtype=torch.int8, device="cuda")
+        vq = torch.empty_like(kq)
+        ks = torch.empty(kc.shape[:3], dtype=torch.float32, device="cuda")
+        vs = torch.empty_like(ks)
+        layer.kv_quantize(kc, vc, wl.max_pos, kq, vq, ks, vs)
+        caches = [kq, vq, ks.unsqueeze(-1), vs.unsqueeze(-1)]  # scales page like rows of one element
+    else:
+        caches = [kc, vc]
+    del kc, vc
     nb = wl.max_pos // page
     perm = torch.randperm(B * nb, generator=torch.Generator().manual_seed(11))
     bt = perm.view(B, nb).to(torch.int32).cuda()
-    kp = torch.empty(B * nb, wl.n_kv_heads, page, wl.head_dim, dtype=kc.dtype, device="cuda")
-    vp = torch.empty_like(kp)
     idx = bt.view(-1).long()
-    kp[idx] = kc.view(B, wl.n_kv_heads, nb, page, wl.head_dim).transpose(1, 2).reshape(B * nb, wl.n_kv_heads, page,
-                                                                                         wl.head_dim)
-    vp[idx] = vc.view(B, wl.n_kv_heads, nb, page, wl.head_dim).transpose(1, 2).reshape(B * nb, wl.n_kv_heads, page,
-                                                                                         wl.head_dim)
-    del kc, vc
+    pools = []
+    for c in caches:
+        e = c.shape[-1]
+        pool = torch.empty(B * nb, Hkv, page, e, dtype=c.dtype, device="cuda")
+        pool[idx] = c.reshape(B, Hkv, nb, page, e).transpose(1, 2).reshape(B * nb, Hkv, page, e)
+        pools.append(pool if e > 1 else pool.squeeze(-1).contiguous())
+    del caches
+    torch.cuda.synchronize()
     y = torch.empty_like(x)
-    layer = lib.LlamaLayer(layer_config(lib, wl, B), w)
+    if int8:
+        def call():
+            layer.decode_paged_int8(x, pos, *pools, bt, y=y)
+    else:
+        def call():
+            layer.decode_paged(x, pos, *pools, bt, y=y)
     flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    ramp_clocks(lambda: layer.decode_paged(x, pos, kp, vp, bt, y=y))
+    ramp_clocks(call)
     for _ in range(warmup):
-        layer.decode_paged(x, pos, kp, vp, bt, y=y)
+        call()
     times = []
     for _ in range(steps):
         flush.sum()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        layer.decode_paged(x, pos, kp, vp, bt, y=y)
+        call()  # a repeated decode at one position is idempotent
         e1.record(stream)
         times.append((e0, e1))
     torch.cuda.synchronize()
     ms = sorted(a.elapsed_time(b) for a, b in times)
     med = ms[len(ms) // 2]
-    nbytes = decode_bytes(wl, B, p)
+    nbytes = decode_int8_bytes(wl, B, p) if int8 else decode_bytes(wl, B, p)
     layer.close()
-    return {"workload": "llama7b_decode, paged KV cache", "page_slots": page, "pages": B * nb, "batch": B,
-            "position": p, "ms_per_step_median": med, "bytes_per_step": nbytes, "GBps": nbytes / med / 1e6,
-            "hbm_frac": nbytes / med / 1e6 / PEAK_HBM_GBPS, "tokens_per_s": B / med * 1e3}
+    return {"workload": "llama7b_decode, paged " + ("int8 KV cache" if int8 else "KV cache"), "page_slots": page,
+            "pages": B * nb, "batch": B, "position": p, "ms_per_step_median": med, "bytes_per_step": nbytes,
+            "GBps": nbytes / med / 1e6, "hbm_frac": nbytes / med / 1e6 / PEAK_HBM_GBPS,
+            "tokens_per_s": B / med * 1e3}
 
 
 def decode_int8_bytes(wl, B, pos):
@@ -716,6 +737,7 @@ def main():
         if not args.headline_only:
             out["decode_paged"] = bench_decode_paged(lib, synth, args.decode_steps, 3)
             out["decode_int8"] = bench_decode_int8(lib, synth, args.decode_steps, 3)
+            out["decode_paged_int8"] = bench_decode_paged(lib, synth, args.decode_steps, 3, int8=True)
     # fractions of what this GPU sustains (the roofline above uses the published peaks)
     ceil = measure_ceilings(lib)
     ceil["prefill_layer_frac_of_mfma_loop"] = out["layer"]["tflops"] / ceil["mfma_loop_tflops"]
