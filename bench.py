@@ -32,7 +32,9 @@ Also reported on the same line:
                 code * scale);
   other_configs the 7B shape with bidirectional attention, the 13B-shape
                 prefill, the 70B-shape GQA prefill and its 64 decode steps,
-                and greedy generation with a 32-layer 7B-shape stack;
+                the same two at one GPU's share of the 70B layer under 8-way
+                tensor parallelism, and greedy generation with a 32-layer
+                7B-shape stack;
   cpu_baseline  the CPU oracle on a bounded prefix of the same prefill
                 workload, on this host's cores.
 
@@ -447,12 +449,16 @@ def bench_other_configs(lib, synth, steps, warmup):
     shape with bidirectional attention (the encoder-style variant), 13B-shape
     prefill (2 x 4096 tokens), 70B-shape GQA prefill (4096 tokens) and the 64
     single-token decode steps that follow it (positions 4096..4159; caches
-    evicted by a 512 MB read before each step, as for the 7B decode)."""
+    evicted by a 512 MB read before each step, as for the 7B decode), and the
+    same two at one GPU's share of the 70B layer under 8-way tensor
+    parallelism (the all-reduces after o_proj and down are not part of it)."""
     import torch
     res = {}
     flush = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
-    for name in ("llama7b_prefill_bidirectional", "llama13b_prefill", "llama70b_gqa"):
+    keys = {"llama70b_gqa": ("llama70b_gqa_prefill", "llama70b_gqa_decode"),
+            "llama70b_tp8_shard": ("llama70b_tp8_shard_prefill", "llama70b_tp8_shard_decode")}
+    for name in ("llama7b_prefill_bidirectional", "llama13b_prefill", "llama70b_gqa", "llama70b_tp8_shard"):
         bidir = name.endswith("_bidirectional")
         wl = synth.WORKLOADS[name.replace("_bidirectional", "")]
         B, T = wl.batch, wl.seq
@@ -471,9 +477,10 @@ def bench_other_configs(lib, synth, steps, warmup):
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) / steps * 1e3
         tfl = prefill_flops(wl, T, B, bidir) / (ms * 1e-3) / 1e12
-        res[name.replace("_gqa", "_gqa_prefill")] = {
+        res[keys.get(name, (name,))[0]] = {
             "batch": B, "seq_len": T, "ms_per_step": ms, "tokens_per_s": B * T / ms * 1e3,
-            "tflops": tfl, "mfma_frac": tfl / PEAK_BF16_TFLOPS}
+            "tflops": tfl, "mfma_frac": tfl / PEAK_BF16_TFLOPS,
+            "step_ms_by_kernel": per_step_breakdown(lib, layer, lambda: layer.prefill(x, pos, kc, vc, y=y), 3)}
         log(f"{name}: prefill {ms:.3f} ms/step")
         layer.close()
         if wl.decode_steps:
@@ -496,7 +503,7 @@ def bench_other_configs(lib, synth, steps, warmup):
             ms_all = [a.elapsed_time(b) for a, b in times]
             tot = sum(ms_all)
             med = sorted(ms_all)[len(ms_all) // 2]
-            res[name.replace("_gqa", "_gqa_decode")] = {
+            res[keys[name][1]] = {
                 "batch": B, "positions": [T, T + wl.decode_steps - 1], "steps": wl.decode_steps,
                 "ms_per_step_median": med, "GBps": nbytes / tot / 1e6,
                 "hbm_frac": nbytes / tot / 1e6 / PEAK_HBM_GBPS}

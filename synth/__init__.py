@@ -182,6 +182,10 @@ WORKLOADS = {
                                prior=4095, decode_steps=1, seed=20261206),
     "llama70b_gqa": Workload("llama70b_gqa", "bf16", 8192, 64, 8, 128, 28672, 1, 4096,
                              decode_steps=64, seed=20261207),
+    # one GPU's share of llama70b_gqa under 8-way tensor parallelism (heads
+    # and the MLP's intermediate dimension split 8 ways; d unchanged)
+    "llama70b_tp8_shard": Workload("llama70b_tp8_shard", "bf16", 8192, 8, 1, 128, 3584, 1, 4096,
+                                   decode_steps=64, seed=20261208),
 }
 
 

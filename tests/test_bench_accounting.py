@@ -7,7 +7,7 @@ import synth
 
 
 def test_step_flops_add_up_to_the_layer():
-    for name in ("llama7b_prefill", "llama13b_prefill", "llama70b_gqa"):
+    for name in ("llama7b_prefill", "llama13b_prefill", "llama70b_gqa", "llama70b_tp8_shard"):
         wl = synth.WORKLOADS[name]
         B, T = wl.batch, wl.seq
         one_ms = {k: 1.0 for k in ("rmsnorm_attn", "qkv_rope_cache", "attention", "o_proj_residual",

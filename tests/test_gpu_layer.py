@@ -229,6 +229,40 @@ def test_bf16_decode_steps(B, H, Hkv):
         G.assert_bf16_cache(G.f64(vc)[:, :, p], ex["v"][:, :, 0], vo[:, :, p], f"decode step {s} V")
 
 
+@pytest.mark.parametrize("shape", [
+    # one GPU's share of the 70B layer under 8-way tensor parallelism: 8 query
+    # heads and their one kv head (q width 1024 != d = 8192), f / 8 = 3584
+    dict(d=8192, H=8, Hkv=1, f=3584, B=1, T=300),
+    # the 13B layer's 4-way share: 10 heads, f / 4 = 3456
+    dict(d=5120, H=10, Hkv=10, f=3456, B=2, T=200),
+])
+def test_tensor_parallel_shard_shapes(shape):
+    """A layer whose projections are one GPU's tensor-parallel share (H dh
+    below d): prefill (tiled GEMMs, ragged tiles), then 2 decode steps
+    (weight-streaming GEMMs), each against the oracle at the same shape."""
+    wl = _wl(d=shape["d"], H=shape["H"], Hkv=shape["Hkv"], f=shape["f"], B=shape["B"], T=shape["T"], steps=2,
+             seed=19)
+    print(f"case {shape}", flush=True)
+    B = wl.batch
+    w, x, kc, vc, pos, layer = _setup(wl, random_gains=True)
+    kc0, vc0 = kc.clone(), vc.clone()
+    y = layer.prefill(x, pos, kc, vc)
+    _check_prefill(wl, w, x, kc0, vc0, pos, y, kc, vc)
+    w64 = G.oracle_weights(w)
+    _, ko, vo = G.oracle_prefill(wl, w64, x, pos, kc0, vc0)
+    from oracle import llama_oracle as O
+    for s in range(wl.decode_steps):
+        p = wl.seq + s
+        xs = synth.make_x(wl, (B,), tensor_id=synth.TID_DECODE_BASE + s, device=DEV)
+        ps = torch.full((B,), p, dtype=torch.int32, device=DEV)
+        ys = layer.decode(xs, ps, kc, vc)
+        torch.cuda.synchronize()
+        yo, ko, vo = O.decoder_layer_decode(G.f64(xs), np.full(B, p), w64, ko, vo, n_heads=wl.n_heads,
+                                            n_kv_heads=wl.n_kv_heads, bf16_points=True)
+        G.assert_bf16_output(G.f64(ys), yo, f"decode step {s} y")
+    layer.close()
+
+
 @pytest.mark.parametrize("dtype,H,Hkv", [("bf16", 4, 2), ("bf16", 4, 4), ("f32", 4, 2),
                                           # 3 .. 8 query heads per kv head: every width of
                                           # the decode attention kernel over several of its
