@@ -120,12 +120,13 @@ constexpr float kLazy = 8.f;
 // overlap better)
 //
 // Q8: the int8 cache (contiguous, or paged: code pools [n_pages, Hkv, page,
-// 128] with scale pools [n_pages, Hkv, page]).  A row stands for code * scale; the codes
-// are staged as bf16 (exact), so S^T = K_code Q^T is exact up to fp32
-// accumulation and each score is then multiplied by its row's K scale (times
-// the softmax scale); the weight of slot j enters the P.V product as
-// p_j * s_v(j) (bf16 hi + lo, fp32's range) against the V codes, while the row
-// sum adds p_j.  The tile's 64 K and 64 V scales are staged in LDS.
+// 128] with scale pools [n_pages, Hkv, page]).  A row stands for code *
+// scale; the codes are staged as bf16 (exact), so S^T = K_code Q^T is exact
+// up to fp32 accumulation and each score is then multiplied by its row's K
+// scale (times the softmax scale); the weight of slot j enters the P.V
+// product as p_j * s_v(j) (bf16 hi + lo, fp32's range) against the V codes,
+// while the row sum adds p_j.  The tile's 64 K and 64 V scales are staged in
+// LDS.
 template <int NGRP, bool PAGED, bool Q8>
 __global__ __launch_bounds__(256 * NGRP, 3 - NGRP) void attn_prefill_kernel(
     const bf16_t* __restrict__ q, const void* __restrict__ k_cache,
