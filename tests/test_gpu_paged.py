@@ -249,3 +249,45 @@ def test_paged_int8_prefill_then_decode(shape):
     ydo, *_ = O.decoder_layer_paged_int8(G.f64(xd)[:, None], G.f64(pd)[:, None], w64, *opools, btn, page, cap, **kw)
     G.assert_bf16_output(G.f64(yd), ydo[:, 0], "paged int8 decode y")
     layer.close()
+
+
+def test_paged_decode_of_more_sequences_than_one_attention_chunk():
+    """80 sequences (the decode attention runs in chunks of 64, the block
+    table advancing with them; the GEMMs take the tiled path) at ragged
+    positions over shuffled pages: the bf16 and the int8 paged decode
+    bit-identical to their contiguous calls, appended slots included."""
+    B, page = 80, 64
+    wl = synth.Workload("paged80", "bf16", 512, 4, 2, 128, 1408, B, 0, prior=255, decode_steps=1, seed=47)
+    cap = 256
+    print(f"case B={B} capacity {cap}", flush=True)
+    w = synth.make_weights(wl, DEV, random_gains=True)
+    x = synth.make_x(wl, (B,), device=DEV)
+    kc, vc = synth.make_cache(wl, DEV)
+    pos = torch.tensor([(97 * b) % 256 for b in range(B)], dtype=torch.int32, device=DEV)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, B, max_pos=cap), w)
+    kp, bt = to_pages(kc, page, seed=5)
+    vp, _ = to_pages(vc, page, seed=5)
+    yp = layer.decode_paged(x, pos, kp, vp, bt)
+    kcc, vcc = kc.clone(), vc.clone()
+    yc = layer.decode(x, pos, kcc, vcc)
+    torch.cuda.synchronize()
+    print(f"  bf16 y: {_same(yp, yc)} elements differ", flush=True)
+    assert _same(yp, yc) == 0
+    assert _same(from_pages(kp, bt, page), kcc) == 0 and _same(from_pages(vp, bt, page), vcc) == 0
+    kq = torch.empty(kc.shape, dtype=torch.int8, device=DEV)
+    vq = torch.empty_like(kq)
+    ks = torch.empty(kc.shape[:3], dtype=torch.float32, device=DEV)
+    vs = torch.empty_like(ks)
+    layer.kv_quantize(kc, vc, cap, kq, vq, ks, vs)
+    pools = [to_pages(t if t.dim() == 4 else t.unsqueeze(-1), page, seed=5)[0] for t in (kq, vq, ks, vs)]
+    pools[2], pools[3] = pools[2].squeeze(-1).contiguous(), pools[3].squeeze(-1).contiguous()
+    yq = layer.decode_paged_int8(x, pos, *pools, bt)
+    c = [t.clone() for t in (kq, vq, ks, vs)]
+    yqc = layer.decode_int8(x, pos, *c)
+    torch.cuda.synchronize()
+    print(f"  int8 y: {_same(yq, yqc)} elements differ", flush=True)
+    assert _same(yq, yqc) == 0
+    assert torch.equal(from_pages(pools[0], bt, page), c[0]) and torch.equal(from_pages(pools[1], bt, page), c[1])
+    assert torch.equal(from_pages(pools[2].unsqueeze(-1), bt, page)[..., 0], c[2])
+    assert torch.equal(from_pages(pools[3].unsqueeze(-1), bt, page)[..., 0], c[3])
+    layer.close()
