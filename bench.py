@@ -33,8 +33,8 @@ Also reported on the same line:
   other_configs the 7B shape with bidirectional attention, the 13B-shape
                 prefill, the 70B-shape GQA prefill and its 64 decode steps,
                 the same two at one GPU's share of the 70B layer under 8-way
-                tensor parallelism, and greedy generation with a 32-layer
-                7B-shape stack;
+                tensor parallelism, the 7B shape over chunks of 128 and 512
+                tokens, and greedy generation with a 32-layer 7B-shape stack;
   cpu_baseline  the CPU oracle on a bounded prefix of the same prefill
                 workload, on this host's cores.
 
@@ -512,6 +512,36 @@ def bench_other_configs(lib, synth, steps, warmup):
     return res
 
 
+def bench_prefill_chunks(lib, synth, steps, warmup, sizes=(128, 512)):
+    """The 7B-shape layer over short chunks of tokens (one sequence at
+    positions 0..T-1), where the tiled GEMMs have fewer tiles than CUs and
+    split K: wall time of back-to-back calls."""
+    import dataclasses
+    import torch
+    res = {}
+    for T in sizes:
+        wl = dataclasses.replace(synth.WORKLOADS["llama7b_prefill"], seq=T)
+        w = synth.make_weights(wl, "cuda")
+        x = synth.make_x(wl, (1, T), device="cuda")
+        pos = synth.prefill_positions(1, T, device="cuda")
+        kc, vc = synth.make_cache(wl, "cuda")
+        y = torch.empty_like(x)
+        layer = lib.LlamaLayer(layer_config(lib, wl, T), w)
+        for _ in range(warmup):
+            layer.prefill(x, pos, kc, vc, y=y)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            layer.prefill(x, pos, kc, vc, y=y)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / steps * 1e3
+        tfl = prefill_flops(wl, T, 1) / (ms * 1e-3) / 1e12
+        res[f"llama7b_prefill_{T}"] = {"batch": 1, "seq_len": T, "ms_per_step": ms, "tokens_per_s": T / ms * 1e3,
+                                       "tflops": tfl, "mfma_frac": tfl / PEAK_BF16_TFLOPS}
+        layer.close()
+    return res
+
+
 def bench_generate(lib, synth, n_layers=32, vocab=32000, B=32, T=128, max_new=64):
     """Greedy generation with a 7B-shape stack (32 layers, LLaMA's 32000-token
     vocabulary, random weights): B prompts of T tokens, then max_new tokens
@@ -754,6 +784,7 @@ def main():
     out["ceilings"] = ceil
     if not args.headline_only and not args.no_other_configs:
         out["other_configs"] = bench_other_configs(lib, synth, max(3, args.steps // 4), 2)
+        out["other_configs"].update(bench_prefill_chunks(lib, synth, 20, 5))
         out["other_configs"]["llama7b_generate"] = bench_generate(lib, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, host, args.cpu_budget_s)

@@ -84,6 +84,17 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t v
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
 
+// 16-byte stores and loads coherent across the XCDs' L2s: the sc1 cache
+// policy bit (cache-policy operand 16 on gfx950) is what an agent-scope
+// relaxed atomic store or load carries, in vector form.  Used to hand partial
+// tiles between workgroups (ordered by a counter, not by these accesses).
+__device__ __forceinline__ void buf_store16_sc1(__amdgpu_buffer_rsrc_t r, const f32x4& v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, voff, 0, 16);
+}
+__device__ __forceinline__ f32x4 buf_load16_sc1(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 16));
+}
+
 __device__ __forceinline__ uint2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
@@ -205,18 +216,29 @@ struct QkvEpilogue {
   int stage;
 };
 
+// Split K of the tiled GEMMs: when their tiles fill at most half the CUs,
+// each tile's k range is split (up to 4 ways) over this scratch: partial tiles
+// (gemm_split_part_floats() floats) and one counter per tile (device_cu_count()
+// counters, zero before the first launch; every launch leaves them zero).
+// Null pointers: no split.
+struct GemmSplit {
+  float* part = nullptr;
+  unsigned* cnt = nullptr;
+};
+size_t gemm_split_part_floats();  // one 128 x 512 fp32 tile per CU
+
 hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K,
-                           const QkvEpilogue& ep, hipStream_t s);
+                           const QkvEpilogue& ep, const GemmSplit& gs, hipStream_t s);
 // out_f32[M,N] = A.W^T + resid_bf16[M,N]   (A, W fp16)
 hipError_t launch_gemm_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
-                                    const bf16_t* resid, float* out, hipStream_t s);
+                                    const bf16_t* resid, float* out, const GemmSplit& gs, hipStream_t s);
 // out_bf16[M,N] = bf16(A.W^T + resid_f32[M,N])   (A, W fp16)
 hipError_t launch_gemm_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K,
-                                     const float* resid, bf16_t* out, hipStream_t s);
+                                     const float* resid, bf16_t* out, const GemmSplit& gs, hipStream_t s);
 // W is the gate/up matrix interleaved in blocks of 64 rows [gate 64 | up 64]
 // (N = 2f); out[M, f] = fp16(SiLU(gate) * up)
 hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, int K,
-                              bf16_t* out, hipStream_t s);
+                              bf16_t* out, const GemmSplit& gs, hipStream_t s);
 
 // compute units of the current device (256 if the query fails)
 int device_cu_count();

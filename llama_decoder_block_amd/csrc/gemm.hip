@@ -47,10 +47,20 @@
 //   * Tiles are numbered so that each XCD (blocks are dealt round-robin over 8
 //     XCDs) gets a contiguous, M-grouped range, which keeps the A and W panels
 //     it shares inside its own L2.
+//   * Split K: when the tiles fill at most half the CUs (few tokens: chunked
+//     prefill, batched decode of more than 64 sequences), each tile's slabs
+//     are cut into ks <= 4 ranges of whole ring cycles, one workgroup each
+//     (more would leave the last arriver too many partials to read alone).  Every
+//     split writes its fp32 partial tile with coherent 16-byte stores, waits
+//     for them, and counts itself in on the tile's counter; the last arriver
+//     adds the ks partials in split order (the result does not depend on
+//     arrival order), re-arms the counter and runs the epilogue.
 // Requires K % 128 == 0 (an even number of slabs) and N % BN == 0 except for
 // the QKV and resid epilogues, which bounds-check columns (weight fragments
 // past N read as zeros).
 #include "common.h"
+
+#include <type_traits>
 
 namespace llama {
 namespace {
@@ -61,6 +71,11 @@ struct EpiArgs {
   QkvEpilogue qkv;
   const void* resid;
   void* out;
+  // split K (ks > 1): partial tiles [tiles][ks][BM * BN] fp32 and one counter
+  // per tile (zero between launches)
+  float* part;
+  unsigned* cnt;
+  int ks;
 };
 
 constexpr int BK = 64;
@@ -70,10 +85,9 @@ constexpr int kGroupM = 8;
 // tiles leave the second round half empty)
 constexpr int kQkvBN = 192;
 
-__device__ __forceinline__ void tile_coords(int M, int N, int BM, int BN, int& m0, int& n0) {
+__device__ __forceinline__ void tile_coords(int M, int N, int BM, int BN, int bid, int& m0, int& n0) {
   const int nt_m = (M + BM - 1) / BM, nt_n = (N + BN - 1) / BN;
   const int nt = nt_m * nt_n;
-  int bid = blockIdx.x;
   if ((nt & 7) == 0) bid = (bid & 7) * (nt >> 3) + (bid >> 3);  // contiguous range per XCD
   const int group = kGroupM * nt_n;
   const int first_m = (bid / group) * kGroupM;
@@ -86,10 +100,12 @@ __device__ __forceinline__ void tile_coords(int M, int N, int BM, int BN, int& m
 
 __device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
 
+
 // the residual GEMMs (o_proj, down) multiply fp16 operands, QKV and gate/up bf16
 template <int EPI> constexpr bool kF16Operands = EPI == EPI_RESID32 || EPI == EPI_RESID16;
 
-template <int BM, int BN, int EPI, int RING>
+// SPLIT: the split-K form (ep.ks > 1 workgroups per tile)
+template <int BM, int BN, int EPI, int RING, bool SPLIT>
 __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A, const bf16_t* __restrict__ Wp,
                                                     int M, int N, int K, EpiArgs ep) {
   constexpr bool F16 = kF16Operands<EPI>;
@@ -105,9 +121,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   constexpr int LDS_STAGE = STAGE > 2 * EPI_WAVE ? STAGE : 2 * EPI_WAVE;
   __shared__ __attribute__((aligned(1024))) unsigned char As0[LDS_STAGE];
   __shared__ __attribute__((aligned(1024))) unsigned char As1[LDS_STAGE];
+  __shared__ unsigned s_last;
   auto stage_base = [&](int st) -> unsigned char* { return st == 0 ? As0 : As1; };
+  const int ks = SPLIT ? ep.ks : 1;
+  const int tile = static_cast<int>(blockIdx.x) / ks, split = static_cast<int>(blockIdx.x) - tile * ks;
   int m0, n0;
-  tile_coords(M, N, BM, BN, m0, n0);
+  tile_coords(M, N, BM, BN, tile, m0, n0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = WM == 2 ? wave >> 1 : 0, wn = WM == 2 ? wave & 1 : wave;
   const int KB = K >> 4;
@@ -160,25 +179,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
   bf16x8 fa[2][FM];
 
-  const int nk = K / BK;  // a multiple of RING
-  // prologue: A slab 0 -> stage 0, A slabs 1 .. AD -> registers; B slabs
-  // 0 .. RING-1 -> ring
+  // this split's slabs [s0, s1): whole ring cycles (K / BK is a multiple of RING)
+  const int cycles = K / BK / RING;
+  const int s0 = SPLIT ? split * cycles / ks * RING : 0;
+  const int s1 = SPLIT ? (split + 1) * cycles / ks * RING : K / BK;
+  // prologue: A slab s0 -> stage 0, A slabs s0+1 .. s0+AD -> registers; B
+  // slabs s0 .. s0+RING-1 -> ring
 #pragma unroll
-  for (int i = 0; i < NA; ++i) a_gload(0, i, 0);
+  for (int i = 0; i < NA; ++i) a_gload(0, i, s0);
 #pragma unroll
   for (int i = 0; i < NA; ++i) a_lstore(0, i, 0);
 #pragma unroll
-  for (int i = 0; i < NA; ++i) a_gload(AD == 2 ? 1 : 0, i, 1);
+  for (int i = 0; i < NA; ++i) a_gload(AD == 2 ? 1 : 0, i, s0 + 1);
   if constexpr (AD == 2) {
 #pragma unroll
-    for (int i = 0; i < NA; ++i) a_gload(0, i, 2);
+    for (int i = 0; i < NA; ++i) a_gload(0, i, s0 + 2);
   }
 #pragma unroll
   for (int b = 0; b < RING; ++b)
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) b_load(b, b, kk, j);
+      for (int j = 0; j < FN; ++j) b_load(b, s0 + b, kk, j);
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < FM; ++i) fa[0][i] = frag_a(0, 0, i);
@@ -219,7 +241,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
       }
     }
   };
-  for (int kt = 0; kt < nk; kt += RING) {
+  for (int kt = s0; kt < s1; kt += RING) {
     slab(0, 0, kt);
     slab(1, 1, kt + 1);
     if constexpr (RING == 4) {
@@ -228,6 +250,35 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
+
+  // split K: partial tile of split t at part + (tile ks + t) BM BN; chunk q =
+  // (i FN + j) 4 + r4 of thread tid (4 floats) at ((q * 256) + tid) * 16
+  // bytes, so each store and load of a wavefront is 1 KB contiguous
+  constexpr uint32_t TILE_BYTES = BM * BN * 4u;
+  const __amdgpu_buffer_rsrc_t all =
+      make_rsrc(SPLIT ? ep.part + static_cast<size_t>(tile) * ks * (BM * BN) : nullptr,
+                SPLIT ? TILE_BYTES * static_cast<uint32_t>(ks) : 0u);
+  if constexpr (SPLIT) {  // hand the partial tile over; only the last split goes on
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 v{acc[i][j][4 * r4], acc[i][j][4 * r4 + 1], acc[i][j][4 * r4 + 2], acc[i][j][4 * r4 + 3]};
+          buf_store16_sc1(all, v, static_cast<uint32_t>((((i * FN + j) * 4 + r4) * 256 + tid) * 16) +
+                                      static_cast<uint32_t>(split) * TILE_BYTES);
+        }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the partial has reached the coherent level
+    __syncthreads();
+    if (tid == 0) {
+      s_last = __hip_atomic_fetch_add(ep.cnt + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               static_cast<unsigned>(ks - 1);
+      if (s_last) __hip_atomic_store(ep.cnt + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // re-arm
+    }
+    __syncthreads();
+    if (!s_last) return;
+  }
 
   // ---------------------------------------------------------------- epilogue
   // Each wave moves its tile through LDS one 32-row block at a time, so the
@@ -306,10 +357,40 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
       if (i + 1 < FM) resid_fetch(i + 1, (i + 1) & 1);
     }
     // registers -> LDS: acc[i][j][r] is row 8 (r/4) + hr + r%4, column 32 j + lc
+    if constexpr (SPLIT) {
+      // the last split: the same values as the sum of the ks partials, added
+      // in split order (its own partial read back like the others), one
+      // 32 x 32 block (4 chunks x ks loads) at a time
+      auto put = [&](auto ks_tag) {
+        constexpr int KS = decltype(ks_tag)::value;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
+          f32x4 v[4][KS];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ebuf[(8 * (r >> 2) + hr + (r & 3)) * TNP + 32 * j + lc] = acc[i][j][r];
+          for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+            for (int t = 0; t < KS; ++t)
+              v[r4][t] = buf_load16_sc1(all, static_cast<uint32_t>((((i * FN + j) * 4 + r4) * 256 + tid) * 16) +
+                                                 static_cast<uint32_t>(t) * TILE_BYTES);
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            f32x4 sum = v[r4][0];
+#pragma unroll
+            for (int t = 1; t < KS; ++t) sum += v[r4][t];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ebuf[(8 * r4 + hr + e) * TNP + 32 * j + lc] = sum[e];
+          }
+        }
+      };
+      if (ks == 2) put(std::integral_constant<int, 2>{});
+      else if (ks == 3) put(std::integral_constant<int, 3>{});
+      else put(std::integral_constant<int, 4>{});
+    } else {
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) ebuf[(8 * (r >> 2) + hr + (r & 3)) * TNP + 32 * j + lc] = acc[i][j][r];
+    }
     // the same wave reads the block back: its LDS accesses complete in order
     const int row0 = m0 + wm * TM + i * 32;
     if constexpr (EPI == EPI_QKV) {
@@ -393,16 +474,37 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
 // MFMA work (~0.4 us per slab) to arrive; wider tiles do 12-16 MFMAs per k step and
 // keep 2 slabs (their registers go to the accumulators).  A 4-slab ring
 // needs K % 256 == 0, else the 2-slab ring runs.
+// K splits for `tiles` tiles of `cycles` ring cycles each: as many as keep the
+// grid within one round (at most 4, each split at least two cycles) when the
+// tiles fill at most half the CUs; else 1
+int split_count(int tiles, int cycles, const GemmSplit& gs) {
+  if (!gs.part || !gs.cnt) return 1;
+  const int n_cu = device_cu_count();
+  if (2 * tiles > n_cu) return 1;
+  int ks = n_cu / tiles < 4 ? n_cu / tiles : 4;
+  if (ks > cycles / 2) ks = cycles / 2;
+  return ks >= 2 ? ks : 1;
+}
+
 template <int BM, int BN, int EPI>
-hipError_t launch_tiled(const bf16_t* A, const bf16_t* Wp, int M, int N, int K, const EpiArgs& ep, hipStream_t s) {
+hipError_t launch_tiled(const bf16_t* A, const bf16_t* Wp, int M, int N, int K, EpiArgs ep, const GemmSplit& gs,
+                        hipStream_t s) {
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const bool ring4 = BM == 128 && BN == 256 && K % 256 == 0;
+  ep.ks = split_count(tiles, K / BK / (ring4 ? 4 : 2), gs);
+  ep.part = gs.part;
+  ep.cnt = gs.cnt;
+  const dim3 grid(static_cast<unsigned>(tiles * ep.ks));
+  const bool split = ep.ks > 1;
   if constexpr (BM == 128 && BN == 256) {
-    if (K % 256 == 0) {
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, 4>), dim3(tiles), dim3(256), 0, s, A, Wp, M, N, K, ep);
+    if (ring4) {
+      if (split) hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, 4, true>), grid, dim3(256), 0, s, A, Wp, M, N, K, ep);
+      else hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, 4, false>), grid, dim3(256), 0, s, A, Wp, M, N, K, ep);
       return hipGetLastError();
     }
   }
-  hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, 2>), dim3(tiles), dim3(256), 0, s, A, Wp, M, N, K, ep);
+  if (split) hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, 2, true>), grid, dim3(256), 0, s, A, Wp, M, N, K, ep);
+  else hipLaunchKernelGGL((gemm_kernel<BM, BN, EPI, 2, false>), grid, dim3(256), 0, s, A, Wp, M, N, K, ep);
   return hipGetLastError();
 }
 
@@ -436,24 +538,30 @@ int device_cu_count() {
   return n_cu;
 }
 
-hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, const QkvEpilogue& q, hipStream_t s) {
+size_t gemm_split_part_floats() { return static_cast<size_t>(device_cu_count()) * 128 * 512; }
+
+hipError_t launch_gemm_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, const QkvEpilogue& q,
+                           const GemmSplit& gs, hipStream_t s) {
   EpiArgs ep{}; ep.qkv = q;
-  return wide_qkv_tiles(M, N) ? launch_tiled<128, 512, EPI_QKV>(A, W, M, N, K, ep, s)
-                              : launch_tiled<256, kQkvBN, EPI_QKV>(A, W, M, N, K, ep, s);
+  return wide_qkv_tiles(M, N) ? launch_tiled<128, 512, EPI_QKV>(A, W, M, N, K, ep, gs, s)
+                              : launch_tiled<256, kQkvBN, EPI_QKV>(A, W, M, N, K, ep, gs, s);
 }
-hipError_t launch_gemm_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K, const bf16_t* resid, float* out, hipStream_t s) {
+hipError_t launch_gemm_resid_f32out(const bf16_t* A, const bf16_t* W, int M, int N, int K, const bf16_t* resid,
+                                    float* out, const GemmSplit& gs, hipStream_t s) {
   EpiArgs ep{}; ep.resid = resid; ep.out = out;
-  return wide_resid_tiles(M, N) ? launch_tiled<128, 512, EPI_RESID32>(A, W, M, N, K, ep, s)
-                                : launch_tiled<128, 256, EPI_RESID32>(A, W, M, N, K, ep, s);
+  return wide_resid_tiles(M, N) ? launch_tiled<128, 512, EPI_RESID32>(A, W, M, N, K, ep, gs, s)
+                                : launch_tiled<128, 256, EPI_RESID32>(A, W, M, N, K, ep, gs, s);
 }
-hipError_t launch_gemm_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K, const float* resid, bf16_t* out, hipStream_t s) {
+hipError_t launch_gemm_resid_bf16out(const bf16_t* A, const bf16_t* W, int M, int N, int K, const float* resid,
+                                     bf16_t* out, const GemmSplit& gs, hipStream_t s) {
   EpiArgs ep{}; ep.resid = resid; ep.out = out;
-  return wide_resid_tiles(M, N) ? launch_tiled<128, 512, EPI_RESID16>(A, W, M, N, K, ep, s)
-                                : launch_tiled<128, 256, EPI_RESID16>(A, W, M, N, K, ep, s);
+  return wide_resid_tiles(M, N) ? launch_tiled<128, 512, EPI_RESID16>(A, W, M, N, K, ep, gs, s)
+                                : launch_tiled<128, 256, EPI_RESID16>(A, W, M, N, K, ep, gs, s);
 }
-hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, int K, bf16_t* out, hipStream_t s) {
+hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, int K, bf16_t* out,
+                              const GemmSplit& gs, hipStream_t s) {
   EpiArgs ep{}; ep.out = out;
-  return N % 512 == 0 ? launch_tiled<128, 512, EPI_SWIGLU>(A, Wgu, M, N, K, ep, s)
-                      : launch_tiled<256, 256, EPI_SWIGLU>(A, Wgu, M, N, K, ep, s);
+  return N % 512 == 0 ? launch_tiled<128, 512, EPI_SWIGLU>(A, Wgu, M, N, K, ep, gs, s)
+                      : launch_tiled<256, 256, EPI_SWIGLU>(A, Wgu, M, N, K, ep, gs, s);
 }
 }  // namespace llama

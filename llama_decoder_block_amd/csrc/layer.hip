@@ -99,6 +99,7 @@ struct llama_layer {
   int part_seqs = 0;      // sequences the partial buffer holds at once
   void* kv_stage = nullptr;  // bf16 layers: [2, rows, Hkv, 128] new keys / values for the int8 cache's append
   SkinnyScratch sk{};     // split column groups of the weight-streaming GEMMs
+  GemmSplit gs{};         // split K of the tiled GEMMs (bf16 layers taking more than 64 tokens)
   int* check_flag = nullptr;  // LLAMA_LAYER_CHECK=1 at create: position validation result
   // per-step event timing (measurement aid)
   static constexpr int kRing = 256;
@@ -125,6 +126,7 @@ struct CallScratch {
   int part_seqs;   // sequences whose partials fit at once
   SkinnyScratch sk;
   void* kv_stage;  // [2, rows, Hkv, 128] bf16 (the int8 cache's append), or null
+  GemmSplit gs;    // split K of the tiled GEMMs (null: no split)
 };
 
 // The call's cache: contiguous [B, Hkv, max_pos, 128] K and V (pg null), or
@@ -142,7 +144,7 @@ struct KvArgs {
 };
 
 CallScratch handle_scratch(llama_layer* L) {
-  return CallScratch{L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->part_seqs, L->sk, L->kv_stage};
+  return CallScratch{L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->part_seqs, L->sk, L->kv_stage, L->gs};
 }
 
 }  // namespace
@@ -175,7 +177,7 @@ void release(llama_layer* L) {
       for (auto& e : row) (void)hipEventDestroy(e);
   void* bufs[] = {L->wqkv, L->wo, L->wgu, L->wd, L->g1, L->g2, L->rope_cos, L->rope_sin,
                   L->xn, L->q, L->o, L->x1, L->h, L->gu, L->part, L->sk.part, L->sk.cnt, L->check_flag,
-                  L->kv_stage};
+                  L->kv_stage, L->gs.part, L->gs.cnt};
   for (void* p : bufs)
     if (p) (void)hipFree(p);
 }
@@ -355,6 +357,12 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
     L->sk.cnt_len = static_cast<int>(groups);
     L->sk.part_len = skinny_scratch_floats();
     HIP_OR_FAIL(hipMemsetAsync(L->sk.cnt, 0, groups * sizeof(unsigned), s), "clear counters");
+    if (cfg->max_tokens > kSkinnyMaxTokens) {  // calls of more than 64 tokens take the tiled GEMMs
+      ALLOC_OR_FAIL(L->gs.part, gemm_split_part_floats() * sizeof(float));
+      ALLOC_OR_FAIL(L->gs.cnt, static_cast<size_t>(device_cu_count()) * sizeof(unsigned));
+      HIP_OR_FAIL(hipMemsetAsync(L->gs.cnt, 0, static_cast<size_t>(device_cu_count()) * sizeof(unsigned), s),
+                  "clear counters");
+    }
   } else {
     ALLOC_OR_FAIL(L->q, mt * (nq + 2 * nkv) * es);
     ALLOC_OR_FAIL(L->gu, mt * 2 * f * sizeof(float));
@@ -554,7 +562,7 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
   HIP_OR_RETURN(launch_rmsnorm(xb, 0, L->g1, 0, xn, 0, skinny, M, d, c.rms_eps, s), "rmsnorm 1");
   HIP_OR_RETURN(mark(1), "event record");
   HIP_OR_RETURN(skinny ? launch_skinny_qkv(xn, wqkv, M, nqkv, d, ep, S.sk, s)
-                       : launch_gemm_qkv(xn, wqkv, M, nqkv, d, ep, s),
+                       : launch_gemm_qkv(xn, wqkv, M, nqkv, d, ep, S.gs, s),
                 "qkv projection");
   if (q8)
     HIP_OR_RETURN(launch_kv_int8_append(k_stage, v_stage, pos, B, T, Hkv, c.max_pos, kv.span, kv.pg, static_cast<int8_t*>(kc),
@@ -588,17 +596,17 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
   }
   HIP_OR_RETURN(mark(3), "event record");
   HIP_OR_RETURN(skinny ? launch_skinny_resid_f32out(o, wo, M, d, H * 128, xb, S.x1, S.sk, s)
-                       : launch_gemm_resid_f32out(o, wo, M, d, H * 128, xb, S.x1, s),
+                       : launch_gemm_resid_f32out(o, wo, M, d, H * 128, xb, S.x1, S.gs, s),
                 "o_proj");
   HIP_OR_RETURN(mark(4), "event record");
   HIP_OR_RETURN(launch_rmsnorm(S.x1, 1, L->g2, 0, xn, 0, skinny, M, d, c.rms_eps, s), "rmsnorm 2");
   HIP_OR_RETURN(mark(5), "event record");
   HIP_OR_RETURN(skinny ? launch_skinny_swiglu(xn, wgu, M, f, d, h, S.sk, s)
-                       : launch_gemm_swiglu(xn, wgu, M, 2 * f, d, h, s),
+                       : launch_gemm_swiglu(xn, wgu, M, 2 * f, d, h, S.gs, s),
                 "gate/up projection");
   HIP_OR_RETURN(mark(6), "event record");
   HIP_OR_RETURN(skinny ? launch_skinny_resid_bf16out(h, wd, M, d, f, S.x1, yb, S.sk, s)
-                       : launch_gemm_resid_bf16out(h, wd, M, d, f, S.x1, yb, s),
+                       : launch_gemm_resid_bf16out(h, wd, M, d, f, S.x1, yb, S.gs, s),
                 "down projection");
   HIP_OR_RETURN(mark(7), "event record");
   if (ev) ++L->prof_next;
