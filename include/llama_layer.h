@@ -112,7 +112,7 @@ typedef struct llama_layer llama_layer;
  * weights.  Blocks until the copies on `stream` are done.  The scratch is
  * sized by max_tokens, plus, for bf16 layers with max_tokens > 64, one
  * 128 x 512 fp32 tile per compute unit (64 MiB on 256 CUs) for the partial
- * sums of projections that split their reduction over several workgroups. */
+ * sums of projections that split their reduction over several workgroups.
  * With the environment variable LLAMA_LAYER_CHECK=1 at creation, every later
  * prefill/decode call of the handle first validates its positions on the
  * device and waits for the result (a debug aid: it synchronises the stream).
