@@ -110,7 +110,7 @@ typedef struct llama_layer llama_layer;
 /* Validate the config, allocate the handle's weights, RoPE table (cos and sin
  * of p * base^(-2i/dh), built in fp64 on the host) and scratch, and copy the
  * weights.  Blocks until the copies on `stream` are done.  The scratch is
- * sized by max_tokens, plus, for bf16 layers with max_tokens > 64, one
+ * sized by max_tokens, plus, for bf16 layers with max_tokens > 128, one
  * 128 x 512 fp32 tile per compute unit (64 MiB on 256 CUs) for the partial
  * sums of projections that split their reduction over several workgroups.
  * With the environment variable LLAMA_LAYER_CHECK=1 at creation, every later

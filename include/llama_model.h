@@ -74,7 +74,7 @@ void llama_model_destroy(llama_model* model);
  *   k_caches, v_caches  host arrays of L device pointers, each [B, Hkv,
  *              max_pos, dh] in the layer dtype (as for llama_layer_prefill)
  *   logits     [B, V] fp32: the last position's logits of each prompt.
- * Errors: NULL, INVALID (B, T < 1), CAPACITY (B > 64, B*T > max_tokens or
+ * Errors: NULL, INVALID (B, T < 1), CAPACITY (B > 128, B*T > max_tokens or
  * T > max_pos), HIP. */
 int llama_model_prefill(llama_model* model, const int32_t* ids, int32_t B, int32_t T,
                         void* const* k_caches, void* const* v_caches, float* logits, void* stream);

@@ -127,7 +127,7 @@ __device__ __forceinline__ uint2 load8_nt(const void* p) {
 // wavefront reads one chunk with one contiguous 1 KB load, and rows
 // [32 rb, 32 rb + n) of the matrix occupy elements [32 rb K, (32 rb + n) K),
 // exactly where they sit in row-major order.  The weights of every bf16 layer
-// are stored this way, and so are the activations of calls with <= 64 tokens.
+// are stored this way, and so are the activations of calls with <= 128 tokens.
 __device__ __forceinline__ uint32_t frag_index(int row, int k, int K) {
   return ((static_cast<uint32_t>(row >> 5) * static_cast<uint32_t>(K >> 4) + static_cast<uint32_t>(k >> 4)) << 9) +
          (static_cast<uint32_t>((row & 31) + ((k >> 3) & 1) * 32) << 3) + static_cast<uint32_t>(k & 7);
@@ -243,18 +243,18 @@ hipError_t launch_gemm_swiglu(const bf16_t* A, const bf16_t* Wgu, int M, int N, 
 // compute units of the current device (256 if the query fails)
 int device_cu_count();
 
-// Weight-streaming versions of the same four GEMMs for M <= 64 tokens: A and
+// Weight-streaming versions of the same four GEMMs for M <= 128 tokens: A and
 // W both in fragment order (A holds ceil(M/32)*32 rows; rows >= M are never
 // written out, whatever they hold), in the same operand formats as the tiled
 // ones.  The SwiGLU output h (fp16) is written in fragment order, ready to be
 // the A operand of the down projection.
 // Scratch for column groups split between workgroups: part holds part_len
 // floats (skinny_scratch_floats() always suffices; a call with G workgroups
-// needs 2 G x (1 or 2 blocks) x (1 or 2 token blocks) x 1024), cnt cnt_len
+// needs 2 G x (1 or 2 blocks) x (1, 2 or 4 token blocks) x 1024), cnt cnt_len
 // counters (one per column group: N / 32 or N / 64 for the paired SwiGLU),
 // all zero before the first call; each call leaves them zero.
 // Calls that share a scratch must not overlap.
-constexpr int kSkinnyMaxTokens = 64;
+constexpr int kSkinnyMaxTokens = 128;
 constexpr int kSkinnyGrid = 512;  // workgroups per call, at most
 struct SkinnyScratch {
   float* part;

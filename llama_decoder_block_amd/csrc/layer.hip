@@ -87,7 +87,7 @@ struct llama_layer {
   void* g2 = nullptr;
   float* rope_cos = nullptr;  // [max_pos, dh/2]
   float* rope_sin = nullptr;
-  // scratch (owned); bf16 activations hold max(max_tokens, 64) rows so that
+  // scratch (owned); bf16 activations hold max(max_tokens, 128) rows so that
   // the fragment-order form (whole 32-row blocks) always fits
   void* xn = nullptr;     // [max_tokens, d]
   void* q = nullptr;      // bf16: [max_tokens, H dh]; fp32: qkv [max_tokens, (H+2Hkv) dh]
@@ -99,7 +99,7 @@ struct llama_layer {
   int part_seqs = 0;      // sequences the partial buffer holds at once
   void* kv_stage = nullptr;  // bf16 layers: [2, rows, Hkv, 128] new keys / values for the int8 cache's append
   SkinnyScratch sk{};     // split column groups of the weight-streaming GEMMs
-  GemmSplit gs{};         // split K of the tiled GEMMs (bf16 layers taking more than 64 tokens)
+  GemmSplit gs{};         // split K of the tiled GEMMs (bf16 layers taking more than 128 tokens)
   int* check_flag = nullptr;  // LLAMA_LAYER_CHECK=1 at create: position validation result
   // per-step event timing (measurement aid)
   static constexpr int kRing = 256;
@@ -208,7 +208,7 @@ int check_config(const llama_layer_config* c) {
     if (c->head_dim != 128) return fail(LLAMA_ERR_UNSUPPORTED, "bf16 kernels need head_dim 128");
     if (c->d_model % 128 || c->d_ff % 128)
       return fail(LLAMA_ERR_UNSUPPORTED, "bf16 kernels need d_model and d_ff multiples of 128");
-    // calls of <= 64 tokens normalise into fragment order: one wavefront per
+    // calls of <= 128 tokens normalise into fragment order: one wavefront per
     // row up to d = 8192, a workgroup per row at d = 16384 (2048 x 8)
     if (c->d_model > 8192 && c->d_model != 16384)
       return fail(LLAMA_ERR_UNSUPPORTED, "bf16 kernels need d_model <= 8192 or d_model = 16384");
@@ -245,6 +245,7 @@ namespace {
 // the per-device address from hipGetSymbolAddress (the array's name on the
 // host is only a stand-in).
 constexpr size_t kNoAllocScratchBytes = static_cast<size_t>(32) << 20;
+constexpr int kNoAllocMaxSeqs = 64;  // sequences per allocation-free decode call
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -357,7 +358,7 @@ int llama_layer_create(const llama_layer_config* cfg, const llama_layer_weights*
     L->sk.cnt_len = static_cast<int>(groups);
     L->sk.part_len = skinny_scratch_floats();
     HIP_OR_FAIL(hipMemsetAsync(L->sk.cnt, 0, groups * sizeof(unsigned), s), "clear counters");
-    if (cfg->max_tokens > kSkinnyMaxTokens) {  // calls of more than 64 tokens take the tiled GEMMs
+    if (cfg->max_tokens > kSkinnyMaxTokens) {  // calls of more than 128 tokens take the tiled GEMMs
       ALLOC_OR_FAIL(L->gs.part, gemm_split_part_floats() * sizeof(float));
       ALLOC_OR_FAIL(L->gs.cnt, static_cast<size_t>(device_cu_count()) * sizeof(unsigned));
       HIP_OR_FAIL(hipMemsetAsync(L->gs.cnt, 0, static_cast<size_t>(device_cu_count()) * sizeof(unsigned), s),
@@ -570,8 +571,10 @@ static int run_layer(llama_layer* L, const CallScratch& S, const void* x, void* 
                   "int8 cache append");
   HIP_OR_RETURN(mark(2), "event record");
   if (T == 1) {
-    // sequences in chunks of part_seqs (one chunk for <= 64 tokens, whose o is
-    // in fragment order): contiguous caches or block-table rows move with b0
+    // sequences in chunks of part_seqs (64: a chunk starts on a 32-row block,
+    // where fragment order and row-major order agree, so o, in fragment order
+    // for <= 128 tokens, moves with b0 as well); contiguous caches or
+    // block-table rows move with b0
     const bool paged = kv.pg.block_table != nullptr;
     const size_t kv_seq = paged ? 0 : static_cast<size_t>(Hkv) * c.max_pos * 128;  // elements per sequence
     const size_t kv_es = q8 ? 1 : 2;
@@ -804,15 +807,15 @@ int llama_layer_decode_noalloc(llama_layer* L, const void* x, void* y, const int
   const llama_layer_config& c = L->cfg;
   if (c.dtype != LLAMA_BF16) return fail(LLAMA_ERR_UNSUPPORTED, "the allocation-free decode serves bf16 layers");
   if (B < 1) return fail(LLAMA_ERR_INVALID, "B must be >= 1 (got %d)", B);
-  if (B > kSkinnyMaxTokens)
+  if (B > kNoAllocMaxSeqs)
     return fail(LLAMA_ERR_CAPACITY, "the allocation-free decode takes at most %d sequences (got %d)",
-                kSkinnyMaxTokens, B);
+                kNoAllocMaxSeqs, B);
   if (!aligned16(x) || !aligned16(y) || !aligned16(k_cache) || !aligned16(v_cache))
     return fail(LLAMA_ERR_INVALID, "x, y and the caches must be 16-byte aligned");
   // slices of the static array, 256-byte aligned; activations in fragment
   // order hold whole 32-row blocks, i.e. 64 rows
   const size_t d = c.d_model, nq = static_cast<size_t>(c.n_heads) * 128, f = c.d_ff;
-  const size_t nkv = static_cast<size_t>(c.n_kv_heads) * 128, rows = kSkinnyMaxTokens;
+  const size_t nkv = static_cast<size_t>(c.n_kv_heads) * 128, rows = kNoAllocMaxSeqs;
   size_t off = 0;
   auto take = [&off](size_t bytes) {
     const size_t at = off;

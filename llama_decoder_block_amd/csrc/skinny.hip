@@ -365,22 +365,25 @@ hipError_t launch(const bf16_t* X, const bf16_t* W, int M, int N, int K, SkinnyA
   const int groups = N / (32 * NB);
   const int G = grid_for(groups, K / 16, device_cu_count());
   // split groups need 2 G partial slots of NB x TB tiles and a counter each
-  const int TBn = M <= 32 ? 1 : 2;
+  const int TBn = M <= 32 ? 1 : (M <= 64 ? 2 : 4);
   if (G != groups && (G > kSkinnyGrid || groups > ep.cnt_len ||
                       static_cast<size_t>(2) * G * NB * TBn * 1024 > ep.part_len))
     return hipErrorInvalidValue;
   if (M <= 32)
     hipLaunchKernelGGL((skinny_kernel<NB, 1, kNW, paired ? 12 : 16, EPI>), dim3(G), dim3(kNW * 64), 0, s, X, W, M,
                        N, K, G, ep);
-  else
+  else if (M <= 64)
     hipLaunchKernelGGL((skinny_kernel<NB, 2, kNW, paired ? 8 : 12, EPI>), dim3(G), dim3(kNW * 64), 0, s, X, W, M,
                        N, K, G, ep);
+  else  // 4 token blocks: a wavefront per block, so 4 wavefronts
+    hipLaunchKernelGGL((skinny_kernel<NB, 4, 4, paired ? 6 : 8, EPI>), dim3(G), dim3(4 * 64), 0, s, X, W, M, N, K,
+                       G, ep);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t skinny_scratch_floats() { return static_cast<size_t>(2) * kSkinnyGrid * 4 * 1024; }
+size_t skinny_scratch_floats() { return static_cast<size_t>(2) * kSkinnyGrid * 8 * 1024; }  // NB x TB <= 8
 
 hipError_t launch_skinny_qkv(const bf16_t* A, const bf16_t* W, int M, int N, int K, const QkvEpilogue& q,
                              const SkinnyScratch& sc, hipStream_t s) {

@@ -70,9 +70,11 @@ def test_tiny_fp32_layer():
     dict(d=384, H=3, Hkv=1, f=640, B=1, T=129),       # odd heads, MQA, N not a multiple of 256
     dict(d=256, H=2, Hkv=2, f=384, B=3, T=5),         # 15 tokens: weight-streaming GEMMs
     dict(d=1024, H=8, Hkv=2, f=2816, B=1, T=1),       # single token prefill
-    dict(d=512, H=4, Hkv=4, f=1408, B=1, T=64),       # 64 tokens: largest skinny call
-    dict(d=512, H=4, Hkv=4, f=1408, B=1, T=65),       # 65 tokens: smallest tiled call
-    dict(d=512, H=4, Hkv=2, f=1408, B=1, T=127),      # one short of a 128-row tile
+    dict(d=512, H=4, Hkv=4, f=1408, B=1, T=64),       # 64 tokens: two token blocks of weight streaming
+    dict(d=512, H=4, Hkv=4, f=1408, B=1, T=65),       # 65 tokens: the four-block weight-streaming GEMMs
+    dict(d=512, H=4, Hkv=2, f=1408, B=1, T=127),      # one short of four token blocks
+    dict(d=1024, H=8, Hkv=2, f=2816, B=2, T=64),      # 128 tokens: the largest weight-streaming call
+    dict(d=512, H=4, Hkv=4, f=1408, B=1, T=129),      # 129 tokens: the smallest tiled call (split K)
     dict(d=512, H=4, Hkv=1, f=1408, B=1, T=1000),     # long ragged sequence, MQA
 ])
 def test_bf16_prefill_small(shape):
