@@ -48,7 +48,7 @@
 //     XCDs) gets a contiguous, M-grouped range, which keeps the A and W panels
 //     it shares inside its own L2.
 //   * Split K: when the tiles fill at most half the CUs (few tokens: chunked
-//     prefill, batched decode of more than 64 sequences), each tile's slabs
+//     prefill, batched decode of more than 128 sequences), each tile's slabs
 //     are cut into ks <= 4 ranges of whole ring cycles, one workgroup each
 //     (more would leave the last arriver too many partials to read alone).  Every
 //     split writes its fp32 partial tile with coherent 16-byte stores, waits

@@ -11,7 +11,7 @@
 //
 // gfx950 design.
 //   * The logits are needed for the last position of each sequence only:
-//     those B <= 64 rows are gathered, normalised into fragment order and
+//     those B <= 128 rows are gathered, normalised into fragment order and
 //     multiplied by the LM head with the weight-streaming GEMM (its fp32
 //     epilogue); the LM head rows are padded to a multiple of 128 at create.
 //   * Sampling runs one 1024-thread workgroup per row and never writes the

@@ -1,4 +1,4 @@
-// Weight-streaming GEMMs for few tokens (decode: M = batch <= 64), with the
+// Weight-streaming GEMMs for few tokens (decode: M = batch <= 128), with the
 // same fused epilogues as the tiled prefill GEMMs (RoPE + cache append,
 // residual adds, SwiGLU).  Sources as for the prefill projections: "LMDrive
 // LLM core inference unit" page §2.3-§2.5, "Llama MLP deep dive" page §2.2,
@@ -28,7 +28,9 @@
 // one reads all partials back, adds them in range order (so the result does
 // not depend on arrival order) and runs the epilogue, then re-arms the
 // counter.  Each weight byte is read exactly once (nontemporal loads); the
-// activations (<= 64 x K bf16) are re-read by every workgroup from L2.
+// activations (<= 128 x K bf16) are re-read by every workgroup from L2.
+// Calls of 65-128 tokens take four 32-token blocks with 4 wavefronts (a
+// wavefront finishes one token block).
 //
 // Pairing: the QKV weight's heads are in rotary-pair order (dims x and x + 64
 // on rows 2x and 2x + 1), so a rotation's two inputs are neighbouring
