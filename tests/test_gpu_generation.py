@@ -181,12 +181,19 @@ def test_sampled_generation_matches_oracle():
     model.close()
 
 
-def test_bf16_model_logits_and_decode_steps():
+@pytest.mark.parametrize("B,T", [
+    (3, 40),
+    # 100 sequences: the logits rows and the decode steps take the four-block
+    # weight-streaming GEMMs, the decode attention two chunks of sequences
+    (100, 8),
+])
+def test_bf16_model_logits_and_decode_steps(B, T):
     """A 2-layer bf16 model, vocab 1000 (not a multiple of 128: padded LM
     head): prefill logits and teacher-forced decode-step logits against the
     oracle in its bf16-rounding-point mode."""
-    wl = synth.Workload("small_model", "bf16", 512, 4, 2, 128, 1408, 3, 40, decode_steps=3, seed=33)
-    L, V, B, T = 2, 1000, 3, 40
+    wl = synth.Workload("small_model", "bf16", 512, 4, 2, 128, 1408, B, T, decode_steps=3, seed=33)
+    L, V = 2, 1000
+    print(f"case B={B} T={T}", flush=True)
     mw = _model(wl, L, V)
     om = _oracle_model(wl, mw)
     model = _gpu_model(wl, mw, L, V, B * T)
