@@ -469,11 +469,6 @@ __global__ __launch_bounds__(256) void gemm_kernel(const bf16_t* __restrict__ A,
   }
 }
 
-// Weight ring depth: a wave tile with 8 MFMAs per k step (128 x 256 tiles)
-// gets a 4-slab ring, so a weight load that misses L2 still has ~3 slabs of
-// MFMA work (~0.4 us per slab) to arrive; wider tiles do 12-16 MFMAs per k step and
-// keep 2 slabs (their registers go to the accumulators).  A 4-slab ring
-// needs K % 256 == 0, else the 2-slab ring runs.
 // K splits for `tiles` tiles of `cycles` ring cycles each: as many as keep the
 // grid within one round (at most 4, each split at least two cycles) when the
 // tiles fill at most half the CUs; else 1
@@ -486,6 +481,11 @@ int split_count(int tiles, int cycles, const GemmSplit& gs) {
   return ks >= 2 ? ks : 1;
 }
 
+// Weight ring depth: a wave tile with 8 MFMAs per k step (128 x 256 tiles)
+// gets a 4-slab ring, so a weight load that misses L2 still has ~3 slabs of
+// MFMA work (~0.4 us per slab) to arrive; wider tiles do 12-16 MFMAs per k step and
+// keep 2 slabs (their registers go to the accumulators).  A 4-slab ring
+// needs K % 256 == 0, else the 2-slab ring runs.
 template <int BM, int BN, int EPI>
 hipError_t launch_tiled(const bf16_t* A, const bf16_t* Wp, int M, int N, int K, EpiArgs ep, const GemmSplit& gs,
                         hipStream_t s) {
