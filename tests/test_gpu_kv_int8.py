@@ -206,3 +206,86 @@ def test_prefill_over_the_int8_cache(shape):
     _check_appended("K", kq, ks, okq, oks, slots, before[0], before[1])
     _check_appended("V", vq, vs, ovq, ovs, slots, before[2], before[3])
     layer.close()
+
+
+@pytest.mark.slow
+def test_llama7b_int8_prefill():
+    """The 7B prefill workload over an int8 cache, as the benchmark runs it: a
+    2048-token prompt from position 0 quantized into its slots while every
+    query attends over code * scale; y of all 2048 rows at the raw gate and
+    every appended row against the oracle's int8 call."""
+    wl = synth.WORKLOADS["llama7b_prefill"]
+    B, T = wl.batch, wl.seq
+    print(f"case llama7b_prefill int8: B={B} T={T}", flush=True)
+    w = synth.make_weights(wl, DEV)
+    x = synth.make_x(wl, (B, T), device=DEV)
+    pos = synth.prefill_positions(B, T, device=DEV)
+    kq, vq, ks, vs = _int8_cache(wl)
+    before = (kq.clone(), ks.clone(), vq.clone(), vs.clone())
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, B * T), w)
+    y = layer.prefill_int8(x, pos, kq, vq, ks, vs)
+    torch.cuda.synchronize()
+    print("  gpu done; running the oracle on every row", flush=True)
+    p = pos.cpu().numpy()
+    yo, okq, oks, ovq, ovs = O.decoder_layer_int8(
+        G.f64(x), p, G.oracle_weights(w), *(t.cpu().numpy() for t in (before[0], before[1], before[2], before[3])),
+        n_heads=wl.n_heads, n_kv_heads=wl.n_kv_heads, eps=wl.rms_eps, rope_base=wl.rope_base, bf16_points=True)
+    G.assert_bf16_output(G.f64(y).reshape(B * T, -1), yo.reshape(B * T, -1), f"y (all {B * T} rows)")
+    slots = [list(p[b]) for b in range(B)]
+    _check_appended("K", kq, ks, okq, oks, slots, before[0], before[1])
+    _check_appended("V", vq, vs, ovq, ovs, slots, before[2], before[3])
+    layer.close()
+
+
+@pytest.mark.slow
+def test_llama7b_int8_decode_and_its_paged_form():
+    """The 7B decode workload over an int8 cache, as the benchmark runs it:
+    32 sequences at position 4095 whose 4096 random bf16 rows per head are
+    converted (codes and scales bit for bit the oracle's at this size), then
+    one step: y of every sequence at the raw gate and the appended rows
+    against the oracle's int8 step.  The same step over the codes and scales
+    on shuffled pages of 64 slots is bit-identical to the contiguous one."""
+    from tests.test_gpu_paged import from_pages, to_pages
+    wl = synth.WORKLOADS["llama7b_decode"]
+    B, p = wl.batch, wl.prior
+    print(f"case llama7b_decode int8: B={B} pos={p}", flush=True)
+    w = synth.make_weights(wl, DEV)
+    x = synth.make_x(wl, (B,), device=DEV)
+    kc, vc = synth.make_cache(wl, DEV)
+    kq, vq, ks, vs = _int8_cache(wl)
+    layer = lib.LlamaLayer(G.layer_config(lib, wl, B), w)
+    layer.kv_quantize(kc, vc, wl.max_pos, kq, vq, ks, vs)
+    torch.cuda.synchronize()
+    okq, oks = O.kv_int8_quantize(G.f64(kc))
+    ovq, ovs = O.kv_int8_quantize(G.f64(vc))
+    del kc, vc
+    for name, q, s, oq, os_ in (("K", kq, ks, okq, oks), ("V", vq, vs, ovq, ovs)):
+        np.testing.assert_array_equal(q.cpu().numpy(), oq, err_msg=f"{name} codes")
+        np.testing.assert_array_equal(s.cpu().numpy(), os_, err_msg=f"{name} scales")
+    print("  conversion bit-identical to the oracle's", flush=True)
+
+    def pages(t):  # scales [B, Hkv, S] ride as rows of one element
+        pool, bt = to_pages(t if t.dim() == 4 else t.unsqueeze(-1), 64, seed=5)
+        return (pool if t.dim() == 4 else pool.squeeze(-1).contiguous()), bt
+    (kp, bt), (vp, _), (ksp, _), (vsp, _) = pages(kq), pages(vq), pages(ks), pages(vs)
+    before = (kq.clone(), ks.clone(), vq.clone(), vs.clone())
+    pos = torch.full((B,), p, dtype=torch.int32, device=DEV)
+    y = layer.decode_int8(x, pos, kq, vq, ks, vs)
+    yp = layer.decode_paged_int8(x, pos, kp, vp, ksp, vsp, bt)
+    torch.cuda.synchronize()
+    nd = int((yp.view(torch.int16) != y.view(torch.int16)).sum())
+    print(f"  paged y: {nd} elements differ from the contiguous call", flush=True)
+    assert nd == 0
+    for a, b_ in ((from_pages(kp, bt, 64), kq), (from_pages(vp, bt, 64), vq),
+                  (from_pages(ksp.unsqueeze(-1), bt, 64)[..., 0], ks), (from_pages(vsp.unsqueeze(-1), bt, 64)[..., 0], vs)):
+        assert torch.equal(a, b_)
+    del kp, vp, ksp, vsp
+    pn = np.full(B, p)
+    yo, okq, oks, ovq, ovs = O.decoder_layer_decode_int8(
+        G.f64(x), pn, G.oracle_weights(w), okq, oks, ovq, ovs, n_heads=wl.n_heads, n_kv_heads=wl.n_kv_heads,
+        eps=wl.rms_eps, rope_base=wl.rope_base, bf16_points=True)
+    G.assert_bf16_output(G.f64(y), yo, f"y (all {B} sequences)")
+    slots = [[p] for _ in range(B)]
+    _check_appended("K", kq, ks, okq, oks, slots, before[0], before[1])
+    _check_appended("V", vq, vs, ovq, ovs, slots, before[2], before[3])
+    layer.close()
