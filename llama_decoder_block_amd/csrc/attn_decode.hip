@@ -135,8 +135,16 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
 
   // the 4 K and 4 V rows of this row group's next slots j, j + 16, ...
   // (int8: 8 codes per lane in .x / .y, and the rows' scales)
-  auto fetch = [&](int j, uint4 (&ku)[4], uint4 (&vu)[4], float (&kss)[4], float (&vss)[4]) {
+  // (int8: of a row group's 16 lanes, lane u < 4 loads the key scale of its
+  // u-th row and lane 4 + u the value scale; the rest of the group takes them
+  // by lane shuffles, one scale load per lane instead of eight)
+  const float* const SS = (dc & 4) ? VS : KS;
+  auto fetch = [&](int j, uint4 (&ku)[4], uint4 (&vu)[4], float& sw) {
     const long long base = PAGED ? page_shift(j) : 0;
+    if constexpr (Q8) {
+      const int js = j + 16 * (dc & 3);
+      sw = dc < 8 && js < n ? SS[base + js] : 0.f;
+    }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const bool ok = j + 16 * u < n;
@@ -146,8 +154,6 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
         const uint2 v8 = ok ? load8_nt(V + r * DH) : make_uint2(0, 0);
         ku[u] = make_uint4(k8.x, k8.y, 0, 0);
         vu[u] = make_uint4(v8.x, v8.y, 0, 0);
-        kss[u] = ok ? KS[r] : 0.f;
-        vss[u] = ok ? VS[r] : 0.f;
       } else {
         ku[u] = ok ? load16_nt(K + r * DH * 2) : make_uint4(0, 0, 0, 0);
         vu[u] = ok ? load16_nt(V + r * DH * 2) : make_uint4(0, 0, 0, 0);
@@ -172,12 +178,20 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
   // with fewer, where up to four share a CU, it still measured 1% (R = 1, 2)
   // to 6% (R = 4) faster than fetching at the top of each iteration
   uint4 ku[4], vu[4];  // this iteration's rows
-  float kss[4], vss[4];  // (int8) their scales
-  fetch(sub, ku, vu, kss, vss);
+  float sw = 0.f;        // (int8) one of their scales (see fetch)
+  fetch(sub, ku, vu, sw);
   for (int j = sub; j < n; j += 64) {
     uint4 kn[4], vn[4];  // the next iteration's rows (prefetch)
-    float ksn[4], vsn[4];
-    fetch(j + 64, kn, vn, ksn, vsn);
+    float swn = 0.f;
+    fetch(j + 64, kn, vn, swn);
+    float kss[4], vss[4];  // (int8) the scales of this row group's rows
+    if constexpr (Q8) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        kss[u] = __shfl(sw, (lane & 48) + u, 64);
+        vss[u] = __shfl(sw, (lane & 48) + 4 + u, 64);
+      }
+    }
     float sc[R][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -220,9 +234,8 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(
     for (int u = 0; u < 4; ++u) {
       ku[u] = kn[u];
       vu[u] = vn[u];
-      kss[u] = ksn[u];
-      vss[u] = vsn[u];
     }
+    sw = swn;
   }
 
   // merge the 4 row groups of a wave (lanes 16 and 32 apart), then the 4 waves
